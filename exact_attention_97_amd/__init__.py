@@ -1,0 +1,20 @@
+"""Exact fused scaled-dot-product attention for AMD MI355X (gfx950).
+
+The compute lives in hand-written HIP kernels behind the C ABI of
+``include/attn97.h`` (libattn97.so).  This package only loads that library
+and marshals arguments: ``attn_fwd`` returns (O, LSE), ``attn_bwd`` returns
+(dQ, dK, dV).
+"""
+
+from ._lib import (  # noqa: F401
+    AttnError,
+    attn_bwd,
+    attn_fwd,
+    bwd_workspace_bytes,
+    exp2_eval,
+    load,
+    prof_collect,
+    prof_enable,
+    prof_reset,
+    version,
+)

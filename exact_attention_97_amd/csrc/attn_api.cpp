@@ -1,0 +1,237 @@
+// attn_api.cpp - the C ABI declared in include/attn97.h: argument checks,
+// option handling, workspace layout, kernel dispatch and the timing hooks.
+// Nothing here allocates device memory or synchronises with the device
+// (except attn_prof_collect, which waits on its own timing events).
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+#include "attn97.h"
+#include "attn_kernels.hpp"
+
+namespace {
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+attn_status check_shape(int B, int H, int S, int D) {
+  if (B < 1 || H < 1 || S < 1) return ATTN_ERR_SHAPE;
+  if (D != 64 && D != 128 && D != 256) return ATTN_ERR_UNSUPPORTED;
+  const double elems = (double)B * H * S * D;
+  if (elems > 2147483647.0) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+attn_status read_opts(const attn_opts* in, attn_opts* out) {
+  attn_default_opts(out);
+  if (in == nullptr) return ATTN_OK;
+  if (in->exp_mode < 0 || in->exp_mode > 2) return ATTN_ERR_UNSUPPORTED;
+  if (in->bwd_mode < 0 || in->bwd_mode > 1) return ATTN_ERR_UNSUPPORTED;
+  if (!(in->rescale_tau >= 0.0f) || !isfinite(in->rescale_tau)) return ATTN_ERR_VALUE;
+  *out = *in;
+  return ATTN_OK;
+}
+
+// ---- timing hooks -----------------------------------------------------------
+struct ProfRec {
+  int kid;
+  hipEvent_t start, stop;
+};
+constexpr size_t kMaxProf = 65536;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_pool;  // events, created on first use and reused
+size_t g_prof_used = 0;
+size_t g_prof_open = (size_t)-1;
+
+}  // namespace
+
+namespace attn97 {
+
+void prof_begin(int kid, hipStream_t st) {
+  g_prof_open = (size_t)-1;
+  if (!g_prof_on || g_prof_used >= kMaxProf) return;
+  if (g_prof_used == g_prof_pool.size()) {
+    ProfRec r{kid, nullptr, nullptr};
+    if (hipEventCreate(&r.start) != hipSuccess) return;
+    if (hipEventCreate(&r.stop) != hipSuccess) {
+      (void)hipEventDestroy(r.start);
+      return;
+    }
+    g_prof_pool.push_back(r);
+  }
+  ProfRec& r = g_prof_pool[g_prof_used];
+  r.kid = kid;
+  if (hipEventRecord(r.start, st) != hipSuccess) return;
+  g_prof_open = g_prof_used;
+}
+
+void prof_end(int kid, hipStream_t st) {
+  if (g_prof_open == (size_t)-1) return;
+  ProfRec& r = g_prof_pool[g_prof_open];
+  g_prof_open = (size_t)-1;
+  if (r.kid != kid) return;
+  if (hipEventRecord(r.stop, st) != hipSuccess) return;
+  ++g_prof_used;
+}
+
+}  // namespace attn97
+
+extern "C" {
+
+void attn_default_opts(attn_opts* opts) {
+  if (opts == nullptr) return;
+  opts->exp_mode = ATTN_EXP_NATIVE;
+  opts->rescale_tau = 8.0f;
+  opts->bwd_mode = ATTN_BWD_ATOMIC;
+}
+
+const char* attn_version(void) { return "attn97 0.1.0 (gfx950)"; }
+
+const char* attn_strerror(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "invalid shape (B, H and S must be >= 1; tensors below 2^31 elements)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension or option";
+    case ATTN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case ATTN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case ATTN_ERR_HIP: return "HIP runtime error at launch";
+    case ATTN_ERR_VALUE: return "scale or an option value is not finite or out of range";
+  }
+  return "unknown status";
+}
+
+attn_status attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                     int S, int D, float scale, int causal, const attn_opts* opts, void* stream) {
+  if (!Q || !K || !V || !O || !LSE) return ATTN_ERR_NULL;
+  attn_status st = check_shape(B, H, S, D);
+  if (st != ATTN_OK) return st;
+  if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(V, 16) || misaligned(O, 16) ||
+      misaligned(LSE, 16))
+    return ATTN_ERR_ALIGN;
+  if (!isfinite(scale)) return ATTN_ERR_VALUE;
+  attn_opts o;
+  st = read_opts(opts, &o);
+  if (st != ATTN_OK) return st;
+
+  attn97::FwdArgs a;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.LSE = LSE;
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.D = D;
+  a.causal = causal ? 1 : 0;
+  a.exp_mode = o.exp_mode;
+  a.C = fabsf(scale) * kLog2eHost;
+  a.qsign = (scale < 0.0f) ? 0x80008000u : 0u;
+  a.tau = o.rescale_tau;
+  hipError_t e = attn97::launch_fwd(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+size_t attn_bwd_workspace_bytes(int B, int H, int S, int D, int causal, const attn_opts* opts) {
+  (void)causal;
+  if (check_shape(B, H, S, D) != ATTN_OK) return 0;
+  attn_opts o;
+  if (read_opts(opts, &o) != ATTN_OK) return 0;
+  size_t n = attn97::bwd_delta_bytes(B, H, S);
+  if (o.bwd_mode == ATTN_BWD_ATOMIC) n += attn97::bwd_dq32_bytes(B, H, S, D);
+  return n;
+}
+
+attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                     const float* LSE, void* dQ, void* dK, void* dV, void* workspace,
+                     size_t workspace_bytes, int B, int H, int S, int D, float scale, int causal,
+                     const attn_opts* opts, void* stream) {
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return ATTN_ERR_NULL;
+  attn_status st = check_shape(B, H, S, D);
+  if (st != ATTN_OK) return st;
+  if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(V, 16) || misaligned(O, 16) ||
+      misaligned(dO, 16) || misaligned(LSE, 16) || misaligned(dQ, 16) || misaligned(dK, 16) ||
+      misaligned(dV, 16))
+    return ATTN_ERR_ALIGN;
+  if (!isfinite(scale)) return ATTN_ERR_VALUE;
+  attn_opts o;
+  st = read_opts(opts, &o);
+  if (st != ATTN_OK) return st;
+  if (o.bwd_mode != ATTN_BWD_ATOMIC || !attn97::bwd_supported(D)) return ATTN_ERR_UNSUPPORTED;
+  const size_t need = attn_bwd_workspace_bytes(B, H, S, D, causal, &o);
+  if (workspace == nullptr || workspace_bytes < need || misaligned(workspace, 256))
+    return ATTN_ERR_WORKSPACE;
+
+  attn97::BwdArgs a;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.dO = dO;
+  a.LSE = LSE;
+  a.dQ = dQ;
+  a.dK = dK;
+  a.dV = dV;
+  a.delta = static_cast<float*>(workspace);
+  a.dq32 = reinterpret_cast<float*>(static_cast<char*>(workspace) + attn97::bwd_delta_bytes(B, H, S));
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.D = D;
+  a.causal = causal ? 1 : 0;
+  a.scale = scale;
+  hipError_t e = attn97::launch_bwd_atomic(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_exp2_eval(const float* x, float* y, long n, int mode, void* stream) {
+  if (n < 0) return ATTN_ERR_SHAPE;
+  if (mode != ATTN_EXP_NATIVE && mode != ATTN_EXP_POLY) return ATTN_ERR_UNSUPPORTED;
+  if (n == 0) return ATTN_OK;
+  if (!x || !y) return ATTN_ERR_NULL;
+  if (misaligned(x, 4) || misaligned(y, 4)) return ATTN_ERR_ALIGN;
+  hipError_t e = attn97::launch_exp2_eval(x, y, n, mode, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_prof_enable(int on) {
+  g_prof_on = on != 0;
+  return ATTN_OK;
+}
+
+attn_status attn_prof_reset(void) {
+  g_prof_used = 0;
+  g_prof_open = (size_t)-1;
+  return ATTN_OK;
+}
+
+attn_status attn_prof_collect(const char* kernel, int* count, double* total_ms) {
+  if (!kernel || !count || !total_ms) return ATTN_ERR_NULL;
+  static const char* names[attn97::KID_COUNT] = {"fwd", "bwd_pre", "bwd_main", "dq_convert", "bwd_dkdv", "bwd_dq"};
+  int kid = -1;
+  for (int i = 0; i < attn97::KID_COUNT; ++i)
+    if (strcmp(kernel, names[i]) == 0) kid = i;
+  if (kid < 0) return ATTN_ERR_UNSUPPORTED;
+  int n = 0;
+  double ms = 0.0;
+  for (size_t i = 0; i < g_prof_used; ++i) {
+    ProfRec& r = g_prof_pool[i];
+    if (r.kid != kid) continue;
+    if (hipEventSynchronize(r.stop) != hipSuccess) return ATTN_ERR_HIP;
+    float t = 0.0f;
+    if (hipEventElapsedTime(&t, r.start, r.stop) != hipSuccess) return ATTN_ERR_HIP;
+    ms += t;
+    ++n;
+  }
+  *count = n;
+  *total_ms = ms;
+  return ATTN_OK;
+}
+
+}  // extern "C"

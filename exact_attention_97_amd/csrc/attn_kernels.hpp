@@ -1,0 +1,62 @@
+// attn_kernels.hpp - host-side launch interface between the C ABI layer and
+// the kernel translation units.  Plain structs of device pointers and sizes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn97 {
+
+struct FwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  float* LSE;
+  int B, H, S, D;
+  int causal;
+  int exp_mode;
+  float C;         // |scale| * log2(e)
+  uint32_t qsign;  // 0x80008000 flips the sign of Q (negative scale), else 0
+  float tau;       // conditional rescale threshold, log2 units
+};
+
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  const float* LSE;
+  void* dQ;
+  void* dK;
+  void* dV;
+  float* delta;  // workspace: fp32 [B,H,S]
+  float* dq32;   // workspace: fp32 [B,H,S,D] (atomic mode)
+  int B, H, S, D;
+  int causal;
+  float scale;
+};
+
+// Workspace layout of attn_bwd: delta (rounded up to 256 bytes), then dq32.
+inline size_t bwd_delta_bytes(int B, int H, int S) {
+  size_t n = (size_t)B * H * S * sizeof(float);
+  return (n + 255) & ~(size_t)255;
+}
+inline size_t bwd_dq32_bytes(int B, int H, int S, int D) {
+  return (size_t)B * H * S * D * sizeof(float);
+}
+
+// Kernel names used by the timing hooks.
+enum KernelId { KID_FWD = 0, KID_BWD_PRE, KID_BWD_MAIN, KID_DQ_CONVERT, KID_BWD_DKDV, KID_BWD_DQ, KID_COUNT };
+
+// Called by the launchers around each kernel launch (no-ops unless timing is on).
+void prof_begin(int kid, hipStream_t st);
+void prof_end(int kid, hipStream_t st);
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
+hipError_t launch_exp2_eval(const float* x, float* y, long n, int mode, hipStream_t st);
+hipError_t launch_bwd_atomic(const BwdArgs& a, hipStream_t st);
+bool bwd_supported(int D);
+
+}  // namespace attn97

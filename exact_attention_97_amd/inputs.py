@@ -46,7 +46,7 @@ WORKLOADS = {
     "tiny": Workload("tiny", 1, 2, 256, 64, (False,), seed=0),
     "fwd2k": Workload("fwd2k", 8, 16, 2048, 128, (False, True), seed=1, passes="fwd"),
     "long8k": Workload("long8k", 2, 16, 8192, 128, (False, True), seed=2,
-                       outlier_frac=0.01, outlier_scale=20.0),
+                       outlier_frac=0.01, outlier_scale=20.0, passes="fwd"),
     "bwd4k": Workload("bwd4k", 4, 16, 4096, 128, (False, True), seed=3),
     "ctx32k": Workload("ctx32k", 1, 32, 32768, 128, (True,), seed=4, std=0.5),
     "d64": Workload("d64", 2, 16, 8192, 64, (False, True), seed=5, std=0.5),

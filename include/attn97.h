@@ -1,0 +1,159 @@
+/*
+ * attn97.h - C ABI of the exact fused attention library for AMD MI355X (gfx950).
+ *
+ * The library computes exact scaled-dot-product attention
+ *     O = softmax(scale * Q K^T) V
+ * for one GPU.  Attention is two matrix products with a softmax between
+ * them: the scores S = Q K^T and the output O = P V (page "FlashAttention-4 :
+ * comment Together AI a accéléré l'attention sur GPU Blackwell", section
+ * "Pourquoi l'approche standard ne fonctionne plus"; page "FlashAttention-3 и
+ * FlashAttention-4", section "Режим 2-CTA MMA", which also names the
+ * softmax, normalisation, masking and row reductions between the products).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Q, K, V, O, dO, dQ, dK, dV are bfloat16 tensors in contiguous row-major
+ *    layout [B, H, S, D] (D fastest), resident in device memory.
+ *  - LSE is float32 [B, H, S]: the natural-log log-sum-exp of each row of
+ *    scaled scores, LSE_i = ln sum_j exp(scale * q_i . k_j) over visible j.
+ *  - causal != 0 hides key j from query i when j > i (0-based indices).
+ *    Queries and keys have the same length S, so no row is fully hidden.
+ *  - Every pointer is a device pointer, owned by the caller, and must be
+ *    16-byte aligned.  Inputs are read-only.  Outputs must not alias inputs.
+ *  - B, H, S >= 1 and D in {64, 128, 256}; S need not be a multiple of any
+ *    tile size.  B*H*S*D must fit in 2^31 - 1 elements per tensor.
+ *  - scale must be finite (any sign; 0 gives the mean of the visible rows).
+ *  - stream is a hipStream_t (NULL = the default stream).  Calls are
+ *    asynchronous with respect to the host; the library never synchronises,
+ *    never allocates device memory and keeps no per-call state, so calls on
+ *    different streams may run concurrently.
+ *  - Errors are return codes only.  Argument errors are detected before
+ *    anything is launched.  A failed launch returns ATTN_ERR_HIP; a fault
+ *    inside a kernel surfaces at the caller's next synchronisation.
+ */
+#ifndef ATTN97_H
+#define ATTN97_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,        /* a required pointer is NULL                 */
+    ATTN_ERR_SHAPE = 2,       /* B, H or S < 1, or a tensor too large       */
+    ATTN_ERR_UNSUPPORTED = 3, /* D not in {64,128,256}, or an unknown option */
+    ATTN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned            */
+    ATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required     */
+    ATTN_ERR_HIP = 6,         /* the HIP runtime rejected a launch           */
+    ATTN_ERR_VALUE = 7        /* scale or an option value is not finite / out of range */
+} attn_status;
+
+/* How the forward kernel computes exp2 of the shifted scores.  The pages
+ * describe computing the softmax exponential in software with a polynomial
+ * on the fused multiply-add units instead of the special-function units
+ * (page "FlashAttention-3 и FlashAttention-4", section "Программная эмуляция
+ * экспоненты"; abstract of "FlashAttention-4: Algorithm and Kernel Pipelining
+ * Co-Design for Asymmetric Hardware Scaling"). */
+typedef enum {
+    ATTN_EXP_NATIVE = 0, /* hardware v_exp_f32 for every element                  */
+    ATTN_EXP_POLY = 1,   /* range reduction + degree-3 polynomial on the FMA pipe  */
+    ATTN_EXP_MIXED = 2   /* half of each lane's scores native, half polynomial     */
+} attn_exp_mode;
+
+/* How the backward pass forms dQ.  The pages name the atomic additions of
+ * the backward pass as an overhead at long sequence lengths (page
+ * "FlashAttention-3 и FlashAttention-4", section "Режим 2-CTA MMA"). */
+typedef enum {
+    ATTN_BWD_ATOMIC = 0, /* one kernel per key tile; dQ summed with fp32 atomics into the workspace */
+    ATTN_BWD_SPLIT = 1   /* a dK/dV kernel plus a separate dQ kernel; no atomics, deterministic    */
+} attn_bwd_mode;
+
+typedef struct {
+    int exp_mode;      /* attn_exp_mode; default ATTN_EXP_NATIVE                               */
+    float rescale_tau; /* conditional rescaling threshold in log2 units, >= 0; default 8.
+                          The running row maximum used to shift the scores is only moved when
+                          some row of a wavefront sees its maximum grow by more than tau, so
+                          unnormalised probabilities stay below 2^tau.  0 = always rescale.
+                          (Conditional softmax rescaling: abstract of "FlashAttention-4:
+                          Algorithm and Kernel Pipelining Co-Design for Asymmetric Hardware
+                          Scaling".)  The result is the same for every tau up to rounding.  */
+    int bwd_mode;      /* attn_bwd_mode; default ATTN_BWD_ATOMIC                               */
+} attn_opts;
+
+/* Defaults: {ATTN_EXP_NATIVE, 8.0f, ATTN_BWD_ATOMIC}. */
+void attn_default_opts(attn_opts* opts);
+
+/*
+ * Forward pass.
+ *   in : Q, K, V   bf16 [B,H,S,D]
+ *   out: O         bf16 [B,H,S,D]  O = softmax(scale*Q K^T (+ causal mask)) V,
+ *                                  rounded to nearest even from fp32
+ *        LSE       fp32 [B,H,S]    natural-log log-sum-exp of each row
+ *   opts may be NULL (defaults).
+ */
+attn_status attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                     int B, int H, int S, int D, float scale, int causal,
+                     const attn_opts* opts, void* stream);
+
+/*
+ * Bytes of device workspace attn_bwd needs for this shape and mode: the
+ * per-row Delta_i = sum_d dO_id * O_id (fp32 [B,H,S]) and, in ATTN_BWD_ATOMIC
+ * mode, the fp32 dQ accumulator [B,H,S,D].  Returns 0 for invalid shapes.
+ */
+size_t attn_bwd_workspace_bytes(int B, int H, int S, int D, int causal, const attn_opts* opts);
+
+/*
+ * Backward pass.  P is recomputed from LSE (it is never stored):
+ *   P = exp(scale*Q K^T - LSE), dV = P^T dO, dP = dO V^T,
+ *   dS = P * (dP - Delta), dQ = scale * dS K, dK = scale * dS^T Q.
+ *   in : Q, K, V, O, dO  bf16 [B,H,S,D];  LSE fp32 [B,H,S] from attn_fwd with
+ *        the same scale and causal flag
+ *   out: dQ, dK, dV      bf16 [B,H,S,D]
+ *   workspace: caller-owned device memory of at least
+ *        attn_bwd_workspace_bytes(...) bytes, 256-byte aligned; its contents
+ *        on entry do not matter and are overwritten.  Two calls in flight at
+ *        once must not share a workspace.
+ */
+attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                     const float* LSE, void* dQ, void* dK, void* dV,
+                     void* workspace, size_t workspace_bytes,
+                     int B, int H, int S, int D, float scale, int causal,
+                     const attn_opts* opts, void* stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* attn_strerror(attn_status s);
+
+/*
+ * Diagnostic: evaluate the kernels' exp2 on n fp32 values, y[i] = 2^x[i],
+ * with the same device code the forward kernel uses for mode (an
+ * attn_exp_mode).  x and y are device pointers of n floats (n >= 0; n = 0
+ * launches nothing).  Arguments below the clamp point (-127) return the
+ * value at the clamp point in ATTN_EXP_POLY mode.
+ */
+attn_status attn_exp2_eval(const float* x, float* y, long n, int mode, void* stream);
+
+/*
+ * Timing of the library's own kernels, for measurement tools.  While enabled,
+ * every kernel launch is bracketed by two hipEvents recorded on the launch
+ * stream.  attn_prof_collect synchronises on those events and returns, for
+ * the kernel named `kernel` ("fwd", "bwd_pre", "bwd_main", "bwd_dq", "bwd_dkdv",
+ * "dq_convert"), the number of launches and the summed milliseconds since the
+ * last reset.  Events are created on first use and kept; at most 65536
+ * launches are recorded between resets (later ones are not timed).
+ * Not thread-safe; meant for single-threaded benchmark drivers.
+ */
+attn_status attn_prof_enable(int on);
+attn_status attn_prof_reset(void);
+attn_status attn_prof_collect(const char* kernel, int* count, double* total_ms);
+
+/* Library version string. */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN97_H */

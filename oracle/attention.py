@@ -135,22 +135,26 @@ def attention_fwd_rows(q, k, v, scale: float, causal: bool, rows):
 
     ``rows`` is an iterable of (b, h, i).  Rows of attention are independent
     of one another, so each is the full definition applied to one query.
-    Returns (O_rows [n, D], LSE_rows [n]).
+    Returns (O_rows [n, D], LSE_rows [n]) in the order of ``rows``.
     """
     rows = list(rows)
     dv = v.shape[-1]
     o = np.zeros((len(rows), dv))
     lse = np.zeros(len(rows))
+    by_head = {}
     for n, (b, h, i) in enumerate(rows):
-        qi = _f64(q[b, h, i : i + 1])
+        by_head.setdefault((b, h), []).append((n, i))
+    for (b, h), items in by_head.items():
         kk = _f64(k[b, h])
         vv = _f64(v[b, h])
-        s = scale * (qi @ kk.T)
-        if causal:
-            s[:, i + 1 :] = -np.inf
-        p, l = softmax_rows(s)
-        o[n] = (p @ vv)[0]
-        lse[n] = l[0]
+        for n, i in items:
+            qi = _f64(q[b, h, i : i + 1])
+            s = scale * (qi @ kk.T)
+            if causal:
+                s[:, i + 1 :] = -np.inf
+            p, l = softmax_rows(s)
+            o[n] = (p @ vv)[0]
+            lse[n] = l[0]
     return o, lse
 
 

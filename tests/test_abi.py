@@ -1,0 +1,160 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments with the documented status codes
+before launching anything (so these run without a GPU)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn97.h")
+
+from exact_attention_97_amd import _lib as L  # noqa: E402
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="libattn97.so not built")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, HIP, VALUE = range(8)
+P = 0x10000  # a fake, 256-byte aligned device address: never dereferenced on these paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(attn_[a-z0-9_]+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.load()
+    names = declared_functions()
+    assert len(names) >= 10, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in attn97.h but not exported"
+    assert set(names) == set(L.EXPORTS)
+
+
+def test_version_and_strerror():
+    lib = L.load()
+    assert b"gfx950" in lib.attn_version()
+    texts = {lib.attn_strerror(c) for c in range(8)}
+    assert len(texts) == 8
+    assert lib.attn_strerror(99) == b"unknown status"
+
+
+def test_default_opts():
+    lib = L.load()
+    o = L.AttnOpts()
+    o.exp_mode, o.rescale_tau, o.bwd_mode = 7, -1.0, 7
+    lib.attn_default_opts(ctypes.byref(o))
+    assert (o.exp_mode, o.rescale_tau, o.bwd_mode) == (0, 8.0, 0)
+
+
+def fwd(**kw):
+    a = dict(Q=P, K=P, V=P, O=P, LSE=P, B=1, H=1, S=16, D=64, scale=0.125, causal=0, opts=None, stream=None)
+    a.update(kw)
+    opts = ctypes.byref(a["opts"]) if a["opts"] is not None else None
+    return L.load().attn_fwd(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H"], a["S"], a["D"],
+                             a["scale"], a["causal"], opts, a["stream"])
+
+
+def bwd(**kw):
+    a = dict(Q=P, K=P, V=P, O=P, dO=P, LSE=P, dQ=P, dK=P, dV=P, ws=P, wsb=1 << 40, B=1, H=1, S=16, D=64,
+             scale=0.125, causal=0, opts=None, stream=None)
+    a.update(kw)
+    opts = ctypes.byref(a["opts"]) if a["opts"] is not None else None
+    return L.load().attn_bwd(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["LSE"], a["dQ"], a["dK"], a["dV"],
+                             a["ws"], a["wsb"], a["B"], a["H"], a["S"], a["D"], a["scale"], a["causal"],
+                             opts, a["stream"])
+
+
+@pytest.mark.parametrize("name", ["Q", "K", "V", "O", "LSE"])
+def test_fwd_null(name):
+    assert fwd(**{name: None}) == NULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), SHAPE), (dict(H=0), SHAPE), (dict(S=0), SHAPE), (dict(S=-3), SHAPE),
+    (dict(D=32), UNSUP), (dict(D=96), UNSUP), (dict(D=512), UNSUP),
+    (dict(B=1 << 10, H=1 << 10, S=1 << 10, D=64), SHAPE),
+    (dict(Q=P + 8), ALIGN), (dict(V=P + 2), ALIGN), (dict(LSE=P + 4), ALIGN),
+    (dict(scale=float("nan")), VALUE), (dict(scale=float("inf")), VALUE),
+])
+def test_fwd_rejects(kw, code):
+    assert fwd(**kw) == code
+
+
+def test_fwd_bad_options():
+    assert fwd(opts=L.make_opts(exp_mode=3)) == UNSUP
+    assert fwd(opts=L.make_opts(exp_mode=-1)) == UNSUP
+    assert fwd(opts=L.make_opts(rescale_tau=-1.0)) == VALUE
+    assert fwd(opts=L.make_opts(rescale_tau=float("nan"))) == VALUE
+    assert fwd(opts=L.make_opts(rescale_tau=float("inf"))) == VALUE
+
+
+@pytest.mark.parametrize("name", ["Q", "K", "V", "O", "dO", "LSE", "dQ", "dK", "dV"])
+def test_bwd_null(name):
+    assert bwd(**{name: None}) == NULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(S=0), SHAPE), (dict(D=48), UNSUP), (dict(dO=P + 8), ALIGN), (dict(dK=P + 2), ALIGN),
+    (dict(scale=float("nan")), VALUE), (dict(ws=None), WS), (dict(wsb=16), WS), (dict(ws=P + 16), WS),
+])
+def test_bwd_rejects(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_bwd_bad_options():
+    assert bwd(opts=L.make_opts(bwd_mode=2)) == UNSUP
+
+
+def test_workspace_bytes():
+    lib = L.load()
+    o = L.make_opts()
+    B, H, S, D = 2, 3, 100, 128
+    delta = (B * H * S * 4 + 255) // 256 * 256
+    assert lib.attn_bwd_workspace_bytes(B, H, S, D, 0, ctypes.byref(o)) == delta + B * H * S * D * 4
+    assert lib.attn_bwd_workspace_bytes(B, H, S, D, 1, None) == delta + B * H * S * D * 4
+    o.bwd_mode = 1
+    assert lib.attn_bwd_workspace_bytes(B, H, S, D, 0, ctypes.byref(o)) == delta
+    assert lib.attn_bwd_workspace_bytes(0, H, S, D, 0, None) == 0
+    assert lib.attn_bwd_workspace_bytes(B, H, S, 80, 0, None) == 0
+
+
+def test_exp2_eval_rejects():
+    lib = L.load()
+    assert lib.attn_exp2_eval(None, None, 0, 0, None) == OK  # empty: nothing launched
+    assert lib.attn_exp2_eval(None, P, 4, 0, None) == NULL
+    assert lib.attn_exp2_eval(P, P, -1, 0, None) == SHAPE
+    assert lib.attn_exp2_eval(P, P, 4, 2, None) == UNSUP
+    assert lib.attn_exp2_eval(P + 2, P, 4, 0, None) == ALIGN
+
+
+def test_prof_hooks_without_launches():
+    lib = L.load()
+    assert lib.attn_prof_reset() == OK
+    n, ms = ctypes.c_int(-1), ctypes.c_double(-1.0)
+    assert lib.attn_prof_collect(b"fwd", ctypes.byref(n), ctypes.byref(ms)) == OK
+    assert (n.value, ms.value) == (0, 0.0)
+    assert lib.attn_prof_collect(b"nope", ctypes.byref(n), ctypes.byref(ms)) == UNSUP
+    assert lib.attn_prof_collect(None, ctypes.byref(n), ctypes.byref(ms)) == NULL
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros((1, 1, 4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        L.attn_fwd(q, q, q)
+
+
+def test_product_path_does_not_import_oracle():
+    """The package and its sources never reference the oracle."""
+    pkg = os.path.join(ROOT, "exact_attention_97_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "import oracle" not in text and "from oracle" not in text, f
