@@ -212,13 +212,23 @@ def test_workload_full_size(name):
         del o, lse
 
 
-def test_bwd_outliers_magnitude_scaled():
+def test_bwd_outliers_rounding_bound():
     """Backward on the outlier inputs (Q, K entries x20 with probability 1%).
 
-    Their gradients reach magnitudes where one bf16 rounding step of the
-    output already exceeds an absolute 2e-2, so here the per-element bound
-    is 2e-2 + 2^-7 |reference| (two bf16 half-steps), the mean bound stays
-    2e-3.
+    Here the gradients reach magnitudes where an absolute 2e-2 is below what
+    bf16 operands allow: the kernels round P and dS to bf16 (relative 2^-9)
+    before the products dV = P^T dO, dK = scale dS^T Q and dQ = scale dS K,
+    and those products then carry an error up to 2^-9 times the matching sum
+    of absolute terms (e.g. scale |dS| |K| for dQ), which outlier rows of K
+    make large even where dQ itself is small.  Second, Delta_i is formed as
+    sum_d dO_id O_id from the bf16 output O (the forward pass keeps no fp32
+    copy), which is off by up to e_i = 2^-9 sum_d |dO_id O_id|; that enters
+    dS_ij as P_ij e_i and hence dQ_i as scale e_i sum_j P_ij |K_j| and dK_j
+    as scale sum_i P_ij e_i |Q_i| (K and Q with x20 outliers amplify it).
+    The per-element bound is these first-order terms (with a factor 2
+    margin), plus one bf16 step of the output and the usual 2e-2; the mean
+    bound stays 2e-3.  The absolute terms are formed here in float32 from
+    the plain definitions.
     """
     import torch
 
@@ -231,13 +241,27 @@ def test_bwd_outliers_magnitude_scaled():
         torch.cuda.synchronize()
         rdq, rdk, rdv = oracle.attention_bwd_f32(q, k, v, do, w.scale, causal, heads=[(0, 0), (0, 1)])
         for n, h in enumerate((0, 1)):
+            qf, kf, vf, dof = (x[0, h].float() for x in (q, k, v, do))
+            sc = (qf @ kf.T) * w.scale
+            if causal:
+                sc = sc.masked_fill(torch.ones_like(sc, dtype=torch.bool).triu(1), float("-inf"))
+            pr = torch.softmax(sc, dim=-1)
+            dpr = dof @ vf.T
+            dsr = pr * (dpr - (pr * dpr).sum(-1, keepdim=True))
+            of = (pr @ vf)
+            e = (dof * of).abs().sum(-1, keepdim=True)  # sum_d |dO O|; times 2^-9 in the bound
+            terms = {"dQ": w.scale * (dsr.abs() @ kf.abs() + (pr * e) @ kf.abs()),
+                     "dK": w.scale * (dsr.abs().T @ qf.abs() + (pr * e).T @ qf.abs()),
+                     "dV": pr.T @ dof.abs()}
             for nm, g, r in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
                 got = _np(g[0, h])
                 ref = r[n].double().numpy()
                 err = np.abs(got - ref)
-                worst = float(np.max(err - (O_MAX + 2.0**-7 * np.abs(ref))))
+                bound = O_MAX + 2.0**-8 * np.abs(ref) + 2.0 * 2.0**-9 * terms[nm].double().numpy()
+                worst = float(np.max(err - bound))
                 print(f"    {nm} head {h} causal={causal}: max-abs {err.max():.3e} "
-                      f"(|ref| max {np.abs(ref).max():.1f}) mean-abs {err.mean():.3e}", flush=True)
+                      f"(|ref| max {np.abs(ref).max():.1f}) mean-abs {err.mean():.3e} worst-vs-bound {worst:.3e}",
+                      flush=True)
                 assert worst <= 0.0 and err.mean() <= O_MEAN
 
 
