@@ -37,6 +37,8 @@
 // computes the scores of tile j+1; then P_j V_j.  K tiles are loaded two
 // tiles ahead and V tiles one ahead, each into a double buffer, so one
 // barrier per tile suffices.
+#include <stdlib.h>
+
 #include "attn_kernels.hpp"
 #include "device_common.hpp"
 
@@ -45,18 +47,50 @@ namespace attn97 {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-template <int D>
+// Tile configuration: head dim D, BC keys per tile, NW wavefronts (32 query
+// rows each) per workgroup, NBUF LDS buffers per K and V tile.  With three
+// buffers, loads are issued two iterations before they are consumed and a
+// wave only waits for the ones issued an iteration earlier.
+template <int D_, int BC_, int NW_, int NBUF_>
 struct FwdCfg {
-  static constexpr int BC = (D == 64) ? 128 : (D == 128 ? 64 : 32);  // keys per tile
-  static constexpr int BR = 128;                                     // queries per workgroup
-  static constexpr int CPR = D / 8;                                  // 16-byte chunks per row
-  static constexpr int TILE_BYTES = BC * D * 2;                      // 16 KiB
-  static constexpr int NKB = BC / 32;                                // 32-key blocks per tile
-  static constexpr int NKS = D / 16;                                 // reduction steps over D
-  static constexpr int NDB = D / 32;                                 // 32-wide blocks of D
-  static constexpr int DMA_PER_WAVE = TILE_BYTES / 1024 / 4;         // 1 KiB loads per wave per tile
-  static_assert(TILE_BYTES == 16384, "tile size");
+  static constexpr int D = D_;
+  static constexpr int BC = BC_;                       // keys per tile
+  static constexpr int NW = NW_;                       // wavefronts per workgroup
+  static constexpr int NBUF = NBUF_;                   // LDS buffers per tile kind
+  static constexpr int BR = 32 * NW;                   // queries per workgroup
+  static constexpr int CPR = D / 8;                    // 16-byte chunks per row
+  static constexpr int TILE_BYTES = BC * D * 2;
+  static constexpr int NKB = BC / 32;                  // 32-key blocks per tile
+  static constexpr int NKS = D / 16;                   // reduction steps over D
+  static constexpr int NDB = D / 32;                   // 32-wide blocks of D
+  static constexpr int DMA_PER_WAVE = TILE_BYTES / 1024 / NW;  // 1 KiB loads per wave per tile
+  static constexpr int LDS_BYTES = 2 * NBUF * TILE_BYTES;
+  static_assert(DMA_PER_WAVE >= 1 && DMA_PER_WAVE * 1024 * NW == TILE_BYTES, "tile split over waves");
+  static_assert(NBUF == 2 || NBUF == 3, "two or three buffers");
+  static_assert(BC % 32 == 0 && BC >= 32, "key tile");
 };
+
+// Default configurations per head dim (measured on MI355X).
+template <int D>
+struct FwdDefault;
+template <>
+struct FwdDefault<64> {
+  using type = FwdCfg<64, 128, 4, 2>;
+};
+template <>
+struct FwdDefault<128> {
+  using type = FwdCfg<128, 64, 4, 2>;
+};
+template <>
+struct FwdDefault<256> {
+  using type = FwdCfg<256, 32, 4, 2>;
+};
+
+// s_waitcnt with vmcnt <= N, lgkmcnt = 0, expcnt unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+}
 
 // Physical 16-byte chunk index, inside a K or V tile, of logical chunk c of
 // row `row`.  Rows of 256 bytes (D = 128) or 512 bytes (D = 256) XOR the low
@@ -100,10 +134,10 @@ __device__ __forceinline__ void unswz_chunk(int P, int& row, int& c) {
 // logical element offset inside the tile (row * D + 8 * chunk), fixed per
 // lane.  In a ragged last tile, rows past S are clamped to S-1 (finite data;
 // the scores of those keys are masked).
-template <int D>
+template <class Cfg>
 __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, int k0, int S, uint16_t* dst,
-                                         int wave, const uint32_t (&loff)[FwdCfg<D>::DMA_PER_WAVE]) {
-  constexpr int NPW = FwdCfg<D>::DMA_PER_WAVE, BC = FwdCfg<D>::BC;
+                                         int wave, const uint32_t (&loff)[Cfg::DMA_PER_WAVE]) {
+  constexpr int NPW = Cfg::DMA_PER_WAVE, BC = Cfg::BC, D = Cfg::D;
   const uint16_t* tile = src + (size_t)k0 * D;
   const bool ragged = k0 + BC > S;
 #pragma unroll
@@ -136,10 +170,9 @@ __device__ __forceinline__ bf16x8 pack_probs(const float (&p)[8]) {
 }
 
 // Per-lane LDS offsets (elements) that stay fixed over the whole loop.
-template <int D>
+template <class Cfg>
 struct FwdOffsets {
-  using Cfg = FwdCfg<D>;
-  static constexpr int NKS = Cfg::NKS, NDB = Cfg::NDB, CPR = Cfg::CPR;
+  static constexpr int D = Cfg::D, NKS = Cfg::NKS, NDB = Cfg::NDB, CPR = Cfg::CPR;
   // K operand: row c32 (+32 kb), chunk 2 ks + hh.  The swizzle depends on
   // row & 15 only, so the key block adds 32 * CPR chunks.
   int kfrag[NKS];
@@ -169,13 +202,12 @@ struct FwdOffsets {
   }
 };
 
-template <int D, int EXPMODE>
+template <class Cfg, int EXPMODE>
 struct FwdWave {
-  using Cfg = FwdCfg<D>;
-  static constexpr int NKB = Cfg::NKB, NKS = Cfg::NKS, NDB = Cfg::NDB, BC = Cfg::BC, CPR = Cfg::CPR;
+  static constexpr int D = Cfg::D, NKB = Cfg::NKB, NKS = Cfg::NKS, NDB = Cfg::NDB, BC = Cfg::BC, CPR = Cfg::CPR;
 
   // S^T of one tile: sacc[kb] = K[32kb + ., :] Q^T.
-  __device__ __forceinline__ static void scores(const uint16_t* kt, const FwdOffsets<D>& of,
+  __device__ __forceinline__ static void scores(const uint16_t* kt, const FwdOffsets<Cfg>& of,
                                                 const bf16x8 (&qreg)[NKS], f32x16 (&sacc)[NKB]) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
@@ -233,7 +265,7 @@ struct FwdWave {
 
   // O^T += V^T P^T; the V^T operand comes from two LDS transpose loads of
   // four keys each: slots 0..3 -> keys 16t + 4h + s, 4..7 -> 16t + 8 + 4h + s-4.
-  __device__ __forceinline__ static void pv(const uint16_t* vt, const FwdOffsets<D>& of,
+  __device__ __forceinline__ static void pv(const uint16_t* vt, const FwdOffsets<Cfg>& of,
                                             const bf16x8 (&pb)[2 * NKB], f32x16 (&oacc)[NDB]) {
     typedef short s16x8 __attribute__((ext_vector_type(8)));
 #pragma unroll
@@ -257,7 +289,7 @@ struct FwdWave {
   // tile's scores are computed even after the wave's last tile (from a
   // stale but finite buffer) so that region 1 has no branch.
   template <bool MASK>
-  __device__ __forceinline__ static void step(const uint16_t* knext, const uint16_t* vcur, const FwdOffsets<D>& of,
+  __device__ __forceinline__ static void step(const uint16_t* knext, const uint16_t* vcur, const FwdOffsets<Cfg>& of,
                                               const bf16x8 (&qreg)[NKS], f32x16 (&scur)[NKB], f32x16 (&oacc)[NDB],
                                               float& m_run, float& l_part, int k0, int lim, int hh, float C,
                                               float tau) {
@@ -274,22 +306,39 @@ struct FwdWave {
     l_part *= alpha;
     scores(knext, of, qreg, snext);
     probs<MASK>(scur, C, m_run, pb, l_part);
+    // Schedule: the K fragment reads run four ahead of the MFMAs that use
+    // them, and each MFMA is followed by a share of the softmax VALU work.
+    constexpr int NS = NKS * NKB;  // score MFMAs of the next tile
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int i = 0; i < NKS * NKB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+    for (int i = 0; i < NS - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+    // keep the exponentials and the packed P above the (rare) rescale branch
+#pragma unroll
+    for (int t = 0; t < 2 * NKB; ++t) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pb[t])));
+    asm volatile("" ::"v"(l_part));
     if (grow) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
     }
     pv(vcur, of, pb, oacc);
+    // PV: transpose reads run four ahead (two per MFMA operand).
+    constexpr int NP = 2 * NKB * NDB;
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
 #pragma unroll
-    for (int i = 0; i < 2 * NKB * NDB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // two LDS transpose reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // one MFMA
+    for (int i = 0; i < NP - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) scur[kb] = snext[kb];
   }
@@ -299,21 +348,18 @@ struct FwdWave {
 // order, tile counts, the last visible key), and one instantiation for both
 // settings keeps the compiler from restructuring the non-causal loop into a
 // version that spills registers.
-template <int D, int EXPMODE>
-__global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void fwd_kernel(const uint16_t* __restrict__ Q,
-                                                                      const uint16_t* __restrict__ K,
-                                                                      const uint16_t* __restrict__ V,
-                                                                      uint16_t* __restrict__ O,
-                                                                      float* __restrict__ LSE, int BH, int S,
-                                                                      float C, uint32_t qsign, float tau, int nqt,
-                                                                      int causal) {
-  using Cfg = FwdCfg<D>;
-  using W = FwdWave<D, EXPMODE>;
-  constexpr int BC = Cfg::BC, BR = Cfg::BR, NKB = Cfg::NKB, NKS = Cfg::NKS, NDB = Cfg::NDB;
+template <class Cfg, int EXPMODE>
+__global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 : 2) void fwd_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int S, float C, uint32_t qsign, float tau, int nqt,
+    int causal) {
+  using W = FwdWave<Cfg, EXPMODE>;
+  constexpr int D = Cfg::D, BC = Cfg::BC, BR = Cfg::BR, NKB = Cfg::NKB, NKS = Cfg::NKS, NDB = Cfg::NDB;
+  constexpr int NBUF = Cfg::NBUF, DPW = Cfg::DMA_PER_WAVE;
   constexpr int TILE = Cfg::TILE_BYTES / 2;  // elements
 
-  __shared__ __attribute__((aligned(1024))) uint16_t Kb[2][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vb[2][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t Kb[NBUF][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vb[NBUF][TILE];
 
   // Heaviest causal query tiles first, all heads of one rank together; with
   // B*H a multiple of 8 every workgroup of one head lands on the same XCD.
@@ -362,39 +408,61 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void fwd_kernel(const uint
   float m_run = kNegInf;  // running max, in units of log2 (scores times C)
   float l_part = 0.0f;    // this lane's partial row sum
 
-  FwdOffsets<D> of;
+  FwdOffsets<Cfg> of;
   of.init(wave, lane);
 
-  // prologue: K0, V0, K1 in flight; S^T(0) once K0 is in.
-  dma_tile<D>(Kh, 0, S, Kb[0], wave, of.dma);
-  dma_tile<D>(Vh, 0, S, Vb[0], wave, of.dma);
-  if (nkt > 1) dma_tile<D>(Kh, BC, S, Kb[1], wave, of.dma);
-  __builtin_amdgcn_s_waitcnt(0);
+  // Load schedule: iteration j issues K(j + NBUF) and V(j + NBUF - 1) into
+  // the buffers freed by the barrier of iteration j-1, and needs K(j + 1)
+  // (scores of the next tile) and V(j).  The prologue issues what iterations
+  // -NBUF..-1 would have.
+  auto issue = [&](int j) {  // loads of "iteration" j; returns the number of ops issued
+    int n = 0;
+    if (j + NBUF < nkt) {
+      dma_tile<Cfg>(Kh, (j + NBUF) * BC, S, Kb[(j + NBUF) % NBUF], wave, of.dma);
+      n += DPW;
+    }
+    if (j + NBUF - 1 >= 0 && j + NBUF - 1 < nkt) {
+      dma_tile<Cfg>(Vh, (j + NBUF - 1) * BC, S, Vb[(j + NBUF - 1) % NBUF], wave, of.dma);
+      n += DPW;
+    }
+    return n;
+  };
+  // Wait until only the loads of the latest issuing iteration are in flight
+  // (three buffers) or none (two buffers).
+  auto wait_loads = [&](int n_latest) {
+    if (NBUF == 2 || n_latest == 0)
+      wait_vm_lds<0>();
+    else if (n_latest == DPW)
+      wait_vm_lds<DPW>();
+    else
+      wait_vm_lds<2 * DPW>();
+  };
+
+  int n_last = 0;
+  for (int j = -NBUF; j < 0; ++j) n_last = issue(j);
+  wait_loads(n_last);
   __syncthreads();
 
   f32x16 scur[NKB];
   W::scores(Kb[0], of, qreg, scur);
 
   for (int kt = 0; kt < nkt; ++kt) {
-    // loads for later tiles: K two ahead, V one ahead (buffers freed by the
-    // barrier that ended the previous iteration)
-    if (kt + 2 < nkt) dma_tile<D>(Kh, (kt + 2) * BC, S, Kb[kt & 1], wave, of.dma);
-    if (kt + 1 < nkt) dma_tile<D>(Vh, (kt + 1) * BC, S, Vb[(kt + 1) & 1], wave, of.dma);
+    n_last = issue(kt);
     __builtin_amdgcn_sched_barrier(0);  // keep the load issue out of the compute schedule
 
     if (kt < nkt_w) {
       if (kt < nfull)
-        W::template step<false>(Kb[(kt + 1) & 1], Vb[kt & 1], of, qreg, scur, oacc, m_run, l_part, kt * BC, lim,
-                                hh, C, tau);
+        W::template step<false>(Kb[(kt + 1) % NBUF], Vb[kt % NBUF], of, qreg, scur, oacc, m_run, l_part, kt * BC,
+                                lim, hh, C, tau);
       else
-        W::template step<true>(Kb[(kt + 1) & 1], Vb[kt & 1], of, qreg, scur, oacc, m_run, l_part, kt * BC, lim,
-                               hh, C, tau);
+        W::template step<true>(Kb[(kt + 1) % NBUF], Vb[kt % NBUF], of, qreg, scur, oacc, m_run, l_part, kt * BC,
+                               lim, hh, C, tau);
     }
-    __builtin_amdgcn_s_waitcnt(0);
+    wait_loads(n_last);
     __syncthreads();
   }
 
-  // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l) ----------------------
+// ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l) ----------------------
   const float l_tot = l_part + wave_swap_halves(l_part);
   const float inv = 1.0f / l_tot;
   if (qrow < S) {
@@ -425,33 +493,50 @@ __global__ void exp2_eval_kernel(const float* __restrict__ x, float* __restrict_
 // ---------------------------------------------------------------------------
 // host-side launchers
 // ---------------------------------------------------------------------------
-template <int D, int EXPMODE>
+template <class Cfg, int EXPMODE>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
-  const int nqt = (a.S + FwdCfg<D>::BR - 1) / FwdCfg<D>::BR;
+  const int nqt = (a.S + Cfg::BR - 1) / Cfg::BR;
   const int BH = a.B * a.H;
-  dim3 grid(nqt * BH), block(256);
+  dim3 grid(nqt * BH), block(64 * Cfg::NW);
   prof_begin(KID_FWD, st);
-  hipLaunchKernelGGL((fwd_kernel<D, EXPMODE>), grid, block, 0, st,
-                     (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                     (uint16_t*)a.O, a.LSE, BH, a.S, a.C, a.qsign, a.tau, nqt, a.causal);
+  hipLaunchKernelGGL((fwd_kernel<Cfg, EXPMODE>), grid, block, 0, st, (const uint16_t*)a.Q, (const uint16_t*)a.K,
+                     (const uint16_t*)a.V, (uint16_t*)a.O, a.LSE, BH, a.S, a.C, a.qsign, a.tau, nqt, a.causal);
   prof_end(KID_FWD, st);
   return hipGetLastError();
 }
 
-template <int D>
+template <class Cfg>
 static hipError_t launch_fwd_e(const FwdArgs& a, hipStream_t st) {
   switch (a.exp_mode) {
-    case 1: return launch_fwd_t<D, 1>(a, st);
-    case 2: return launch_fwd_t<D, 2>(a, st);
-    default: return launch_fwd_t<D, 0>(a, st);
+    case 1: return launch_fwd_t<Cfg, 1>(a, st);
+    case 2: return launch_fwd_t<Cfg, 2>(a, st);
+    default: return launch_fwd_t<Cfg, 0>(a, st);
   }
+}
+
+// Tile-configuration variants of the D = 128 kernel, selectable for tuning
+// through the environment variable ATTN97_FWD_VARIANT (0 = default).
+static int fwd_variant() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("ATTN97_FWD_VARIANT");
+    v = e ? atoi(e) : 0;
+  }
+  return v;
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   switch (a.D) {
-    case 64: return launch_fwd_e<64>(a, st);
-    case 128: return launch_fwd_e<128>(a, st);
-    case 256: return launch_fwd_e<256>(a, st);
+    case 64: return launch_fwd_e<FwdDefault<64>::type>(a, st);
+    case 128:
+      switch (fwd_variant()) {
+        case 1: return launch_fwd_e<FwdCfg<128, 64, 8, 3>>(a, st);
+        case 2: return launch_fwd_e<FwdCfg<128, 32, 4, 3>>(a, st);
+        case 3: return launch_fwd_e<FwdCfg<128, 64, 8, 2>>(a, st);
+        case 4: return launch_fwd_e<FwdCfg<128, 64, 4, 3>>(a, st);
+        default: return launch_fwd_e<FwdDefault<128>::type>(a, st);
+      }
+    case 256: return launch_fwd_e<FwdDefault<256>::type>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
