@@ -42,6 +42,8 @@ def _flags():
         "-I", INCLUDE,
         "-I", CSRC,
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # keep private arrays in registers (LLVM would otherwise move some into LDS)
+        "-mllvm", "-disable-promote-alloca-to-lds",
     ]
 
 

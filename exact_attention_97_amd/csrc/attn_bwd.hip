@@ -29,6 +29,7 @@
 // 128 keys and adds it to an fp32 accumulator in global memory.
 #include "attn_kernels.hpp"
 #include "device_common.hpp"
+#include "tile_layout.hpp"
 
 namespace attn97 {
 
@@ -40,27 +41,26 @@ struct BwdCfg {
   static constexpr int NQB = BQ / 32;              // 32-query blocks per tile
   static constexpr int NKS = D / 16;               // reduction steps over D
   static constexpr int NDB = D / 32;               // 32-wide blocks of D
-  static constexpr int QRS = D + 8;                // row stride of Qs / dOs (elements)
-  static constexpr int TRS = BQ + 8;               // row stride of Qt / dOt
-  static constexpr int SRS = BK + 8;               // row stride of dSs / Kt
+  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int SRS = BK + 8;               // row stride of dSs (elements)
   static constexpr int NDQ = NQB * NDB / NW;       // dQ blocks per wavefront
-  static constexpr int UNITS = (BQ / 4) * (D / 8); // 4x8 staging units per tensor
-  static constexpr int UPT = 2 * UNITS / 256;      // staging units per thread (Q and dO)
+  static constexpr int QTILE = BQ * D;             // elements of a Q or dO tile
+  static constexpr int KTILE = BK * D;             // elements of the K tile
+  static constexpr int DMA_Q = QTILE * 2 / 1024 / NW;  // 1 KiB loads per wave per Q (or dO) tile
+  static constexpr int DMA_K = KTILE * 2 / 1024 / NW;  // ... for the K tile
   static_assert(NDQ >= 1 && NQB * NDB == NDQ * NW, "dQ blocks split evenly");
-  static_assert(2 * UNITS % 256 == 0 && UPT >= 1, "staging units split evenly");
+  static_assert(DMA_Q >= 1 && DMA_Q * 1024 * NW == QTILE * 2, "Q tile split over waves");
 };
 
 template <int D>
 struct BwdSmem {
   using Cfg = BwdCfg<D>;
-  uint16_t Qs[Cfg::BQ * Cfg::QRS];
-  uint16_t dOs[Cfg::BQ * Cfg::QRS];
-  uint16_t Qt[D * Cfg::TRS];
-  uint16_t dOt[D * Cfg::TRS];
+  uint16_t Qs[2][Cfg::QTILE];   // swizzled row-major Q tiles (double buffer)
+  uint16_t dOs[2][Cfg::QTILE];  // swizzled row-major dO tiles
+  uint16_t Ks[Cfg::KTILE];      // swizzled row-major K tile of the workgroup
   uint16_t dSs[Cfg::BQ * Cfg::SRS];
-  uint16_t Kt[D * Cfg::SRS];
-  float lse2s[Cfg::BQ];
-  float dlts[Cfg::BQ];
+  float lse[2][Cfg::BQ];
+  float dlt[2][Cfg::BQ];
 };
 
 // Exchange with the neighbouring lane (l ^ 1) through DPP (quad_perm 1,0,3,2).
@@ -75,18 +75,98 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// Two LDS transpose loads (four rows each, at this lane's column) as one
+// MFMA operand.
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* p0, const uint16_t* p1) {
+  const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
+  const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p1));
+  const s16x8 v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Per-lane LDS offsets (elements) fixed over the whole kernel.
+template <int D>
+struct BwdOffsets {
+  using Cfg = BwdCfg<D>;
+  static constexpr int NKS = Cfg::NKS, NDB = Cfg::NDB;
+  // A operand of S = Q K^T and dP = dO V^T: row c32 (+32 qb), chunk 2 ks + h.
+  int arow[NKS];
+  // B operand of dV += P^T dO and dK += dS^T Q (q contraction, rows permuted
+  // like the P / dS registers): rows 8 r2 + 4 h + (i >> 2) (+16 t).
+  int trq[NDB][2];
+  // B operand of dQ += dS K (key contraction, natural key order): rows
+  // 8 h + 4 r2 + (i >> 2) (+16 t).
+  int trk[NDB][2];
+  uint32_t dmaq[Cfg::DMA_Q];
+  uint32_t dmak[Cfg::DMA_K];
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+    const int hh = lane >> 5, c32 = lane & 31, i = lane & 15, g16 = lane >> 4;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) arow[ks] = swz_chunk<D>(c32, 2 * ks + hh) * 8;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = 32 * db + 16 * (g16 & 1) + 4 * (i & 3);
+#pragma unroll
+      for (int r2 = 0; r2 < 2; ++r2) {
+        trq[db][r2] = swz_chunk<D>(8 * r2 + 4 * (g16 >> 1) + (i >> 2), d >> 3) * 8 + (d & 7);
+        trk[db][r2] = swz_chunk<D>(8 * (g16 >> 1) + 4 * r2 + (i >> 2), d >> 3) * 8 + (d & 7);
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < Cfg::DMA_Q; ++n) {
+      int row, c;
+      unswz_chunk<D>(64 * (wave * Cfg::DMA_Q + n) + lane, row, c);
+      dmaq[n] = (uint32_t)(row * D + 8 * c);
+    }
+#pragma unroll
+    for (int n = 0; n < Cfg::DMA_K; ++n) {
+      int row, c;
+      unswz_chunk<D>(64 * (wave * Cfg::DMA_K + n) + lane, row, c);
+      dmak[n] = (uint32_t)(row * D + 8 * c);
+    }
+  }
+};
+
+// Load rows r0.. of a [S, D] bf16 matrix into a swizzled LDS tile with
+// global_load_lds; rows past S are clamped to S-1 (finite data, masked
+// later).  `loff` are this lane's logical element offsets inside the tile.
+template <int D, int NPW>
+__device__ __forceinline__ void dma_rows(const uint16_t* __restrict__ src, int r0, int rows, int S, uint16_t* dst,
+                                         int wave, const uint32_t (&loff)[NPW]) {
+  const uint16_t* tile = src + (size_t)r0 * D;
+  const bool ragged = r0 + rows > S;
+#pragma unroll
+  for (int n = 0; n < NPW; ++n) {
+    uint32_t off = loff[n];
+    if (ragged) {
+      const uint32_t row = off / D;
+      const uint32_t last = (uint32_t)(S - 1 - r0);
+      off = (row > last ? last : row) * D + off % D;
+    }
+    __builtin_amdgcn_global_load_lds(tile + off,
+                                     (__attribute__((address_space(3))) void*)(dst + 512 * (wave * NPW + n)), 16, 0,
+                                     0);
+  }
+}
+
 // One query tile against one wavefront's 32 keys: S = Q K^T and dP = dO V^T,
 // P = exp2(S c - LSE log2e), dS = P (dP - Delta), dS to LDS (queries as rows)
-// for the dQ product, then dV += P^T dO and dK += dS^T Q.  MASK selects the
-// diagonal / ragged path; the interior runs without any masking.
+// for the dQ product, then dV += P^T dO and dK += dS^T Q with the q-major
+// operands read by LDS transpose loads.  MASK selects the diagonal / ragged
+// path; the interior runs without any masking.
 template <int D, bool CAUSAL, bool MASK>
-__device__ __forceinline__ void bwd_tile(BwdSmem<D>& sm, const bf16x8 (&kreg)[D / 16],
-                                         const bf16x8 (&vreg)[D / 16], f32x16 (&dk)[D / 32],
-                                         f32x16 (&dv)[D / 32], int q0, int key, int S, float C, int c32,
-                                         int hh, int dsw) {
+__device__ __forceinline__ void bwd_tile(BwdSmem<D>& sm, int buf, const BwdOffsets<D>& of,
+                                         const bf16x8 (&kreg)[D / 16], const bf16x8 (&vreg)[D / 16],
+                                         f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], int q0, int key, int S, float C,
+                                         int c32, int hh, int dsw) {
   using Cfg = BwdCfg<D>;
-  constexpr int NQB = Cfg::NQB, NKS = Cfg::NKS, NDB = Cfg::NDB, QRS = Cfg::QRS, TRS = Cfg::TRS,
-                SRS = Cfg::SRS;
+  constexpr int NQB = Cfg::NQB, NKS = Cfg::NKS, NDB = Cfg::NDB, SRS = Cfg::SRS, CPR = Cfg::CPR;
+  const uint16_t* Qb = sm.Qs[buf];
+  const uint16_t* dOb = sm.dOs[buf];
   const bool odd = c32 & 1;
   bf16x8 pb[2 * NQB], dsb[2 * NQB];
 #pragma unroll
@@ -94,21 +174,29 @@ __device__ __forceinline__ void bwd_tile(BwdSmem<D>& sm, const bf16x8 (&kreg)[D 
     f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      sacc = mfma32(lds_frag(&sm.Qs[(32 * qb + c32) * QRS + 16 * ks + 8 * hh]), kreg[ks], sacc);
-      dpacc = mfma32(lds_frag(&sm.dOs[(32 * qb + c32) * QRS + 16 * ks + 8 * hh]), vreg[ks], dpacc);
+      sacc = mfma32(lds_frag(Qb + of.arow[ks] + 32 * qb * CPR * 8), kreg[ks], sacc);
+      dpacc = mfma32(lds_frag(dOb + of.arow[ks] + 32 * qb * CPR * 8), vreg[ks], dpacc);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * NKS - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     float p[16], ds[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int qr = 32 * qb + 8 * g + 4 * hh;  // tile row of register 4g
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2s[qr]);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlts[qr]);
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse[buf][qr]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[buf][qr]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * g + e;
-        float pv = exp2_native(__builtin_fmaf(sacc[r], C, -l4[e]));
+        float pv = exp2_native(__builtin_fmaf(sacc[r], C, -l4[e] * kLog2e));
         if (MASK) {
-          if (key >= S || (CAUSAL && key > q0 + qr + e)) pv = 0.0f;
+          const int q = q0 + qr + e;
+          if (key >= S || q >= S || (CAUSAL && key > q)) pv = 0.0f;
         }
         p[r] = pv;
         ds[r] = pv * (dpacc[r] - d4[e]);
@@ -118,10 +206,10 @@ __device__ __forceinline__ void bwd_tile(BwdSmem<D>& sm, const bf16x8 (&kreg)[D 
     pb[2 * qb + 1] = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
     dsb[2 * qb] = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
     dsb[2 * qb + 1] = to_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
-    // dS to LDS with queries as rows.  Lanes l and l^1 hold adjacent keys; for
-    // rows (r, r+1) the even lane writes row r and the odd lane row r+1, each
-    // as one 32-bit pair of adjacent keys (dsw already holds the odd lane's
-    // one-row offset and the even key column).
+    // dS to LDS with queries as rows and keys in natural order.  Lanes l and
+    // l^1 hold adjacent keys; for rows (r, r+1) the even lane writes row r
+    // and the odd lane row r+1, each as one 32-bit pair of adjacent keys
+    // (dsw holds the odd lane's one-row offset and the even key column).
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       const float recv = swap_lane_pair(odd ? ds[r] : ds[r + 1]);
@@ -135,10 +223,18 @@ __device__ __forceinline__ void bwd_tile(BwdSmem<D>& sm, const bf16x8 (&kreg)[D 
   for (int t = 0; t < 2 * NQB; ++t) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      dv[db] = mfma32(pb[t], lds_frag(&sm.dOt[(32 * db + c32) * TRS + 16 * t + 8 * hh]), dv[db]);
-      dk[db] = mfma32(dsb[t], lds_frag(&sm.Qt[(32 * db + c32) * TRS + 16 * t + 8 * hh]), dk[db]);
+      const int o = 16 * t * CPR * 8;
+      dv[db] = mfma32(pb[t], tr_operand(dOb + of.trq[db][0] + o, dOb + of.trq[db][1] + o), dv[db]);
+      dk[db] = mfma32(dsb[t], tr_operand(Qb + of.trq[db][0] + o, Qb + of.trq[db][1] + o), dk[db]);
     }
   }
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+  for (int i = 0; i < 4 * NQB * NDB - 2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
 }
 
 template <int D, bool CAUSAL>
@@ -148,10 +244,10 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
     float* __restrict__ dq32, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int S,
     float scale, float C) {
   using Cfg = BwdCfg<D>;
-  constexpr int BK = Cfg::BK, BQ = Cfg::BQ, NKS = Cfg::NKS, NDB = Cfg::NDB, QRS = Cfg::QRS,
-                TRS = Cfg::TRS, SRS = Cfg::SRS, NDQ = Cfg::NDQ, UNITS = Cfg::UNITS, UPT = Cfg::UPT;
+  constexpr int BK = Cfg::BK, BQ = Cfg::BQ, NKS = Cfg::NKS, NDB = Cfg::NDB, SRS = Cfg::SRS, NDQ = Cfg::NDQ,
+                CPR = Cfg::CPR, DMA_Q = Cfg::DMA_Q, DMA_K = Cfg::DMA_K;
 
-  __shared__ __attribute__((aligned(16))) BwdSmem<D> sm;
+  __shared__ __attribute__((aligned(1024))) BwdSmem<D> sm;
 
   const int id = blockIdx.x;
   const int bh = id % BH;
@@ -173,75 +269,41 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   const int c32 = lane & 31;
   const int kw0 = k0 + 32 * wave;  // first key of this wavefront
   const int key = kw0 + c32;       // this lane's key (MFMA column)
-  const int keyc = min(key, S - 1);
+
+  BwdOffsets<D> of;
+  of.init(wave, lane);
+
+  // per-tile loads: Q and dO tiles by all waves, LSE / Delta (64 floats
+  // each, 4 bytes per lane) by waves 0 / 1
+  auto issue = [&](int qt, int buf) {
+    const int q0 = qt * BQ;
+    dma_rows<D, DMA_Q>(Qh, q0, BQ, S, sm.Qs[buf], wave, of.dmaq);
+    dma_rows<D, DMA_Q>(dOh, q0, BQ, S, sm.dOs[buf], wave, of.dmaq);
+    if (wave < 2) {
+      const float* src = (wave == 0 ? LSEh : dlth) + min(q0 + lane, S - 1);
+      float* dst = (wave == 0) ? sm.lse[buf] : sm.dlt[buf];
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+    }
+  };
+
+  const int nqt = (S + BQ - 1) / BQ;
+  const int qt0 = CAUSAL ? (k0 / BQ) : 0;
+  // the workgroup's K tile (for dQ), the first query tile
+  dma_rows<D, DMA_K>(Kh, k0, BK, S, sm.Ks, wave, of.dmak);
+  issue(qt0, 0);
 
   // K^T / V^T operands of S = Q K^T and dP = dO V^T: lane holds row `key`.
   // Rows past the end are clamped (finite data); their P is masked to zero.
   bf16x8 kreg[NKS], vreg[NKS];
+  {
+    const int keyc = min(key, S - 1);
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    const uint32_t off = (uint32_t)keyc * D + 16 * ks + 8 * hh;
-    kreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(Kh + off));
-    vreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(Vh + off));
+    for (int ks = 0; ks < NKS; ++ks) {
+      const uint32_t off = (uint32_t)keyc * D + 16 * ks + 8 * hh;
+      kreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(Kh + off));
+      vreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(Vh + off));
+    }
   }
-
-  // K transposed into LDS for the dQ product (B operand, keys permuted).
-  for (int u = tid; u < (BK / 4) * (D / 8); u += 256) {
-    const int g = u % (BK / 4);
-    const int c = u / (BK / 4);
-    u32x4 rows[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t kk = min(k0 + 4 * g + i, S - 1);
-      rows[i] = *reinterpret_cast<const u32x4*>(Kh + kk * D + 8 * c);
-    }
-    store_transposed_4x8(sm.Kt, SRS, 8 * c, perm_pos_of_group(g), rows);
-  }
-
-  // Staging of one query tile through registers: UPT units of 4 rows x 8
-  // columns of Q or dO per thread; threads 0..BQ-1 also take LSE and Delta.
-  u32x4 srows[UPT][4];
-  float s_lse = 0.0f, s_dlt = 0.0f;
-  auto stage = [&](int qt) {
-    const int q0 = qt * BQ;
-#pragma unroll
-    for (int j = 0; j < UPT; ++j) {
-      const int u = tid + 256 * j;
-      const uint16_t* src = (u < UNITS) ? Qh : dOh;
-      const int lu = u % UNITS;
-      const int g = lu % (BQ / 4);
-      const int c = lu / (BQ / 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t q = min(q0 + 4 * g + i, S - 1);
-        srows[j][i] = *reinterpret_cast<const u32x4*>(src + q * D + 8 * c);
-      }
-    }
-    if (tid < BQ) {
-      const int q = q0 + tid;
-      s_lse = (q < S) ? LSEh[q] * kLog2e : __builtin_huge_valf();  // rows past the end: P = 0
-      s_dlt = (q < S) ? dlth[q] : 0.0f;
-    }
-  };
-  auto commit = [&]() {
-#pragma unroll
-    for (int j = 0; j < UPT; ++j) {
-      const int u = tid + 256 * j;
-      const bool isq = u < UNITS;
-      const int lu = u % UNITS;
-      const int g = lu % (BQ / 4);
-      const int c = lu / (BQ / 4);
-      uint16_t* rowdst = isq ? sm.Qs : sm.dOs;
-      uint16_t* trdst = isq ? sm.Qt : sm.dOt;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(rowdst + (4 * g + i) * QRS + 8 * c) = srows[j][i];
-      store_transposed_4x8(trdst, TRS, 8 * c, perm_pos_of_group(g), srows[j]);
-    }
-    if (tid < BQ) {
-      sm.lse2s[tid] = s_lse;
-      sm.dlts[tid] = s_dlt;
-    }
-  };
 
   f32x16 dk[NDB], dv[NDB];
 #pragma unroll
@@ -250,27 +312,26 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
     dv[db] = f32x16{};
   }
 
-  const int nqt = (S + BQ - 1) / BQ;
-  const int qt0 = CAUSAL ? (k0 / BQ) : 0;
-  stage(qt0);
-  commit();
-  __syncthreads();
-
   // This lane's dS write column: the even key of its lane pair, one row down
   // for the odd lane.
-  const int dsw = (c32 & 1) * SRS + (perm_pos_of_row(32 * wave + c32) & ~1);
+  const int dsw = (c32 & 1) * SRS + ((32 * wave + c32) & ~1);
+
+  wait_vm_lds<0>();
+  barrier_keep_loads();
 
   for (int qt = qt0; qt < nqt; ++qt) {
+    const int buf = (qt - qt0) & 1;
     const int q0 = qt * BQ;
-    if (qt + 1 < nqt) stage(qt + 1);
+    if (qt + 1 < nqt) issue(qt + 1, buf ^ 1);  // buffer freed by the previous iteration
+    __builtin_amdgcn_sched_barrier(0);
 
     const bool active = !CAUSAL || (q0 + BQ - 1 >= kw0);  // wave-uniform
     if (active) {
-      const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > S);
+      const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > S) || (q0 + BQ > S);
       if (need_mask)
-        bwd_tile<D, CAUSAL, true>(sm, kreg, vreg, dk, dv, q0, key, S, C, c32, hh, dsw);
+        bwd_tile<D, CAUSAL, true>(sm, buf, of, kreg, vreg, dk, dv, q0, key, S, C, c32, hh, dsw);
       else
-        bwd_tile<D, CAUSAL, false>(sm, kreg, vreg, dk, dv, q0, key, S, C, c32, hh, dsw);
+        bwd_tile<D, CAUSAL, false>(sm, buf, of, kreg, vreg, dk, dv, q0, key, S, C, c32, hh, dsw);
     } else {
 #pragma unroll
       for (int r = 0; r < 2 * BQ / 4; r += 2) {
@@ -278,9 +339,8 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
         *reinterpret_cast<uint32_t*>(&sm.dSs[row * SRS + dsw]) = 0u;
       }
     }
-    __syncthreads();  // dSs complete; Q/dO tile no longer read
-
-    if (qt + 1 < nqt) commit();
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (3 << 14));  // lgkmcnt(0): dS stores done
+    barrier_keep_loads();  // dSs complete
 
     // ---- dQ[q, d] += scale * dS K over the workgroup's keys ---------------
 #pragma unroll
@@ -291,10 +351,11 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
       f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
       for (int t = 0; t < BK / 16; t += 2) {
+        const int o0 = 16 * t * CPR * 8, o1 = 16 * (t + 1) * CPR * 8;
         acc0 = mfma32(lds_frag(&sm.dSs[(32 * qb + c32) * SRS + 16 * t + 8 * hh]),
-                      lds_frag(&sm.Kt[(32 * db + c32) * SRS + 16 * t + 8 * hh]), acc0);
+                      tr_operand(sm.Ks + of.trk[db][0] + o0, sm.Ks + of.trk[db][1] + o0), acc0);
         acc1 = mfma32(lds_frag(&sm.dSs[(32 * qb + c32) * SRS + 16 * t + 16 + 8 * hh]),
-                      lds_frag(&sm.Kt[(32 * db + c32) * SRS + 16 * t + 16 + 8 * hh]), acc1);
+                      tr_operand(sm.Ks + of.trk[db][0] + o1, sm.Ks + of.trk[db][1] + o1), acc1);
       }
       const uint32_t off0 = (uint32_t)(q0 + 32 * qb + 4 * hh) * D + 32 * db + c32;
       if (q0 + BQ <= S) {
@@ -309,7 +370,10 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
         }
       }
     }
-    __syncthreads();  // dSs read; next Q/dO tile visible
+    // next tile's loads landed (this wave's) and all LDS reads done; the
+    // barrier publishes the tile and frees dSs
+    __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (0 << 14));  // vmcnt(0) lgkmcnt(0)
+    barrier_keep_loads();
   }
 
   // ---- epilogue: dK = scale * acc, dV = acc (bf16) -------------------------

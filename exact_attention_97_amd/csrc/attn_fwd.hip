@@ -41,6 +41,7 @@
 
 #include "attn_kernels.hpp"
 #include "device_common.hpp"
+#include "tile_layout.hpp"
 
 namespace attn97 {
 
@@ -85,48 +86,6 @@ template <>
 struct FwdDefault<256> {
   using type = FwdCfg<256, 32, 4, 2>;
 };
-
-// s_waitcnt with vmcnt <= N, lgkmcnt = 0, expcnt unconstrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vm_lds() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
-}
-
-// Physical 16-byte chunk index, inside a K or V tile, of logical chunk c of
-// row `row`.  Rows of 256 bytes (D = 128) or 512 bytes (D = 256) XOR the low
-// four bits of the chunk with f(row) = ((row & 3) << 2) | ((row >> 2) & 3),
-// which is distinct over 16 consecutive rows and moves each group of four
-// consecutive rows to distinct 64-byte quarters.  Rows of 128 bytes (D = 64)
-// pair up into 256-byte lines and XOR the chunk-in-line with
-// g(line) = ((line & 1) << 2) | ((line >> 1) & 3).
-template <int D>
-__device__ __forceinline__ int swz_chunk(int row, int c) {
-  if constexpr (D == 64) {
-    const int line = row >> 1;
-    const int cl = ((row & 1) << 3) | c;
-    const int g = ((line & 1) << 2) | ((line >> 1) & 3);
-    return (line << 4) | (cl ^ g);
-  } else {
-    const int f = ((row & 3) << 2) | ((row >> 2) & 3);
-    return row * (D / 8) + (c ^ f);
-  }
-}
-
-// Inverse: logical (row, chunk) stored at physical chunk P.
-template <int D>
-__device__ __forceinline__ void unswz_chunk(int P, int& row, int& c) {
-  if constexpr (D == 64) {
-    const int line = P >> 4;
-    const int g = ((line & 1) << 2) | ((line >> 1) & 3);
-    const int cl = (P & 15) ^ g;
-    row = 2 * line + (cl >> 3);
-    c = cl & 7;
-  } else {
-    row = P / (D / 8);
-    const int f = ((row & 3) << 2) | ((row >> 2) & 3);
-    c = (P % (D / 8)) ^ f;
-  }
-}
 
 // Issue this wave's share of one tile load (rows k0.. of a [S, D] bf16
 // matrix) into the swizzled LDS tile `dst`: lane l of load n fills physical
@@ -445,6 +404,10 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
 
   f32x16 scur[NKB];
   W::scores(Kb[0], of, qreg, scur);
+  // iteration 0 reloads Kb[0] (with K(NBUF)): every wave's reads of K(0)
+  // must be complete first
+  wait_vm_lds<63>();
+  barrier_keep_loads();
 
   for (int kt = 0; kt < nkt; ++kt) {
     n_last = issue(kt);
@@ -459,7 +422,7 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
                                lim, hh, C, tau);
     }
     wait_loads(n_last);
-    __syncthreads();
+    barrier_keep_loads();
   }
 
 // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l) ----------------------
