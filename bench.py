@@ -11,7 +11,11 @@ of the dominant kernel timed with HIP events on its own launch stream, and
 the CPU oracle timed on a bounded sample on the host cores.
 
 Attention flops (algorithmic, not executed): forward 4*B*H*S^2*D, causal
-half of that; backward 2.5x forward.
+half of that; backward 2.5x forward (five S x S x D products).  For the
+per-kernel roofline each kernel is credited with the products it owns: the
+forward kernel two, the split backward's dK/dV kernel four (S, dP, dV, dK)
+and its dQ kernel one (dQ; its recomputation of S and dP is overhead), the
+atomic backward kernel all five.
 """
 
 from __future__ import annotations
@@ -32,8 +36,19 @@ METRIC = "attention TFLOPs/s fwd & bwd, bf16 D=128 S=8192 (causal/non), % of MFM
 PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 B, H, S, D = 2, 16, 8192, 128
 SEED = 2
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_d128_s8192_traffic.md")
-KERNEL_SOURCES = ["exact_attention_97_amd/csrc/attn_bwd.hip", "exact_attention_97_amd/csrc/device_common.hpp"]
+# counter summaries (HBM bytes per launch) of the kernels the roofline may name
+TRAFFIC_FILES = {
+    "bwd_dkdv": os.path.join(ROOT, "profiles", "bwd_dkdv_d128_s8192_traffic.md"),
+    "fwd": os.path.join(ROOT, "profiles", "fwd_d128_s8192_traffic.md"),
+}
+KERNEL_SOURCES = {
+    "bwd_dkdv": ["exact_attention_97_amd/csrc/attn_bwd.hip", "exact_attention_97_amd/csrc/device_common.hpp",
+                 "exact_attention_97_amd/csrc/tile_layout.hpp"],
+    "fwd": ["exact_attention_97_amd/csrc/attn_fwd.hip", "exact_attention_97_amd/csrc/kv_stream.hpp",
+            "exact_attention_97_amd/csrc/device_common.hpp", "exact_attention_97_amd/csrc/tile_layout.hpp"],
+}
+# products (S x S x D, 2 flops each) each kernel is credited with, non-causal
+KERNEL_PRODUCTS = {"fwd": 2, "bwd_main": 5, "bwd_dkdv": 4, "bwd_dq": 1}
 
 
 def fwd_flops(causal):
@@ -45,25 +60,26 @@ def bwd_flops(causal):
     return 2.5 * fwd_flops(causal)
 
 
-def kernel_source_hash():
+def kernel_source_hash(kernel):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per launch of the dominant kernel, from the committed counter summary.
+def read_traffic(kernel):
+    """HBM bytes per launch of `kernel`, from its committed counter summary.
 
     Returns None when the summary is missing or was taken on other kernel sources.
     """
-    if not os.path.exists(TRAFFIC_FILE):
+    path = TRAFFIC_FILES.get(kernel)
+    if path is None or not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash(kernel):
         return None
     return float(m_bytes.group(1))
 
@@ -104,6 +120,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--exp-mode", default="native", choices=["native", "poly", "mixed"])
     ap.add_argument("--tau", type=float, default=8.0)
+    ap.add_argument("--bwd-mode", default="split", choices=["split", "atomic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -127,7 +144,7 @@ def main():
     scale = 1.0 / math.sqrt(D)
     outs = {c: (torch.empty_like(qg), torch.empty((B, H, S), dtype=torch.float32, device=dev)) for c in (False, True)}
     grads = (torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(vg))
-    ws = torch.empty(attn.bwd_workspace_bytes(B, H, S, D), dtype=torch.uint8, device=dev)
+    ws = torch.empty(attn.bwd_workspace_bytes(B, H, S, D, bwd_mode=args.bwd_mode), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def run_pass(causal, which, prof_on):
@@ -137,8 +154,8 @@ def main():
             attn.attn_fwd(qg, kg, vg, scale=scale, causal=causal, exp_mode=args.exp_mode,
                           rescale_tau=args.tau, out=o, lse=lse)
         else:
-            attn.attn_bwd(qg, kg, vg, o, dog, lse, scale=scale, causal=causal, workspace=ws,
-                          dq=grads[0], dk=grads[1], dv=grads[2])
+            attn.attn_bwd(qg, kg, vg, o, dog, lse, scale=scale, causal=causal, bwd_mode=args.bwd_mode,
+                          workspace=ws, dq=grads[0], dk=grads[1], dv=grads[2])
         attn.prof_enable(False)
 
     def step(prof_nc):
@@ -164,9 +181,10 @@ def main():
 
     # per-kernel averages of the non-causal launches inside the timed region
     kern = {}
-    for name in ("fwd", "bwd_pre", "bwd_main", "dq_convert"):
+    for name in ("fwd", "bwd_pre", "bwd_main", "dq_convert", "bwd_dkdv", "bwd_dq"):
         n, ms = attn.prof_collect(name)
-        kern[name] = {"launches": n, "avg_ms": (ms / n) if n else None}
+        if n:
+            kern[name] = {"launches": n, "avg_ms": ms / n}
 
     # ---- per-pass breakdown (separate, untimed for `value`) ----------------
     breakdown = {}
@@ -186,23 +204,22 @@ def main():
                 "ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS, 4)}
 
     # ---- roofline of the dominant kernel ------------------------------------
-    main_ms = kern["bwd_main"]["avg_ms"]
-    fwd_ms = kern["fwd"]["avg_ms"]
-    if main_ms is not None and (fwd_ms is None or main_ms >= fwd_ms):
-        dom, dom_ms, dom_flops = "bwd_main (D=128, non-causal)", main_ms, bwd_flops(False)
-    else:
-        dom, dom_ms, dom_flops = "fwd (D=128, non-causal)", fwd_ms, fwd_flops(False)
+    # dominant = longest average non-causal launch among the MFMA kernels
+    dom = max((k2 for k2 in KERNEL_PRODUCTS if k2 in kern), key=lambda k2: kern[k2]["avg_ms"])
+    dom_ms = kern[dom]["avg_ms"]
+    dom_flops = KERNEL_PRODUCTS[dom] * 2.0 * B * H * S * S * D
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     roofline = {
-        "kernel": dom,
+        "kernel": f"{dom} (D=128, non-causal)",
         "bound": "mfma",
         "achieved": round(achieved, 1),
         "peak": PEAK_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_TFLOPS, 4),
-        "traffic": read_traffic() if dom.startswith("bwd_main") else None,
+        "traffic": read_traffic(dom),
+        "flops_per_launch": dom_flops,
         "avg_launch_ms": round(dom_ms, 4),
-        "launches_timed": kern["bwd_main" if dom.startswith("bwd_main") else "fwd"]["launches"],
+        "launches_timed": kern[dom]["launches"],
     }
 
     result = {
@@ -222,11 +239,11 @@ def main():
             "workload": "exact attention forward+backward, non-causal and causal, bf16, "
                         "B=2 H=16 S=8192 D=128 (Q,K N(0,1) with 1% x20 outliers; V,dO N(0,1); seed 2)",
             "B": B, "H": H, "S": S, "D": D, "exp_mode": args.exp_mode, "rescale_tau": args.tau,
-            "bwd_mode": "atomic",
+            "bwd_mode": args.bwd_mode,
         },
         "frac_of_peak": round(value / PEAK_TFLOPS, 4),
         "breakdown": breakdown,
-        "kernels_noncausal_avg_ms": {k2: (round(v2["avg_ms"], 4) if v2["avg_ms"] else None) for k2, v2 in kern.items()},
+        "kernels_noncausal_avg_ms": {k2: round(v2["avg_ms"], 4) for k2, v2 in kern.items()},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

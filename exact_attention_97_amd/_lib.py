@@ -84,7 +84,7 @@ def _check(fn, code):
         raise AttnError(fn, code, load().attn_strerror(code).decode())
 
 
-def make_opts(exp_mode="native", rescale_tau=8.0, bwd_mode="atomic") -> AttnOpts:
+def make_opts(exp_mode="native", rescale_tau=8.0, bwd_mode="split") -> AttnOpts:
     o = AttnOpts()
     o.exp_mode = EXP_MODES[exp_mode] if isinstance(exp_mode, str) else int(exp_mode)
     o.rescale_tau = float(rescale_tau)
@@ -131,12 +131,12 @@ def attn_fwd(q, k, v, scale=None, causal=False, exp_mode="native", rescale_tau=8
     return out, lse
 
 
-def bwd_workspace_bytes(B, H, S, D, causal=False, bwd_mode="atomic"):
+def bwd_workspace_bytes(B, H, S, D, causal=False, bwd_mode="split"):
     opts = make_opts(bwd_mode=bwd_mode)
     return int(load().attn_bwd_workspace_bytes(B, H, S, D, int(bool(causal)), ctypes.byref(opts)))
 
 
-def attn_bwd(q, k, v, o, do, lse, scale=None, causal=False, bwd_mode="atomic",
+def attn_bwd(q, k, v, o, do, lse, scale=None, causal=False, bwd_mode="split",
              workspace=None, dq=None, dk=None, dv=None, stream=None):
     """Backward pass; returns (dQ, dK, dV), bf16 [B,H,S,D]."""
     import torch

@@ -87,7 +87,7 @@ void attn_default_opts(attn_opts* opts) {
   if (opts == nullptr) return;
   opts->exp_mode = ATTN_EXP_NATIVE;
   opts->rescale_tau = 8.0f;
-  opts->bwd_mode = ATTN_BWD_ATOMIC;
+  opts->bwd_mode = ATTN_BWD_SPLIT;
 }
 
 const char* attn_version(void) { return "attn97 0.1.0 (gfx950)"; }
@@ -163,7 +163,7 @@ attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O,
   attn_opts o;
   st = read_opts(opts, &o);
   if (st != ATTN_OK) return st;
-  if (o.bwd_mode != ATTN_BWD_ATOMIC || !attn97::bwd_supported(D)) return ATTN_ERR_UNSUPPORTED;
+  if (!attn97::bwd_supported(D)) return ATTN_ERR_UNSUPPORTED;
   const size_t need = attn_bwd_workspace_bytes(B, H, S, D, causal, &o);
   if (workspace == nullptr || workspace_bytes < need || misaligned(workspace, 256))
     return ATTN_ERR_WORKSPACE;
@@ -179,14 +179,17 @@ attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O,
   a.dK = dK;
   a.dV = dV;
   a.delta = static_cast<float*>(workspace);
-  a.dq32 = reinterpret_cast<float*>(static_cast<char*>(workspace) + attn97::bwd_delta_bytes(B, H, S));
+  a.dq32 = (o.bwd_mode == ATTN_BWD_ATOMIC)
+               ? reinterpret_cast<float*>(static_cast<char*>(workspace) + attn97::bwd_delta_bytes(B, H, S))
+               : nullptr;
   a.B = B;
   a.H = H;
   a.S = S;
   a.D = D;
   a.causal = causal ? 1 : 0;
   a.scale = scale;
-  hipError_t e = attn97::launch_bwd_atomic(a, (hipStream_t)stream);
+  hipError_t e = (o.bwd_mode == ATTN_BWD_ATOMIC) ? attn97::launch_bwd_atomic(a, (hipStream_t)stream)
+                                                 : attn97::launch_bwd_split(a, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

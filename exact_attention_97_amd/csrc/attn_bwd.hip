@@ -27,17 +27,19 @@
 // The dQ product needs dS with queries as rows, so dS goes through LDS once
 // (bf16); each wavefront then forms a 32x32 block of the tile's dQ over all
 // 128 keys and adds it to an fp32 accumulator in global memory.
+#include <stdlib.h>
+
 #include "attn_kernels.hpp"
 #include "device_common.hpp"
 #include "tile_layout.hpp"
 
 namespace attn97 {
 
-template <int D>
+template <int D, int BQ_ = 64>
 struct BwdCfg {
   static constexpr int NW = 4;                     // wavefronts per workgroup
   static constexpr int BK = 32 * NW;               // keys per workgroup
-  static constexpr int BQ = 64;                    // queries per tile
+  static constexpr int BQ = BQ_;                   // queries per tile
   static constexpr int NQB = BQ / 32;              // 32-query blocks per tile
   static constexpr int NKS = D / 16;               // reduction steps over D
   static constexpr int NDB = D / 32;               // 32-wide blocks of D
@@ -47,20 +49,38 @@ struct BwdCfg {
   static constexpr int QTILE = BQ * D;             // elements of a Q or dO tile
   static constexpr int KTILE = BK * D;             // elements of the K tile
   static constexpr int DMA_Q = QTILE * 2 / 1024 / NW;  // 1 KiB loads per wave per Q (or dO) tile
-  static constexpr int DMA_K = KTILE * 2 / 1024 / NW;  // ... for the K tile
-  static_assert(NDQ >= 1 && NQB * NDB == NDQ * NW, "dQ blocks split evenly");
+  static constexpr int DMA_K = KTILE * 2 / 1024 / NW;  // ... for the K (or V) tile
+  static constexpr int LROWS = BQ < 64 ? 64 : BQ;      // LSE / Delta staging (64 lanes load 64 floats)
   static_assert(DMA_Q >= 1 && DMA_Q * 1024 * NW == QTILE * 2, "Q tile split over waves");
 };
 
-template <int D>
+// LDS of the backward main kernel.  With dQ (atomic mode) it also holds the
+// workgroup's K tile and the bf16 dS tile of the dQ product.
+template <class Cfg, bool WITH_DQ, bool VLDS>
 struct BwdSmem {
-  using Cfg = BwdCfg<D>;
   uint16_t Qs[2][Cfg::QTILE];   // swizzled row-major Q tiles (double buffer)
   uint16_t dOs[2][Cfg::QTILE];  // swizzled row-major dO tiles
   uint16_t Ks[Cfg::KTILE];      // swizzled row-major K tile of the workgroup
   uint16_t dSs[Cfg::BQ * Cfg::SRS];
-  float lse[2][Cfg::BQ];
-  float dlt[2][Cfg::BQ];
+  float lse[2][Cfg::LROWS];
+  float dlt[2][Cfg::LROWS];
+};
+// Without dQ (split mode): Q / dO tiles, LSE / Delta and, with VLDS, the
+// workgroup's V tile (otherwise V rows are held in registers).
+template <class Cfg>
+struct BwdSmem<Cfg, false, true> {
+  uint16_t Qs[2][Cfg::QTILE];
+  uint16_t dOs[2][Cfg::QTILE];
+  uint16_t Vs[Cfg::KTILE];  // swizzled row-major V tile of the workgroup
+  float lse[2][Cfg::LROWS];
+  float dlt[2][Cfg::LROWS];
+};
+template <class Cfg>
+struct BwdSmem<Cfg, false, false> {
+  uint16_t Qs[2][Cfg::QTILE];
+  uint16_t dOs[2][Cfg::QTILE];
+  float lse[2][Cfg::LROWS];
+  float dlt[2][Cfg::LROWS];
 };
 
 // Exchange with the neighbouring lane (l ^ 1) through DPP (quad_perm 1,0,3,2).
@@ -88,9 +108,8 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* p0, const uint16_t*
 }
 
 // Per-lane LDS offsets (elements) fixed over the whole kernel.
-template <int D>
+template <int D, class Cfg>
 struct BwdOffsets {
-  using Cfg = BwdCfg<D>;
   static constexpr int NKS = Cfg::NKS, NDB = Cfg::NDB;
   // A operand of S = Q K^T and dP = dO V^T: row c32 (+32 qb), chunk 2 ks + h.
   int arow[NKS];
@@ -158,12 +177,11 @@ __device__ __forceinline__ void dma_rows(const uint16_t* __restrict__ src, int r
 // for the dQ product, then dV += P^T dO and dK += dS^T Q with the q-major
 // operands read by LDS transpose loads.  MASK selects the diagonal / ragged
 // path; the interior runs without any masking.
-template <int D, bool CAUSAL, bool MASK>
-__device__ __forceinline__ void bwd_tile(BwdSmem<D>& sm, int buf, const BwdOffsets<D>& of,
-                                         const bf16x8 (&kreg)[D / 16], const bf16x8 (&vreg)[D / 16],
-                                         f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], int q0, int key, int S, float C,
-                                         int c32, int hh, int dsw) {
-  using Cfg = BwdCfg<D>;
+template <int D, class Cfg, bool CAUSAL, bool MASK, bool WRITE_DS, bool VLDS>
+__device__ __forceinline__ void bwd_tile(BwdSmem<Cfg, WRITE_DS, VLDS>& sm, int buf, const BwdOffsets<D, Cfg>& of,
+                                         const bf16x8 (&kreg)[D / 16], const bf16x8 (&vreg)[VLDS ? 1 : D / 16],
+                                         const uint16_t* Vw, f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], int q0,
+                                         int key, int S, float C, int c32, int hh, int dsw) {
   constexpr int NQB = Cfg::NQB, NKS = Cfg::NKS, NDB = Cfg::NDB, SRS = Cfg::SRS, CPR = Cfg::CPR;
   const uint16_t* Qb = sm.Qs[buf];
   const uint16_t* dOb = sm.dOs[buf];
@@ -175,7 +193,10 @@ __device__ __forceinline__ void bwd_tile(BwdSmem<D>& sm, int buf, const BwdOffse
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       sacc = mfma32(lds_frag(Qb + of.arow[ks] + 32 * qb * CPR * 8), kreg[ks], sacc);
-      dpacc = mfma32(lds_frag(dOb + of.arow[ks] + 32 * qb * CPR * 8), vreg[ks], dpacc);
+      if constexpr (VLDS)
+        dpacc = mfma32(lds_frag(dOb + of.arow[ks] + 32 * qb * CPR * 8), lds_frag(Vw + of.arow[ks]), dpacc);
+      else
+        dpacc = mfma32(lds_frag(dOb + of.arow[ks] + 32 * qb * CPR * 8), vreg[ks], dpacc);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
@@ -210,13 +231,15 @@ __device__ __forceinline__ void bwd_tile(BwdSmem<D>& sm, int buf, const BwdOffse
     // l^1 hold adjacent keys; for rows (r, r+1) the even lane writes row r
     // and the odd lane row r+1, each as one 32-bit pair of adjacent keys
     // (dsw holds the odd lane's one-row offset and the even key column).
+    if constexpr (WRITE_DS) {
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float recv = swap_lane_pair(odd ? ds[r] : ds[r + 1]);
-      const float lo = odd ? recv : ds[r];
-      const float hi = odd ? ds[r + 1] : recv;
-      const int row = 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
-      *reinterpret_cast<uint32_t*>(&sm.dSs[row * SRS + dsw]) = pack_bf16x2(lo, hi);
+      for (int r = 0; r < 16; r += 2) {
+        const float recv = swap_lane_pair(odd ? ds[r] : ds[r + 1]);
+        const float lo = odd ? recv : ds[r];
+        const float hi = odd ? ds[r + 1] : recv;
+        const int row = 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
+        *reinterpret_cast<uint32_t*>(&sm.dSs[row * SRS + dsw]) = pack_bf16x2(lo, hi);
+      }
     }
   }
 #pragma unroll
@@ -237,17 +260,24 @@ __device__ __forceinline__ void bwd_tile(BwdSmem<D>& sm, int buf, const BwdOffse
   __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_main_kernel(
+// WITH_DQ: dQ is summed here with fp32 atomics (one kernel for the whole
+// backward pass); without it the kernel forms dK and dV only and a separate
+// kernel (attn_bwd_dq.hip) forms dQ.  VLDS (split mode only) reads the V
+// operand from an LDS tile instead of registers; OCC is the target number of
+// workgroups per compute unit.
+template <int D, int BQ_, bool CAUSAL, bool WITH_DQ, bool VLDS, int OCC>
+__global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
     float* __restrict__ dq32, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int S,
     float scale, float C) {
-  using Cfg = BwdCfg<D>;
+  using Cfg = BwdCfg<D, BQ_>;
+  static_assert(!(WITH_DQ && VLDS), "the atomic kernel keeps V in registers");
   constexpr int BK = Cfg::BK, BQ = Cfg::BQ, NKS = Cfg::NKS, NDB = Cfg::NDB, SRS = Cfg::SRS, NDQ = Cfg::NDQ,
                 CPR = Cfg::CPR, DMA_Q = Cfg::DMA_Q, DMA_K = Cfg::DMA_K;
+  static_assert(!WITH_DQ || (NDQ >= 1 && Cfg::NQB * NDB == NDQ * Cfg::NW), "dQ blocks split evenly");
 
-  __shared__ __attribute__((aligned(1024))) BwdSmem<D> sm;
+  __shared__ __attribute__((aligned(1024))) BwdSmem<Cfg, WITH_DQ, VLDS> sm;
 
   const int id = blockIdx.x;
   const int bh = id % BH;
@@ -270,11 +300,11 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   const int kw0 = k0 + 32 * wave;  // first key of this wavefront
   const int key = kw0 + c32;       // this lane's key (MFMA column)
 
-  BwdOffsets<D> of;
+  BwdOffsets<D, Cfg> of;
   of.init(wave, lane);
 
   // per-tile loads: Q and dO tiles by all waves, LSE / Delta (64 floats
-  // each, 4 bytes per lane) by waves 0 / 1
+  // each, 4 bytes per lane, at least BQ of them used) by waves 0 / 1
   auto issue = [&](int qt, int buf) {
     const int q0 = qt * BQ;
     dma_rows<D, DMA_Q>(Qh, q0, BQ, S, sm.Qs[buf], wave, of.dmaq);
@@ -289,21 +319,24 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   const int nqt = (S + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? (k0 / BQ) : 0;
   // the workgroup's K tile (for dQ), the first query tile
-  dma_rows<D, DMA_K>(Kh, k0, BK, S, sm.Ks, wave, of.dmak);
+  if constexpr (WITH_DQ) dma_rows<D, DMA_K>(Kh, k0, BK, S, sm.Ks, wave, of.dmak);
+  if constexpr (VLDS) dma_rows<D, DMA_K>(Vh, k0, BK, S, sm.Vs, wave, of.dmak);
   issue(qt0, 0);
 
   // K^T / V^T operands of S = Q K^T and dP = dO V^T: lane holds row `key`.
   // Rows past the end are clamped (finite data); their P is masked to zero.
-  bf16x8 kreg[NKS], vreg[NKS];
+  bf16x8 kreg[NKS], vreg[VLDS ? 1 : NKS];
   {
     const int keyc = min(key, S - 1);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const uint32_t off = (uint32_t)keyc * D + 16 * ks + 8 * hh;
       kreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(Kh + off));
-      vreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(Vh + off));
+      if constexpr (!VLDS) vreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(Vh + off));
     }
   }
+  const uint16_t* Vw = nullptr;  // this wave's 32 rows of the V tile
+  if constexpr (VLDS) Vw = sm.Vs + 32 * wave * D;
 
   f32x16 dk[NDB], dv[NDB];
 #pragma unroll
@@ -329,18 +362,23 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
     if (active) {
       const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > S) || (q0 + BQ > S);
       if (need_mask)
-        bwd_tile<D, CAUSAL, true>(sm, buf, of, kreg, vreg, dk, dv, q0, key, S, C, c32, hh, dsw);
+        bwd_tile<D, Cfg, CAUSAL, true, WITH_DQ, VLDS>(sm, buf, of, kreg, vreg, Vw, dk, dv, q0, key, S, C, c32, hh,
+                                                      dsw);
       else
-        bwd_tile<D, CAUSAL, false>(sm, buf, of, kreg, vreg, dk, dv, q0, key, S, C, c32, hh, dsw);
+        bwd_tile<D, Cfg, CAUSAL, false, WITH_DQ, VLDS>(sm, buf, of, kreg, vreg, Vw, dk, dv, q0, key, S, C, c32, hh,
+                                                       dsw);
     } else {
+      if constexpr (WITH_DQ) {
 #pragma unroll
-      for (int r = 0; r < 2 * BQ / 4; r += 2) {
-        const int row = 32 * (r >> 4) + 8 * ((r & 15) >> 2) + 4 * hh + (r & 3);
-        *reinterpret_cast<uint32_t*>(&sm.dSs[row * SRS + dsw]) = 0u;
+        for (int r = 0; r < 2 * BQ / 4; r += 2) {
+          const int row = 32 * (r >> 4) + 8 * ((r & 15) >> 2) + 4 * hh + (r & 3);
+          *reinterpret_cast<uint32_t*>(&sm.dSs[row * SRS + dsw]) = 0u;
+        }
       }
     }
-    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (3 << 14));  // lgkmcnt(0): dS stores done
-    barrier_keep_loads();  // dSs complete
+    if constexpr (WITH_DQ) {
+      __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (3 << 14));  // lgkmcnt(0): dS stores done
+      barrier_keep_loads();  // dSs complete
 
     // ---- dQ[q, d] += scale * dS K over the workgroup's keys ---------------
 #pragma unroll
@@ -370,6 +408,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
         }
       }
     }
+    }  // WITH_DQ
     // next tile's loads landed (this wave's) and all LDS reads done; the
     // barrier publishes the tile and frees dSs
     __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (0 << 14));  // vmcnt(0) lgkmcnt(0)
@@ -435,16 +474,17 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict
 
 bool bwd_supported(int D) { return D == 64 || D == 128; }
 
-template <int D, bool CAUSAL>
+template <int D, int BQ, bool CAUSAL, bool WITH_DQ, bool VLDS, int OCC>
 static hipError_t launch_main_t(const BwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
-  const int nkt = (a.S + BwdCfg<D>::BK - 1) / BwdCfg<D>::BK;
-  prof_begin(KID_BWD_MAIN, st);
-  hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL>), dim3(nkt * BH), dim3(256), 0, st,
+  const int nkt = (a.S + BwdCfg<D, BQ>::BK - 1) / BwdCfg<D, BQ>::BK;
+  const int kid = WITH_DQ ? KID_BWD_MAIN : KID_BWD_DKDV;
+  prof_begin(kid, st);
+  hipLaunchKernelGGL((bwd_main_kernel<D, BQ, CAUSAL, WITH_DQ, VLDS, OCC>), dim3(nkt * BH), dim3(256), 0, st,
                      (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                      (const uint16_t*)a.dO, a.LSE, a.delta, a.dq32, (uint16_t*)a.dK,
                      (uint16_t*)a.dV, BH, a.S, a.scale, a.scale * kLog2e);
-  prof_end(KID_BWD_MAIN, st);
+  prof_end(kid, st);
   return hipGetLastError();
 }
 
@@ -459,21 +499,65 @@ static hipError_t launch_pre_t(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_atomic(const BwdArgs& a, hipStream_t st) {
-  hipError_t e;
+// Tile-configuration variants of the split-mode dK/dV kernel, selectable
+// for tuning through the environment variable ATTN97_DKDV_VARIANT
+// (0 = default).
+static int dkdv_variant() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("ATTN97_DKDV_VARIANT");
+    v = e ? atoi(e) : 0;
+  }
+  return v;
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
+  if constexpr (D == 128) {
+    switch (dkdv_variant()) {
+      case 1: return launch_main_t<D, 32, CAUSAL, false, true, 2>(a, st);
+      case 2: return launch_main_t<D, 32, CAUSAL, false, false, 1>(a, st);
+      case 3: return launch_main_t<D, 64, CAUSAL, false, true, 1>(a, st);
+      default: break;
+    }
+    return launch_main_t<D, 64, CAUSAL, false, false, 1>(a, st);
+  }
+  return launch_main_t<D, 32, CAUSAL, false, false, 2>(a, st);
+}
+
+template <bool WITH_DQ>
+static hipError_t launch_main(const BwdArgs& a, hipStream_t st) {
+  if constexpr (WITH_DQ) {
+    switch (a.D * 2 + (a.causal ? 1 : 0)) {
+      case 128: return launch_main_t<64, 64, false, true, false, 1>(a, st);
+      case 129: return launch_main_t<64, 64, true, true, false, 1>(a, st);
+      case 256: return launch_main_t<128, 64, false, true, false, 1>(a, st);
+      case 257: return launch_main_t<128, 64, true, true, false, 1>(a, st);
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (a.D * 2 + (a.causal ? 1 : 0)) {
+      case 128: return launch_dkdv_t<64, false>(a, st);
+      case 129: return launch_dkdv_t<64, true>(a, st);
+      case 256: return launch_dkdv_t<128, false>(a, st);
+      case 257: return launch_dkdv_t<128, true>(a, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+}
+
+static hipError_t launch_pre(const BwdArgs& a, hipStream_t st) {
   switch (a.D) {
-    case 64: e = launch_pre_t<64>(a, st); break;
-    case 128: e = launch_pre_t<128>(a, st); break;
+    case 64: return launch_pre_t<64>(a, st);
+    case 128: return launch_pre_t<128>(a, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_bwd_atomic(const BwdArgs& a, hipStream_t st) {
+  hipError_t e = launch_pre(a, st);
   if (e != hipSuccess) return e;
-  switch (a.D * 2 + (a.causal ? 1 : 0)) {
-    case 128: e = launch_main_t<64, false>(a, st); break;
-    case 129: e = launch_main_t<64, true>(a, st); break;
-    case 256: e = launch_main_t<128, false>(a, st); break;
-    case 257: e = launch_main_t<128, true>(a, st); break;
-    default: return hipErrorInvalidValue;
-  }
+  e = launch_main<true>(a, st);
   if (e != hipSuccess) return e;
   const long n8 = (long)a.B * a.H * a.S * a.D / 8;
   prof_begin(KID_DQ_CONVERT, st);
@@ -481,6 +565,16 @@ hipError_t launch_bwd_atomic(const BwdArgs& a, hipStream_t st) {
                      (const float*)a.dq32, (uint16_t*)a.dQ, n8);
   prof_end(KID_DQ_CONVERT, st);
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_split(const BwdArgs& a, hipStream_t st) {
+  BwdArgs b = a;
+  b.dq32 = nullptr;  // Delta only
+  hipError_t e = launch_pre(b, st);
+  if (e != hipSuccess) return e;
+  e = launch_main<false>(b, st);
+  if (e != hipSuccess) return e;
+  return launch_bwd_dq(b, st);
 }
 
 }  // namespace attn97

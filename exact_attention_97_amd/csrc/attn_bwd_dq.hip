@@ -1,0 +1,240 @@
+// attn_bwd_dq.hip - dQ of the split backward pass (no atomics).
+//
+// The atomic backward pass adds every key tile's contribution to dQ with
+// fp32 atomics; the pages name those atomic additions as an overhead of the
+// backward pass at long sequence lengths (page "FlashAttention-3 и
+// FlashAttention-4", section "Режим 2-CTA MMA"; abstract of
+// "FlashAttention-4: Algorithm and Kernel Pipelining Co-Design for
+// Asymmetric Hardware Scaling").  The split backward pass instead forms dK
+// and dV in one kernel (per key tile) and dQ here, per query tile, walking
+// the key sequence like the forward pass and recomputing what dQ needs:
+//
+//   S^T  = K Q^T           dP^T = V dO^T           (bf16 MFMA)
+//   P    = exp2(S c - LSE log2e)                   (per lane: one query)
+//   dS   = P (dP - Delta)
+//   dQ^T += K^T dS^T      (K^T by LDS transpose loads, dS^T from registers)
+//
+// then dQ = scale * acc in bf16.  No atomics; the result is deterministic.
+// Three products per tile instead of the atomic kernel's one for dQ.
+#include <stdlib.h>
+
+#include "attn_kernels.hpp"
+#include "device_common.hpp"
+#include "kv_stream.hpp"
+#include "tile_layout.hpp"
+
+namespace attn97 {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+template <class Cfg>
+struct DqWave {
+  static constexpr int D = Cfg::D, NKB = Cfg::NKB, NKS = Cfg::NKS, NDB = Cfg::NDB, CPR = Cfg::CPR;
+
+  // One key tile.  MASK: entries with key > lim get P = 0.
+  template <bool MASK>
+  __device__ __forceinline__ static void step(const uint16_t* kt, const uint16_t* vt, const FwdOffsets<Cfg>& of,
+                                              const bf16x8 (&qreg)[NKS], const bf16x8 (&doreg)[NKS],
+                                              f32x16 (&dqacc)[NDB], float C, float nlse2, float dlt, int k0,
+                                              int lim, int hh) {
+    f32x16 sacc[NKB], dpacc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      sacc[kb] = f32x16{};
+      dpacc[kb] = f32x16{};
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int o = of.kfrag[ks] + 32 * kb * CPR * 8;
+        sacc[kb] = mfma32(lds_frag(kt + o), qreg[ks], sacc[kb]);
+        dpacc[kb] = mfma32(lds_frag(vt + o), doreg[ks], dpacc[kb]);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * NKS * NKB - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+
+    bf16x8 dsb[2 * NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        float ds[8];
+#pragma unroll
+        for (int e8 = 0; e8 < 8; ++e8) {
+          const int r = 8 * half + e8;
+          float p = exp2_native(__builtin_fmaf(sacc[kb][r], C, nlse2));
+          if (MASK) {
+            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (key > lim) p = 0.0f;
+          }
+          ds[e8] = p * (dpacc[kb][r] - dlt);
+        }
+        dsb[2 * kb + half] = pack_probs(ds);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2 * NKB; ++t) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int o = 16 * t * CPR * 8;
+        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(kt + of.vfrag[db][0] + o));
+        const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(kt + of.vfrag[db][1] + o));
+        const s16x8 v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+        dqacc[db] = mfma32(__builtin_bit_cast(bf16x8, v), dsb[t], dqacc[db]);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int i = 0; i < 2 * NKB * NDB - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+  }
+};
+
+template <class Cfg, int OCC>
+__global__ __launch_bounds__(64 * Cfg::NW, OCC) void bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
+    uint16_t* __restrict__ dQ, int BH, int S, float scale, float C, int nqt, int causal) {
+  using W = DqWave<Cfg>;
+  constexpr int D = Cfg::D, BC = Cfg::BC, BR = Cfg::BR, NKS = Cfg::NKS, NDB = Cfg::NDB;
+  constexpr int TILE = Cfg::TILE_BYTES / 2;
+
+  __shared__ __attribute__((aligned(1024))) uint16_t Kb[2][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vb[2][TILE];
+
+  // heaviest causal query tiles first; one head's tiles on one XCD when B*H % 8 == 0
+  const int id = blockIdx.x;
+  const int bh = id % BH;
+  const int rank = id / BH;
+  const int qt = causal ? (nqt - 1 - rank) : rank;
+  const int q0 = qt * BR;
+  const size_t base = (size_t)bh * (size_t)S * D;
+  const uint16_t* Kh = K + base;
+  const uint16_t* Vh = V + base;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int hh = lane >> 5;
+  const int c32 = lane & 31;
+  const int qw0 = q0 + wave * 32;
+  const int qrow = qw0 + c32;
+  const int qc = min(qrow, S - 1);
+
+  // Q^T and dO^T operands in registers: lane holds row qrow, d = 16 ks + 8 h ..
+  bf16x8 qreg[NKS], doreg[NKS];
+  {
+    const u32x4* qs = reinterpret_cast<const u32x4*>(Q + base + (size_t)qc * D);
+    const u32x4* ds = reinterpret_cast<const u32x4*>(dO + base + (size_t)qc * D);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      qreg[ks] = as_bf16x8(qs[2 * ks + hh]);
+      doreg[ks] = as_bf16x8(ds[2 * ks + hh]);
+    }
+  }
+  const float nlse2 = -LSE[(size_t)bh * S + qc] * kLog2e;
+  const float dlt = delta[(size_t)bh * S + qc];
+
+  const int kend = causal ? min(S, q0 + BR) : S;
+  const int nkt = (kend + BC - 1) / BC;
+  const int nkt_w = causal ? min(nkt, (qw0 + 32 + BC - 1) / BC) : nkt;
+  int nfull = causal ? (qw0 + 1) / BC : nkt_w;
+  nfull = min(nfull, S / BC);
+  const int lim = causal ? min(qrow, S - 1) : (S - 1);
+
+  FwdOffsets<Cfg> of;
+  of.init(wave, lane);
+
+  f32x16 dqacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16{};
+
+  dma_tile<Cfg>(Kh, 0, S, Kb[0], wave, of.dma);
+  dma_tile<Cfg>(Vh, 0, S, Vb[0], wave, of.dma);
+  wait_vm_lds<0>();
+  barrier_keep_loads();
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nkt) {  // the other buffer was last read in the previous iteration
+      dma_tile<Cfg>(Kh, (kt + 1) * BC, S, Kb[buf ^ 1], wave, of.dma);
+      dma_tile<Cfg>(Vh, (kt + 1) * BC, S, Vb[buf ^ 1], wave, of.dma);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt < nkt_w) {
+      if (kt < nfull)
+        W::template step<false>(Kb[buf], Vb[buf], of, qreg, doreg, dqacc, C, nlse2, dlt, kt * BC, lim, hh);
+      else
+        W::template step<true>(Kb[buf], Vb[buf], of, qreg, doreg, dqacc, C, nlse2, dlt, kt * BC, lim, hh);
+    }
+    wait_vm_lds<0>();
+    barrier_keep_loads();
+  }
+
+  // dQ = scale * acc: lane holds column qrow, rows d = 32 db + 8 g + 4 h + 0..3
+  if (qrow < S) {
+    uint16_t* row = dQ + base + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * hh;
+        *reinterpret_cast<u32x2*>(row + d) = pack_bf16x4(dqacc[db][4 * g] * scale, dqacc[db][4 * g + 1] * scale,
+                                                         dqacc[db][4 * g + 2] * scale, dqacc[db][4 * g + 3] * scale);
+      }
+    }
+  }
+}
+
+template <class Cfg, int OCC>
+static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
+  const int nqt = (a.S + Cfg::BR - 1) / Cfg::BR;
+  const int BH = a.B * a.H;
+  prof_begin(KID_BWD_DQ, st);
+  hipLaunchKernelGGL((bwd_dq_kernel<Cfg, OCC>), dim3(nqt * BH), dim3(64 * Cfg::NW), 0, st, (const uint16_t*)a.Q,
+                     (const uint16_t*)a.K, (const uint16_t*)a.V, (const uint16_t*)a.dO, a.LSE, a.delta,
+                     (uint16_t*)a.dQ, BH, a.S, a.scale, a.scale * kLog2e, nqt, a.causal);
+  prof_end(KID_BWD_DQ, st);
+  return hipGetLastError();
+}
+
+// Tile-configuration variants of the D = 128 kernel, selectable for tuning
+// through the environment variable ATTN97_DQ_VARIANT (0 = default).
+static int dq_variant() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("ATTN97_DQ_VARIANT");
+    v = e ? atoi(e) : 0;
+  }
+  return v;
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
+  switch (a.D) {
+    case 64: return launch_dq_t<FwdCfg<64, 64, 4, 2>, 1>(a, st);
+    case 128:
+      switch (dq_variant()) {
+        case 1: return launch_dq_t<FwdCfg<128, 32, 4, 2>, 1>(a, st);
+        case 2: return launch_dq_t<FwdCfg<128, 64, 4, 2>, 1>(a, st);
+        case 3: return launch_dq_t<FwdCfg<128, 32, 8, 2>, 1>(a, st);
+        case 4: return launch_dq_t<FwdCfg<128, 64, 8, 2>, 1>(a, st);
+        default: return launch_dq_t<FwdCfg<128, 32, 4, 2>, 2>(a, st);
+      }
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace attn97

@@ -42,34 +42,12 @@
 #include "attn_kernels.hpp"
 #include "device_common.hpp"
 #include "tile_layout.hpp"
+#include "kv_stream.hpp"
 
 namespace attn97 {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Tile configuration: head dim D, BC keys per tile, NW wavefronts (32 query
-// rows each) per workgroup, NBUF LDS buffers per K and V tile.  With three
-// buffers, loads are issued two iterations before they are consumed and a
-// wave only waits for the ones issued an iteration earlier.
-template <int D_, int BC_, int NW_, int NBUF_>
-struct FwdCfg {
-  static constexpr int D = D_;
-  static constexpr int BC = BC_;                       // keys per tile
-  static constexpr int NW = NW_;                       // wavefronts per workgroup
-  static constexpr int NBUF = NBUF_;                   // LDS buffers per tile kind
-  static constexpr int BR = 32 * NW;                   // queries per workgroup
-  static constexpr int CPR = D / 8;                    // 16-byte chunks per row
-  static constexpr int TILE_BYTES = BC * D * 2;
-  static constexpr int NKB = BC / 32;                  // 32-key blocks per tile
-  static constexpr int NKS = D / 16;                   // reduction steps over D
-  static constexpr int NDB = D / 32;                   // 32-wide blocks of D
-  static constexpr int DMA_PER_WAVE = TILE_BYTES / 1024 / NW;  // 1 KiB loads per wave per tile
-  static constexpr int LDS_BYTES = 2 * NBUF * TILE_BYTES;
-  static_assert(DMA_PER_WAVE >= 1 && DMA_PER_WAVE * 1024 * NW == TILE_BYTES, "tile split over waves");
-  static_assert(NBUF == 2 || NBUF == 3, "two or three buffers");
-  static_assert(BC % 32 == 0 && BC >= 32, "key tile");
-};
 
 // Default configurations per head dim (measured on MI355X).
 template <int D>
@@ -85,80 +63,6 @@ struct FwdDefault<128> {
 template <>
 struct FwdDefault<256> {
   using type = FwdCfg<256, 32, 4, 2>;
-};
-
-// Issue this wave's share of one tile load (rows k0.. of a [S, D] bf16
-// matrix) into the swizzled LDS tile `dst`: lane l of load n fills physical
-// chunk 64 * (wave * DMA_PER_WAVE + n) + l.  `loff[n]` is that chunk's
-// logical element offset inside the tile (row * D + 8 * chunk), fixed per
-// lane.  In a ragged last tile, rows past S are clamped to S-1 (finite data;
-// the scores of those keys are masked).
-template <class Cfg>
-__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, int k0, int S, uint16_t* dst,
-                                         int wave, const uint32_t (&loff)[Cfg::DMA_PER_WAVE]) {
-  constexpr int NPW = Cfg::DMA_PER_WAVE, BC = Cfg::BC, D = Cfg::D;
-  const uint16_t* tile = src + (size_t)k0 * D;
-  const bool ragged = k0 + BC > S;
-#pragma unroll
-  for (int n = 0; n < NPW; ++n) {
-    uint32_t off = loff[n];
-    if (ragged) {
-      const uint32_t row = off / D;
-      const uint32_t last = (uint32_t)(S - 1 - k0);
-      off = (row > last ? last : row) * D + off % D;
-    }
-    __builtin_amdgcn_global_load_lds(tile + off, (__attribute__((address_space(3))) void*)(dst + 512 * (wave * NPW + n)),
-                                     16, 0, 0);
-  }
-}
-
-// Round eight probabilities to bf16 as four packed 32-bit words for the MFMA
-// operand.  The words are formed as 32-bit scalars: reading 32-bit words
-// back out of a bf16 vector made hipcc reuse one word for all four.  (The
-// row sum is taken from the fp32 values: summing the bf16-rounded ones would
-// put a 2^-9 relative error into the log-sum-exp.)
-__device__ __forceinline__ bf16x8 pack_probs(const float (&p)[8]) {
-  u32x4 w;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    const f32x2 v = {p[2 * m], p[2 * m + 1]};
-    w[m] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-  }
-  return as_bf16x8(w);
-}
-
-// Per-lane LDS offsets (elements) that stay fixed over the whole loop.
-template <class Cfg>
-struct FwdOffsets {
-  static constexpr int D = Cfg::D, NKS = Cfg::NKS, NDB = Cfg::NDB, CPR = Cfg::CPR;
-  // K operand: row c32 (+32 kb), chunk 2 ks + hh.  The swizzle depends on
-  // row & 15 only, so the key block adds 32 * CPR chunks.
-  int kfrag[NKS];
-  // V^T operand: rows 8 r2 + 4 h + (i >> 2) (+16 t), column 32 db + 16 (g & 1)
-  // + 4 (i & 3); the key group adds 16 * CPR chunks.
-  int vfrag[NDB][2];
-  // DMA source offsets of this lane's chunks.
-  uint32_t dma[Cfg::DMA_PER_WAVE];
-
-  __device__ __forceinline__ void init(int wave, int lane) {
-    const int hh = lane >> 5, c32 = lane & 31, i = lane & 15, g16 = lane >> 4;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) kfrag[ks] = swz_chunk<D>(c32, 2 * ks + hh) * 8;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int d = 32 * db + 16 * (g16 & 1) + 4 * (i & 3);
-#pragma unroll
-      for (int r2 = 0; r2 < 2; ++r2)
-        vfrag[db][r2] = swz_chunk<D>(8 * r2 + 4 * (g16 >> 1) + (i >> 2), d >> 3) * 8 + (d & 7);
-    }
-#pragma unroll
-    for (int n = 0; n < Cfg::DMA_PER_WAVE; ++n) {
-      int row, c;
-      unswz_chunk<D>(64 * (wave * Cfg::DMA_PER_WAVE + n) + lane, row, c);
-      dma[n] = (uint32_t)(row * D + 8 * c);
-    }
-  }
 };
 
 template <class Cfg, int EXPMODE>

@@ -57,6 +57,8 @@ void prof_end(int kid, hipStream_t st);
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
 hipError_t launch_exp2_eval(const float* x, float* y, long n, int mode, hipStream_t st);
 hipError_t launch_bwd_atomic(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_split(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st);
 bool bwd_supported(int D);
 
 }  // namespace attn97

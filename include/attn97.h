@@ -80,10 +80,10 @@ typedef struct {
                           (Conditional softmax rescaling: abstract of "FlashAttention-4:
                           Algorithm and Kernel Pipelining Co-Design for Asymmetric Hardware
                           Scaling".)  The result is the same for every tau up to rounding.  */
-    int bwd_mode;      /* attn_bwd_mode; default ATTN_BWD_ATOMIC                               */
+    int bwd_mode;      /* attn_bwd_mode; default ATTN_BWD_SPLIT                                */
 } attn_opts;
 
-/* Defaults: {ATTN_EXP_NATIVE, 8.0f, ATTN_BWD_ATOMIC}. */
+/* Defaults: {ATTN_EXP_NATIVE, 8.0f, ATTN_BWD_SPLIT}. */
 void attn_default_opts(attn_opts* opts);
 
 /*

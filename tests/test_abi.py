@@ -49,7 +49,7 @@ def test_default_opts():
     o = L.AttnOpts()
     o.exp_mode, o.rescale_tau, o.bwd_mode = 7, -1.0, 7
     lib.attn_default_opts(ctypes.byref(o))
-    assert (o.exp_mode, o.rescale_tau, o.bwd_mode) == (0, 8.0, 0)
+    assert (o.exp_mode, o.rescale_tau, o.bwd_mode) == (0, 8.0, 1)
 
 
 def fwd(**kw):
@@ -113,13 +113,14 @@ def test_bwd_bad_options():
 
 def test_workspace_bytes():
     lib = L.load()
-    o = L.make_opts()
+    o = L.make_opts(bwd_mode="atomic")
     B, H, S, D = 2, 3, 100, 128
     delta = (B * H * S * 4 + 255) // 256 * 256
     assert lib.attn_bwd_workspace_bytes(B, H, S, D, 0, ctypes.byref(o)) == delta + B * H * S * D * 4
-    assert lib.attn_bwd_workspace_bytes(B, H, S, D, 1, None) == delta + B * H * S * D * 4
+    assert lib.attn_bwd_workspace_bytes(B, H, S, D, 1, ctypes.byref(o)) == delta + B * H * S * D * 4
     o.bwd_mode = 1
     assert lib.attn_bwd_workspace_bytes(B, H, S, D, 0, ctypes.byref(o)) == delta
+    assert lib.attn_bwd_workspace_bytes(B, H, S, D, 1, None) == delta
     assert lib.attn_bwd_workspace_bytes(0, H, S, D, 0, None) == 0
     assert lib.attn_bwd_workspace_bytes(B, H, S, 80, 0, None) == 0
 

@@ -119,13 +119,14 @@ def test_fwd_constant_v():
 @pytest.mark.parametrize("D", (64, 128))
 @pytest.mark.parametrize("S", SMALL_S)
 @pytest.mark.parametrize("causal", (False, True))
-def test_bwd_small(D, S, causal):
-    print(f"[bwd small] D={D} S={S} causal={causal}", flush=True)
+@pytest.mark.parametrize("bwd_mode", ("atomic", "split"))
+def test_bwd_small(D, S, causal, bwd_mode):
+    print(f"[bwd small] D={D} S={S} causal={causal} mode={bwd_mode}", flush=True)
     q, k, v, do = make_qkvdo(1, 2, S, D, seed=200 + S + D)
     scale = 1.0 / math.sqrt(D)
     qg, kg, vg, dog = _gpu(q, k, v, do)
     o, lse = L.attn_fwd(qg, kg, vg, scale=scale, causal=causal)
-    dq, dk, dv = L.attn_bwd(qg, kg, vg, o, dog, lse, scale=scale, causal=causal)
+    dq, dk, dv = L.attn_bwd(qg, kg, vg, o, dog, lse, scale=scale, causal=causal, bwd_mode=bwd_mode)
     rdq, rdk, rdv = oracle.attention_bwd(q, k, v, do, scale, causal)
     _assert_close("dQ", _np(dq), rdq)
     _assert_close("dK", _np(dk), rdk)
@@ -136,6 +137,33 @@ def test_bwd_small(D, S, causal):
     assert np.max(np.abs(_np(dv).sum(axis=2) - _np(dog).sum(axis=2))) <= n * O_MEAN + O_MAX
     if causal:
         assert np.max(np.abs(_np(dq)[:, :, 0])) <= 1e-3
+
+
+def test_bwd_split_deterministic_and_matches_atomic():
+    """The split backward pass uses no atomics: two runs are bitwise equal; it
+    agrees with the atomic pass within the tolerances."""
+    q, k, v, do = _gpu(*make_qkvdo(2, 4, 1100, 128, seed=21))
+    for causal in (False, True):
+        o, lse = L.attn_fwd(q, k, v, causal=causal)
+        a = L.attn_bwd(q, k, v, o, do, lse, causal=causal, bwd_mode="split")
+        b = L.attn_bwd(q, k, v, o, do, lse, causal=causal, bwd_mode="split")
+        c = L.attn_bwd(q, k, v, o, do, lse, causal=causal, bwd_mode="atomic")
+        for x, y, z, nm in zip(a, b, c, ("dQ", "dK", "dV")):
+            assert bool((x == y).all()), f"split {nm} not bitwise repeatable"
+            _assert_close(f"{nm} split vs atomic", _np(x), _np(z))
+
+
+def test_bwd_split_full_size():
+    import torch
+
+    w = WORKLOADS["bwd8k"]
+    q, k, v, do = make_workload(w)
+    qg, kg, vg, dog = _gpu(q, k, v, do)
+    for causal in w.causal:
+        o, lse = L.attn_fwd(qg, kg, vg, scale=w.scale, causal=causal)
+        dq, dk, dv = L.attn_bwd(qg, kg, vg, o, dog, lse, scale=w.scale, causal=causal, bwd_mode="split")
+        torch.cuda.synchronize()
+        _check_bwd_heads(w, q, k, v, do, dq, dk, dv, causal, [(1, 9)])
 
 
 def test_bwd_d256_reported_unsupported():
