@@ -44,6 +44,9 @@ def _flags():
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         # keep private arrays in registers (LLVM would otherwise move some into LDS)
         "-mllvm", "-disable-promote-alloca-to-lds",
+        # MFMA results in arch VGPRs: with accumulators in AGPRs the compiler
+        # copies them back and forth every loop iteration in the one-wave kernels
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
     ]
 
 

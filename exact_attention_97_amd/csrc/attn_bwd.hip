@@ -175,17 +175,25 @@ __device__ __forceinline__ void dma_rows(const uint16_t* __restrict__ src, int r
 // One query tile against one wavefront's 32 keys: S = Q K^T and dP = dO V^T,
 // P = exp2(S c - LSE log2e), dS = P (dP - Delta), dS to LDS (queries as rows)
 // for the dQ product, then dV += P^T dO and dK += dS^T Q with the q-major
-// operands read by LDS transpose loads.  MASK selects the diagonal / ragged
-// path; the interior runs without any masking.
-template <int D, class Cfg, bool CAUSAL, bool MASK, bool WRITE_DS, bool VLDS>
+// operands read by LDS transpose loads.  need_mask (wave-uniform) applies
+// the diagonal / ragged mask after the exponentials; one code path serves
+// every tile, so the operand reads stay inside the step's read-ahead
+// schedule.
+template <int D, class Cfg, bool CAUSAL, bool WRITE_DS, bool VLDS>
 __device__ __forceinline__ void bwd_tile(BwdSmem<Cfg, WRITE_DS, VLDS>& sm, int buf, const BwdOffsets<D, Cfg>& of,
                                          const bf16x8 (&kreg)[D / 16], const bf16x8 (&vreg)[VLDS ? 1 : D / 16],
                                          const uint16_t* Vw, f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], int q0,
-                                         int key, int S, float C, int c32, int hh, int dsw) {
+                                         int key, int S, float C, int c32, int hh, int dsw, bool need_mask) {
   constexpr int NQB = Cfg::NQB, NKS = Cfg::NKS, NDB = Cfg::NDB, SRS = Cfg::SRS, CPR = Cfg::CPR;
   const uint16_t* Qb = sm.Qs[buf];
   const uint16_t* dOb = sm.dOs[buf];
   const bool odd = c32 & 1;
+  // Register (qb, g, e) holds query q0 + 4 hh + c, c = 32 qb + 8 g + e.  It
+  // is kept iff that query is < S, this lane's key is < S and (causal)
+  // key <= query: as a range of the constant part, mlo <= c < mhi.
+  const int mt = q0 + 4 * hh;
+  const int mlo = CAUSAL ? key - mt : 0;
+  const int mhi = key < S ? S - mt : -1;
   bf16x8 pb[2 * NQB], dsb[2 * NQB];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
@@ -198,11 +206,24 @@ __device__ __forceinline__ void bwd_tile(BwdSmem<Cfg, WRITE_DS, VLDS>& sm, int b
       else
         dpacc = mfma32(lds_frag(dOb + of.arow[ks] + 32 * qb * CPR * 8), vreg[ks], dpacc);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    // two reduction steps of operands read ahead of the MFMAs (Q, dO and,
+    // with VLDS, V fragments: 2 or 3 LDS reads per step of two MFMAs)
+    if constexpr (VLDS) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * NKS - 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int i = 0; i < NKS - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * NKS - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     float p[16], ds[16];
@@ -210,18 +231,21 @@ __device__ __forceinline__ void bwd_tile(BwdSmem<Cfg, WRITE_DS, VLDS>& sm, int b
     for (int g = 0; g < 4; ++g) {
       const int qr = 32 * qb + 8 * g + 4 * hh;  // tile row of register 4g
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse[buf][qr]);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[buf][qr]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g + e;
-        float pv = exp2_native(__builtin_fmaf(sacc[r], C, -l4[e] * kLog2e));
-        if (MASK) {
-          const int q = q0 + qr + e;
-          if (key >= S || q >= S || (CAUSAL && key > q)) pv = 0.0f;
-        }
-        p[r] = pv;
-        ds[r] = pv * (dpacc[r] - d4[e]);
+      for (int e = 0; e < 4; ++e) p[4 * g + e] = exp2_native(__builtin_fmaf(sacc[4 * g + e], C, -l4[e] * kLog2e));
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = 32 * qb + 8 * (r >> 2) + (r & 3);
+        if (!(c >= mlo && c < mhi)) p[r] = 0.0f;
       }
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[buf][32 * qb + 8 * g + 4 * hh]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ds[4 * g + e] = p[4 * g + e] * (dpacc[4 * g + e] - d4[e]);
     }
     pb[2 * qb] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
     pb[2 * qb + 1] = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
@@ -361,12 +385,8 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
     const bool active = !CAUSAL || (q0 + BQ - 1 >= kw0);  // wave-uniform
     if (active) {
       const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > S) || (q0 + BQ > S);
-      if (need_mask)
-        bwd_tile<D, Cfg, CAUSAL, true, WITH_DQ, VLDS>(sm, buf, of, kreg, vreg, Vw, dk, dv, q0, key, S, C, c32, hh,
-                                                      dsw);
-      else
-        bwd_tile<D, Cfg, CAUSAL, false, WITH_DQ, VLDS>(sm, buf, of, kreg, vreg, Vw, dk, dv, q0, key, S, C, c32, hh,
-                                                       dsw);
+      bwd_tile<D, Cfg, CAUSAL, WITH_DQ, VLDS>(sm, buf, of, kreg, vreg, Vw, dk, dv, q0, key, S, C, c32, hh, dsw,
+                                              need_mask);
     } else {
       if constexpr (WITH_DQ) {
 #pragma unroll

@@ -167,6 +167,11 @@ struct FwdWave {
     const float alpha = (grow && m_new != kNegInf) ? exp2_native(m_run - m_new) : 1.0f;
     m_run = grow ? m_new : m_run;
     l_part *= alpha;
+    // Region 1 runs at raised wave priority: of the two wavefronts sharing a
+    // SIMD, the one issuing score MFMAs interleaved with softmax work is
+    // preferred over one in its P V phase, which keeps the matrix unit fed
+    // (measured: about 4% faster than equal priority).
+    __builtin_amdgcn_s_setprio(1);
     scores(knext, of, qreg, snext);
     probs<MASK>(scur, C, m_run, pb, l_part);
     // Schedule: the K fragment reads run four ahead of the MFMAs that use
@@ -192,6 +197,7 @@ struct FwdWave {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
     }
+    __builtin_amdgcn_s_setprio(0);
     pv(vcur, of, pb, oacc);
     // PV: transpose reads run four ahead (two per MFMA operand).
     constexpr int NP = 2 * NKB * NDB;

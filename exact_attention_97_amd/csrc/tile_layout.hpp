@@ -57,4 +57,17 @@ __device__ __forceinline__ void wait_vm_lds() {
 // clobber keeps the compiler from moving LDS accesses across the barrier.
 __device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_barrier" ::: "memory"); }
 
+// Distinct empty asm at the top of the masked and the unmasked variant of a
+// tile step.  Both variants begin with the same LDS operand reads; without a
+// differing first instruction the compiler merges those reads into the block
+// before the branch, outside the reach of the step's read-ahead schedule,
+// and holds every fragment of the tile in registers at once.
+template <bool MASK>
+__device__ __forceinline__ void tile_marker() {
+  if constexpr (MASK)
+    asm volatile("; masked tile" ::: "memory");
+  else
+    asm volatile("; interior tile" ::: "memory");
+}
+
 }  // namespace attn97

@@ -1,0 +1,74 @@
+"""Launch driver for hardware-counter and kernel-trace runs.
+
+Runs, in one process: an optional device-to-device copy of known size (the
+calibration kernel for the HBM byte counters: it reads and writes exactly
+``--copy-mib`` MiB), then ``--iters`` launches of each requested attention
+pass on the headline shape's synthetic inputs.  It prints one line per step
+and nothing else, so a counter run over it sees only these kernels plus
+input set-up.
+
+    python3 -m exact_attention_97_amd.profile_driver --passes fwd,bwd --iters 2 --copy-mib 1024
+"""
+
+from __future__ import annotations
+
+import argparse
+import math
+
+import torch
+
+from . import _lib as L
+from .inputs import make_qkvdo
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--passes", default="fwd,bwd", help="comma list of fwd, bwd")
+    ap.add_argument("--causal", type=int, default=0)
+    ap.add_argument("--B", type=int, default=2)
+    ap.add_argument("--H", type=int, default=16)
+    ap.add_argument("--S", type=int, default=8192)
+    ap.add_argument("--D", type=int, default=128)
+    ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--iters", type=int, default=2)
+    ap.add_argument("--bwd-mode", default="split", choices=["split", "atomic"])
+    ap.add_argument("--copy-mib", type=int, default=0, help="MiB of the calibration copy (0 = none)")
+    a = ap.parse_args()
+    if not torch.cuda.is_available():
+        raise SystemExit("profile_driver needs a GPU")
+    L.load()
+    dev = torch.device("cuda:0")
+
+    if a.copy_mib > 0:
+        x = torch.ones(a.copy_mib << 18, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+        print(f"copy {a.copy_mib} MiB done", flush=True)
+        del x, y
+
+    q, k, v, do = (t.to(dev) for t in make_qkvdo(a.B, a.H, a.S, a.D, a.seed))
+    scale = 1.0 / math.sqrt(a.D)
+    causal = bool(a.causal)
+    o, lse = L.attn_fwd(q, k, v, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    passes = [p for p in a.passes.split(",") if p]
+    for p in passes:
+        if p == "fwd":
+            for _ in range(a.iters):
+                L.attn_fwd(q, k, v, scale=scale, causal=causal, out=o, lse=lse)
+        elif p == "bwd":
+            ws = torch.empty(L.bwd_workspace_bytes(a.B, a.H, a.S, a.D, causal, bwd_mode=a.bwd_mode),
+                             dtype=torch.uint8, device=dev)
+            g = [torch.empty_like(q) for _ in range(3)]
+            for _ in range(a.iters):
+                L.attn_bwd(q, k, v, o, do, lse, scale=scale, causal=causal, bwd_mode=a.bwd_mode,
+                           workspace=ws, dq=g[0], dk=g[1], dv=g[2])
+        else:
+            raise SystemExit(f"unknown pass {p!r}")
+        torch.cuda.synchronize()
+        print(f"{p} x{a.iters} done", flush=True)
+
+
+if __name__ == "__main__":
+    main()
