@@ -143,7 +143,7 @@ size_t attn_bwd_workspace_bytes(int B, int H, int S, int D, int causal, const at
   if (check_shape(B, H, S, D) != ATTN_OK) return 0;
   attn_opts o;
   if (read_opts(opts, &o) != ATTN_OK) return 0;
-  size_t n = attn97::bwd_delta_bytes(B, H, S);
+  size_t n = 2 * attn97::bwd_delta_bytes(B, H, S);
   if (o.bwd_mode == ATTN_BWD_ATOMIC) n += attn97::bwd_dq32_bytes(B, H, S, D);
   return n;
 }
@@ -178,10 +178,11 @@ attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O,
   a.dQ = dQ;
   a.dK = dK;
   a.dV = dV;
+  const size_t vec_bytes = attn97::bwd_delta_bytes(B, H, S);
   a.delta = static_cast<float*>(workspace);
-  a.dq32 = (o.bwd_mode == ATTN_BWD_ATOMIC)
-               ? reinterpret_cast<float*>(static_cast<char*>(workspace) + attn97::bwd_delta_bytes(B, H, S))
-               : nullptr;
+  a.nlse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + vec_bytes);
+  a.dq32 = (o.bwd_mode == ATTN_BWD_ATOMIC) ? reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * vec_bytes)
+                                          : nullptr;
   a.B = B;
   a.H = H;
   a.S = S;

@@ -4,7 +4,8 @@
 // pass recomputes the probabilities from them:
 //
 //   Delta_i = sum_d dO_id O_id                       (bwd_pre_kernel)
-//   P  = exp2(S * scale*log2e - LSE*log2e),  S = Q K^T
+//   P  = exp2(S * scale*log2e - LSE*log2e),  S = Q K^T   (-LSE log2e from
+//                                                       bwd_pre_kernel)
 //   dV += P^T dO,   dP = dO V^T,   dS = P * (dP - Delta)
 //   dK += dS^T Q,   dQ += dS K                       (bwd_main_kernel)
 //   dQ (bf16) = fp32 accumulator                     (dq_convert_kernel)
@@ -62,7 +63,7 @@ struct BwdSmem {
   uint16_t dOs[2][Cfg::QTILE];  // swizzled row-major dO tiles
   uint16_t Ks[Cfg::KTILE];      // swizzled row-major K tile of the workgroup
   uint16_t dSs[Cfg::BQ * Cfg::SRS];
-  float lse[2][Cfg::LROWS];
+  float lse[2][Cfg::LROWS];  // -LSE log2(e) of the tile's rows
   float dlt[2][Cfg::LROWS];
 };
 // Without dQ (split mode): Q / dO tiles, LSE / Delta and, with VLDS, the
@@ -232,7 +233,7 @@ __device__ __forceinline__ void bwd_tile(BwdSmem<Cfg, WRITE_DS, VLDS>& sm, int b
       const int qr = 32 * qb + 8 * g + 4 * hh;  // tile row of register 4g
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse[buf][qr]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) p[4 * g + e] = exp2_native(__builtin_fmaf(sacc[4 * g + e], C, -l4[e] * kLog2e));
+      for (int e = 0; e < 4; ++e) p[4 * g + e] = exp2_native(__builtin_fmaf(sacc[4 * g + e], C, l4[e]));
     }
     if (need_mask) {
 #pragma unroll
@@ -284,6 +285,162 @@ __device__ __forceinline__ void bwd_tile(BwdSmem<Cfg, WRITE_DS, VLDS>& sm, int b
   __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
 }
 
+// ---- split mode: one 64-query tile in four software-pipelined phases -------
+//
+// With one wavefront per SIMD, the matrix unit idles whenever the wavefront
+// is busy with the softmax VALU work or waits for an MFMA result.  The tile's
+// two 32-query blocks are therefore staggered so that each phase pairs MFMAs
+// with independent VALU work of the other block:
+//
+//   A: S, dP of block 0
+//   B: S, dP of block 1        | softmax of block 0 (P, dS -> bf16)
+//   C: dV, dK with block 0     | softmax of block 1
+//   D: dV, dK with block 1
+//
+// (the softmax overlapping the matrix products of another block, page
+// "FlashAttention-3 и FlashAttention-4", section "Чередование matmul и
+// softmax").  Scheduling barriers keep each phase's instructions together and
+// interleave them in fixed proportions.
+
+// One score element of the softmax: P = exp2(S c - LSE log2e), masked, and
+// dS = P (dP - Delta).  r is the accumulator register (row 8 (r/4) + 4 hh +
+// r%4 of block qb), nl / dl the block's -LSE log2e and Delta.
+template <bool MASK>
+__device__ __forceinline__ void dkdv_elem(const f32x16& sacc, const f32x16& dpacc, int r, float nl, float dl,
+                                          float C, int c, int mlo, int mhi, float& p, float& ds) {
+  float pv = exp2_native(__builtin_fmaf(sacc[r], C, nl));
+  if (MASK) pv = (c >= mlo && c < mhi) ? pv : 0.0f;
+  p = pv;
+  ds = pv * (dpacc[r] - dl);
+}
+
+template <int D, class Cfg, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void dkdv_tile(BwdSmem<Cfg, false, false>& sm, int buf, const BwdOffsets<D, Cfg>& of,
+                                          const bf16x8 (&kreg)[D / 16], const bf16x8 (&vreg)[D / 16],
+                                          f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], int q0, int key, int S,
+                                          float C, int hh) {
+  static_assert(Cfg::NQB == 2 && D / 16 == 8 && D / 32 == 4, "two 32-query blocks, D = 128");
+  constexpr int NKS = Cfg::NKS, NDB = Cfg::NDB, CPR = Cfg::CPR;
+  tile_marker<MASK>();
+  const uint16_t* Qb = sm.Qs[buf];
+  const uint16_t* dOb = sm.dOs[buf];
+  const float* nl = sm.lse[buf];
+  const float* dl = sm.dlt[buf];
+  int mlo = 0, mhi = 0;
+  if constexpr (MASK) {  // register (qb, g, e) holds query q0 + 4 hh + 32 qb + 8 g + e
+    const int mt = q0 + 4 * hh;
+    mlo = CAUSAL ? key - mt : 0;
+    mhi = key < S ? S - mt : -1;
+  }
+  auto qfrag = [&](int qb, int ks) { return lds_frag(Qb + of.arow[ks] + 32 * qb * CPR * 8); };
+  auto dofrag = [&](int qb, int ks) { return lds_frag(dOb + of.arow[ks] + 32 * qb * CPR * 8); };
+  auto trdo = [&](int t, int db) {
+    const int o = 16 * t * CPR * 8;
+    return tr_operand(dOb + of.trq[db][0] + o, dOb + of.trq[db][1] + o);
+  };
+  auto trq = [&](int t, int db) {
+    const int o = 16 * t * CPR * 8;
+    return tr_operand(Qb + of.trq[db][0] + o, Qb + of.trq[db][1] + o);
+  };
+
+  f32x16 s0 = f32x16{}, dp0 = f32x16{}, s1 = f32x16{}, dp1 = f32x16{};
+  float p[16], ds[16];
+  bf16x8 pb0[2], dsb0[2], pb1[2], dsb1[2];
+
+  // A: S, dP of block 0; operand reads two steps ahead
+  {
+    bf16x8 qa[NKS], da[NKS];
+    qa[0] = qfrag(0, 0); da[0] = dofrag(0, 0);
+    qa[1] = qfrag(0, 1); da[1] = dofrag(0, 1);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (ks + 2 < NKS) { qa[ks + 2] = qfrag(0, ks + 2); da[ks + 2] = dofrag(0, ks + 2); }
+      s0 = mfma32(qa[ks], kreg[ks], s0);
+      dp0 = mfma32(da[ks], vreg[ks], dp0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // B: S, dP of block 1, each step with two elements of block 0's softmax
+  {
+    bf16x8 qa[NKS], da[NKS];
+    f32x4 l4[4], d4[4];
+    qa[0] = qfrag(1, 0); da[0] = dofrag(1, 0);
+    l4[0] = *reinterpret_cast<const f32x4*>(&nl[4 * hh]);
+    d4[0] = *reinterpret_cast<const f32x4*>(&dl[4 * hh]);
+    qa[1] = qfrag(1, 1); da[1] = dofrag(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (ks + 2 < NKS) { qa[ks + 2] = qfrag(1, ks + 2); da[ks + 2] = dofrag(1, ks + 2); }
+      if ((ks & 1) == 0 && ks / 2 + 1 < 4) {
+        const int g = ks / 2 + 1;
+        l4[g] = *reinterpret_cast<const f32x4*>(&nl[8 * g + 4 * hh]);
+        d4[g] = *reinterpret_cast<const f32x4*>(&dl[8 * g + 4 * hh]);
+      }
+      s1 = mfma32(qa[ks], kreg[ks], s1);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int r = 2 * ks + u, g = r >> 2, e = r & 3;
+        dkdv_elem<MASK>(s0, dp0, r, l4[g][e], d4[g][e], C, 8 * g + e, mlo, mhi, p[r], ds[r]);
+      }
+      dp1 = mfma32(da[ks], vreg[ks], dp1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    pb0[0] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+    pb0[1] = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
+    dsb0[0] = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+    dsb0[1] = to_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
+  }
+  // C: dV, dK with block 0, each MFMA with one element of block 1's softmax
+  {
+    bf16x8 ta[2 * NDB], tb[2 * NDB];  // [t][db] transposed dO / Q operands
+    f32x4 l4[4], d4[4];
+    ta[0] = trdo(0, 0); tb[0] = trq(0, 0);
+    l4[0] = *reinterpret_cast<const f32x4*>(&nl[32 + 4 * hh]);
+    d4[0] = *reinterpret_cast<const f32x4*>(&dl[32 + 4 * hh]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 2 * NDB; ++i) {  // i = 4 t + db
+      const int t = i / NDB, db = i % NDB;
+      if (i + 1 < 2 * NDB) { ta[i + 1] = trdo((i + 1) / NDB, (i + 1) % NDB); tb[i + 1] = trq((i + 1) / NDB, (i + 1) % NDB); }
+      if ((i & 1) == 0 && i / 2 + 1 < 4) {
+        const int g = i / 2 + 1;
+        l4[g] = *reinterpret_cast<const f32x4*>(&nl[32 + 8 * g + 4 * hh]);
+        d4[g] = *reinterpret_cast<const f32x4*>(&dl[32 + 8 * g + 4 * hh]);
+      }
+      dv[db] = mfma32(pb0[t], ta[i], dv[db]);
+      {
+        const int r = 2 * i, g = r >> 2, e = r & 3;
+        dkdv_elem<MASK>(s1, dp1, r, l4[g][e], d4[g][e], C, 32 + 8 * g + e, mlo, mhi, p[r], ds[r]);
+      }
+      dk[db] = mfma32(dsb0[t], tb[i], dk[db]);
+      {
+        const int r = 2 * i + 1, g = r >> 2, e = r & 3;
+        dkdv_elem<MASK>(s1, dp1, r, l4[g][e], d4[g][e], C, 32 + 8 * g + e, mlo, mhi, p[r], ds[r]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    pb1[0] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+    pb1[1] = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
+    dsb1[0] = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+    dsb1[1] = to_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
+  }
+  // D: dV, dK with block 1; transposed operands one step ahead
+  {
+    bf16x8 ta[2 * NDB], tb[2 * NDB];
+    ta[0] = trdo(2, 0); tb[0] = trq(2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 2 * NDB; ++i) {
+      const int t = i / NDB, db = i % NDB;
+      if (i + 1 < 2 * NDB) { ta[i + 1] = trdo(2 + (i + 1) / NDB, (i + 1) % NDB); tb[i + 1] = trq(2 + (i + 1) / NDB, (i + 1) % NDB); }
+      dv[db] = mfma32(pb1[t], ta[i], dv[db]);
+      dk[db] = mfma32(dsb1[t], tb[i], dk[db]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 // WITH_DQ: dQ is summed here with fp32 atomics (one kernel for the whole
 // backward pass); without it the kernel forms dK and dV only and a separate
 // kernel (attn_bwd_dq.hip) forms dQ.  VLDS (split mode only) reads the V
@@ -292,7 +449,7 @@ __device__ __forceinline__ void bwd_tile(BwdSmem<Cfg, WRITE_DS, VLDS>& sm, int b
 template <int D, int BQ_, bool CAUSAL, bool WITH_DQ, bool VLDS, int OCC>
 __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
+    const uint16_t* __restrict__ dO, const float* __restrict__ nlse2, const float* __restrict__ delta,
     float* __restrict__ dq32, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int S,
     float scale, float C) {
   using Cfg = BwdCfg<D, BQ_>;
@@ -312,7 +469,7 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
   const uint16_t* Kh = K + base;
   const uint16_t* Vh = V + base;
   const uint16_t* dOh = dO + base;
-  const float* LSEh = LSE + (size_t)bh * S;
+  const float* LSEh = nlse2 + (size_t)bh * S;
   const float* dlth = delta + (size_t)bh * S;
   float* dqh = dq32 + base;
 
@@ -327,8 +484,8 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
   BwdOffsets<D, Cfg> of;
   of.init(wave, lane);
 
-  // per-tile loads: Q and dO tiles by all waves, LSE / Delta (64 floats
-  // each, 4 bytes per lane, at least BQ of them used) by waves 0 / 1
+  // per-tile loads: Q and dO tiles by all waves, -LSE log2e / Delta (64
+  // floats each, 4 bytes per lane, at least BQ of them used) by waves 0 / 1
   auto issue = [&](int qt, int buf) {
     const int q0 = qt * BQ;
     dma_rows<D, DMA_Q>(Qh, q0, BQ, S, sm.Qs[buf], wave, of.dmaq);
@@ -385,8 +542,15 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
     const bool active = !CAUSAL || (q0 + BQ - 1 >= kw0);  // wave-uniform
     if (active) {
       const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > S) || (q0 + BQ > S);
-      bwd_tile<D, Cfg, CAUSAL, WITH_DQ, VLDS>(sm, buf, of, kreg, vreg, Vw, dk, dv, q0, key, S, C, c32, hh, dsw,
-                                              need_mask);
+      if constexpr (!WITH_DQ && !VLDS && Cfg::NQB == 2) {
+        if (need_mask)
+          dkdv_tile<D, Cfg, CAUSAL, true>(sm, buf, of, kreg, vreg, dk, dv, q0, key, S, C, hh);
+        else
+          dkdv_tile<D, Cfg, CAUSAL, false>(sm, buf, of, kreg, vreg, dk, dv, q0, key, S, C, hh);
+      } else {
+        bwd_tile<D, Cfg, CAUSAL, WITH_DQ, VLDS>(sm, buf, of, kreg, vreg, Vw, dk, dv, q0, key, S, C, c32, hh, dsw,
+                                                need_mask);
+      }
     } else {
       if constexpr (WITH_DQ) {
 #pragma unroll
@@ -450,12 +614,14 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
   }
 }
 
-// Delta_i = sum_d dO_id O_id (fp32) and zero the fp32 dQ accumulator.
-// D/8 lanes share one row; each lane takes eight columns.
+// Delta_i = sum_d dO_id O_id (fp32), nlse2_i = -LSE_i log2(e), and zero the
+// fp32 dQ accumulator (atomic mode).  D/8 lanes share one row; each lane
+// takes eight columns.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ O,
                                                       const uint16_t* __restrict__ dO,
-                                                      float* __restrict__ delta,
+                                                      const float* __restrict__ LSE,
+                                                      float* __restrict__ delta, float* __restrict__ nlse2,
                                                       float* __restrict__ dq32, long rows) {
   constexpr int LPR = D / 8;
   const long row = ((long)blockIdx.x * 256 + threadIdx.x) / LPR;
@@ -477,7 +643,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
   }
 #pragma unroll
   for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (c == 0 && row < rows) delta[row] = acc;
+  if (c == 0 && row < rows) {
+    delta[row] = acc;
+    nlse2[row] = -LSE[row] * kLog2e;
+  }
 }
 
 // dQ (bf16) from the fp32 accumulator, eight elements per thread.
@@ -502,7 +671,7 @@ static hipError_t launch_main_t(const BwdArgs& a, hipStream_t st) {
   prof_begin(kid, st);
   hipLaunchKernelGGL((bwd_main_kernel<D, BQ, CAUSAL, WITH_DQ, VLDS, OCC>), dim3(nkt * BH), dim3(256), 0, st,
                      (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                     (const uint16_t*)a.dO, a.LSE, a.delta, a.dq32, (uint16_t*)a.dK,
+                     (const uint16_t*)a.dO, a.nlse2, a.delta, a.dq32, (uint16_t*)a.dK,
                      (uint16_t*)a.dV, BH, a.S, a.scale, a.scale * kLog2e);
   prof_end(kid, st);
   return hipGetLastError();
@@ -514,7 +683,7 @@ static hipError_t launch_pre_t(const BwdArgs& a, hipStream_t st) {
   const long threads = rows * (D / 8);
   prof_begin(KID_BWD_PRE, st);
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
-                     (const uint16_t*)a.O, (const uint16_t*)a.dO, a.delta, a.dq32, rows);
+                     (const uint16_t*)a.O, (const uint16_t*)a.dO, a.LSE, a.delta, a.nlse2, a.dq32, rows);
   prof_end(KID_BWD_PRE, st);
   return hipGetLastError();
 }

@@ -106,7 +106,7 @@ struct DqWave {
 template <class Cfg, int OCC>
 __global__ __launch_bounds__(64 * Cfg::NW, OCC) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
+    const uint16_t* __restrict__ dO, const float* __restrict__ nlse2v, const float* __restrict__ delta,
     uint16_t* __restrict__ dQ, int BH, int S, float scale, float C, int nqt, int causal) {
   using W = DqWave<Cfg>;
   constexpr int D = Cfg::D, BC = Cfg::BC, BR = Cfg::BR, NKS = Cfg::NKS, NDB = Cfg::NDB;
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(64 * Cfg::NW, OCC) void bwd_dq_kernel(
       doreg[ks] = as_bf16x8(ds[2 * ks + hh]);
     }
   }
-  const float nlse2 = -LSE[(size_t)bh * S + qc] * kLog2e;
+  const float nlse2 = nlse2v[(size_t)bh * S + qc];  // -LSE log2(e)
   const float dlt = delta[(size_t)bh * S + qc];
 
   const int kend = causal ? min(S, q0 + BR) : S;
@@ -205,7 +205,7 @@ static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   prof_begin(KID_BWD_DQ, st);
   hipLaunchKernelGGL((bwd_dq_kernel<Cfg, OCC>), dim3(nqt * BH), dim3(64 * Cfg::NW), 0, st, (const uint16_t*)a.Q,
-                     (const uint16_t*)a.K, (const uint16_t*)a.V, (const uint16_t*)a.dO, a.LSE, a.delta,
+                     (const uint16_t*)a.K, (const uint16_t*)a.V, (const uint16_t*)a.dO, a.nlse2, a.delta,
                      (uint16_t*)a.dQ, BH, a.S, a.scale, a.scale * kLog2e, nqt, a.causal);
   prof_end(KID_BWD_DQ, st);
   return hipGetLastError();

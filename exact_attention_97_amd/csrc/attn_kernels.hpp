@@ -31,14 +31,16 @@ struct BwdArgs {
   void* dQ;
   void* dK;
   void* dV;
-  float* delta;  // workspace: fp32 [B,H,S]
+  float* delta;  // workspace: fp32 [B,H,S], Delta_i = sum_d dO_id O_id
+  float* nlse2;  // workspace: fp32 [B,H,S], -LSE_i * log2(e)
   float* dq32;   // workspace: fp32 [B,H,S,D] (atomic mode)
   int B, H, S, D;
   int causal;
   float scale;
 };
 
-// Workspace layout of attn_bwd: delta (rounded up to 256 bytes), then dq32.
+// Workspace layout of attn_bwd: delta and nlse2 (each rounded up to 256
+// bytes), then dq32 in atomic mode.
 inline size_t bwd_delta_bytes(int B, int H, int S) {
   size_t n = (size_t)B * H * S * sizeof(float);
   return (n + 255) & ~(size_t)255;

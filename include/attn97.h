@@ -99,9 +99,11 @@ attn_status attn_fwd(const void* Q, const void* K, const void* V, void* O, float
                      const attn_opts* opts, void* stream);
 
 /*
- * Bytes of device workspace attn_bwd needs for this shape and mode: the
- * per-row Delta_i = sum_d dO_id * O_id (fp32 [B,H,S]) and, in ATTN_BWD_ATOMIC
- * mode, the fp32 dQ accumulator [B,H,S,D].  Returns 0 for invalid shapes.
+ * Bytes of device workspace attn_bwd needs for this shape and mode: two
+ * per-row fp32 vectors [B,H,S] (Delta_i = sum_d dO_id * O_id, and
+ * -LSE_i * log2(e)), each padded to a multiple of 256 bytes, and, in
+ * ATTN_BWD_ATOMIC mode, the fp32 dQ accumulator [B,H,S,D].  Returns 0 for
+ * invalid shapes.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int S, int D, int causal, const attn_opts* opts);
 
