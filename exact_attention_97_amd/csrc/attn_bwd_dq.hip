@@ -18,6 +18,8 @@
 // Three products per tile instead of the atomic kernel's one for dQ.
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "attn_kernels.hpp"
 #include "device_common.hpp"
 #include "kv_stream.hpp"
@@ -103,12 +105,114 @@ struct DqWave {
   }
 };
 
-template <class Cfg, int OCC>
+// Two 32-key blocks per tile, software-pipelined like the dK/dV tile:
+//   A: S^T, dP^T of block 0
+//   B: S^T, dP^T of block 1   | softmax of block 0
+//   C: dQ^T with block 0      | softmax of block 1
+//   D: dQ^T with block 1
+// Source-level chunks separated by scheduling barriers fix the interleave;
+// operand reads are issued one chunk ahead.
+template <class Cfg>
+struct DqWavePipe {
+  static constexpr int D = Cfg::D, NKS = Cfg::NKS, NDB = Cfg::NDB, CPR = Cfg::CPR;
+  static_assert(Cfg::NKB == 2, "two 32-key blocks per tile");
+
+  template <bool MASK>
+  __device__ __forceinline__ static void elem(const f32x16& sacc, const f32x16& dpacc, int r, float C, float nlse2,
+                                              float dlt, int key, int lim, float& ds) {
+    float p = exp2_native(__builtin_fmaf(sacc[r], C, nlse2));
+    if (MASK) p = (key > lim) ? 0.0f : p;
+    ds = p * (dpacc[r] - dlt);
+  }
+
+  template <bool MASK>
+  __device__ __forceinline__ static void step(const uint16_t* kt, const uint16_t* vt, const FwdOffsets<Cfg>& of,
+                                              const bf16x8 (&qreg)[NKS], const bf16x8 (&doreg)[NKS],
+                                              f32x16 (&dqacc)[NDB], float C, float nlse2, float dlt, int k0,
+                                              int lim, int hh) {
+    tile_marker<MASK>();
+    auto kfrag = [&](int kb, int ks) { return lds_frag(kt + of.kfrag[ks] + 32 * kb * CPR * 8); };
+    auto vfrag = [&](int kb, int ks) { return lds_frag(vt + of.kfrag[ks] + 32 * kb * CPR * 8); };
+    auto ktr = [&](int t, int db) {  // K^T operand of the 16 keys of step t
+      const int o = 16 * t * CPR * 8;
+      const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(kt + of.vfrag[db][0] + o));
+      const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(kt + of.vfrag[db][1] + o));
+      const s16x8 v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+      return __builtin_bit_cast(bf16x8, v);
+    };
+    // key of accumulator register r in block kb
+    auto keyof = [&](int kb, int r) { return k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3); };
+
+    f32x16 s0 = f32x16{}, dp0 = f32x16{}, s1 = f32x16{}, dp1 = f32x16{};
+    float ds[16];
+    bf16x8 dsb0[2], dsb1[2];
+
+    {  // A
+      bf16x8 ka[NKS], va[NKS];
+      ka[0] = kfrag(0, 0); va[0] = vfrag(0, 0);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (ks + 1 < NKS) { ka[ks + 1] = kfrag(0, ks + 1); va[ks + 1] = vfrag(0, ks + 1); }
+        s0 = mfma32(ka[ks], qreg[ks], s0);
+        dp0 = mfma32(va[ks], doreg[ks], dp0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    {  // B
+      bf16x8 ka[NKS], va[NKS];
+      ka[0] = kfrag(1, 0); va[0] = vfrag(1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (ks + 1 < NKS) { ka[ks + 1] = kfrag(1, ks + 1); va[ks + 1] = vfrag(1, ks + 1); }
+        s1 = mfma32(ka[ks], qreg[ks], s1);
+        elem<MASK>(s0, dp0, 2 * ks, C, nlse2, dlt, keyof(0, 2 * ks), lim, ds[2 * ks]);
+        dp1 = mfma32(va[ks], doreg[ks], dp1);
+        elem<MASK>(s0, dp0, 2 * ks + 1, C, nlse2, dlt, keyof(0, 2 * ks + 1), lim, ds[2 * ks + 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      dsb0[0] = pack_probs(*reinterpret_cast<float(*)[8]>(&ds[0]));
+      dsb0[1] = pack_probs(*reinterpret_cast<float(*)[8]>(&ds[8]));
+    }
+    {  // C
+      bf16x8 ta[2 * NDB];
+      ta[0] = ktr(0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 2 * NDB; ++i) {  // i = NDB t + db
+        const int t = i / NDB, db = i % NDB;
+        if (i + 1 < 2 * NDB) ta[i + 1] = ktr((i + 1) / NDB, (i + 1) % NDB);
+        dqacc[db] = mfma32(ta[i], t == 0 ? dsb0[0] : dsb0[1], dqacc[db]);
+        elem<MASK>(s1, dp1, 2 * i, C, nlse2, dlt, keyof(1, 2 * i), lim, ds[2 * i]);
+        elem<MASK>(s1, dp1, 2 * i + 1, C, nlse2, dlt, keyof(1, 2 * i + 1), lim, ds[2 * i + 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      dsb1[0] = pack_probs(*reinterpret_cast<float(*)[8]>(&ds[0]));
+      dsb1[1] = pack_probs(*reinterpret_cast<float(*)[8]>(&ds[8]));
+    }
+    {  // D
+      bf16x8 ta[2 * NDB];
+      ta[0] = ktr(2, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 2 * NDB; ++i) {
+        const int t = i / NDB, db = i % NDB;
+        if (i + 1 < 2 * NDB) ta[i + 1] = ktr(2 + (i + 1) / NDB, (i + 1) % NDB);
+        dqacc[db] = mfma32(ta[i], t == 0 ? dsb1[0] : dsb1[1], dqacc[db]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+};
+
+template <class Cfg, int OCC, bool PIPE>
 __global__ __launch_bounds__(64 * Cfg::NW, OCC) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ nlse2v, const float* __restrict__ delta,
     uint16_t* __restrict__ dQ, int BH, int S, float scale, float C, int nqt, int causal) {
-  using W = DqWave<Cfg>;
+  using W = typename std::conditional<PIPE, DqWavePipe<Cfg>, DqWave<Cfg>>::type;
   constexpr int D = Cfg::D, BC = Cfg::BC, BR = Cfg::BR, NKS = Cfg::NKS, NDB = Cfg::NDB;
   constexpr int TILE = Cfg::TILE_BYTES / 2;
 
@@ -199,12 +303,12 @@ __global__ __launch_bounds__(64 * Cfg::NW, OCC) void bwd_dq_kernel(
   }
 }
 
-template <class Cfg, int OCC>
+template <class Cfg, int OCC, bool PIPE = false>
 static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
   const int nqt = (a.S + Cfg::BR - 1) / Cfg::BR;
   const int BH = a.B * a.H;
   prof_begin(KID_BWD_DQ, st);
-  hipLaunchKernelGGL((bwd_dq_kernel<Cfg, OCC>), dim3(nqt * BH), dim3(64 * Cfg::NW), 0, st, (const uint16_t*)a.Q,
+  hipLaunchKernelGGL((bwd_dq_kernel<Cfg, OCC, PIPE>), dim3(nqt * BH), dim3(64 * Cfg::NW), 0, st, (const uint16_t*)a.Q,
                      (const uint16_t*)a.K, (const uint16_t*)a.V, (const uint16_t*)a.dO, a.nlse2, a.delta,
                      (uint16_t*)a.dQ, BH, a.S, a.scale, a.scale * kLog2e, nqt, a.causal);
   prof_end(KID_BWD_DQ, st);
@@ -212,7 +316,8 @@ static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
 }
 
 // Tile-configuration variants of the D = 128 kernel, selectable for tuning
-// through the environment variable ATTN97_DQ_VARIANT (0 = default).
+// through the environment variable ATTN97_DQ_VARIANT (0 = default: 64-key
+// tiles in the pipelined step, two workgroups of four wavefronts per CU).
 static int dq_variant() {
   static int v = -1;
   if (v < 0) {
@@ -227,11 +332,9 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
     case 64: return launch_dq_t<FwdCfg<64, 64, 4, 2>, 1>(a, st);
     case 128:
       switch (dq_variant()) {
-        case 1: return launch_dq_t<FwdCfg<128, 32, 4, 2>, 1>(a, st);
-        case 2: return launch_dq_t<FwdCfg<128, 64, 4, 2>, 1>(a, st);
-        case 3: return launch_dq_t<FwdCfg<128, 32, 8, 2>, 1>(a, st);
-        case 4: return launch_dq_t<FwdCfg<128, 64, 8, 2>, 1>(a, st);
-        default: return launch_dq_t<FwdCfg<128, 32, 4, 2>, 2>(a, st);
+        case 1: return launch_dq_t<FwdCfg<128, 32, 4, 2>, 2>(a, st);        // 32-key tiles, one block per step
+        case 2: return launch_dq_t<FwdCfg<128, 64, 8, 2>, 1, true>(a, st);  // eight wavefronts per workgroup
+        default: return launch_dq_t<FwdCfg<128, 64, 4, 2>, 2, true>(a, st);
       }
     default: return hipErrorInvalidValue;
   }

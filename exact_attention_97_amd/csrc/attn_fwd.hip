@@ -153,10 +153,9 @@ struct FwdWave {
   // stale but finite buffer) so that region 1 has no branch.
   template <bool MASK>
   __device__ __forceinline__ static void step(const uint16_t* knext, const uint16_t* vcur, const FwdOffsets<Cfg>& of,
-                                              const bf16x8 (&qreg)[NKS], f32x16 (&scur)[NKB], f32x16 (&oacc)[NDB],
-                                              float& m_run, float& l_part, int k0, int lim, int hh, float C,
-                                              float tau) {
-    f32x16 snext[NKB];
+                                              const bf16x8 (&qreg)[NKS], f32x16 (&scur)[NKB],
+                                              f32x16 (&snext)[NKB], f32x16 (&oacc)[NDB], float& m_run,
+                                              float& l_part, int k0, int lim, int hh, float C, float tau) {
     bf16x8 pb[2 * NKB];
     const float mx = tile_max<MASK>(scur, k0, lim, hh);
     const float mxs = (mx == kNegInf) ? kNegInf : mx * C;
@@ -208,8 +207,6 @@ struct FwdWave {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) scur[kb] = snext[kb];
   }
 };
 
@@ -312,27 +309,32 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
   wait_loads(n_last);
   __syncthreads();
 
-  f32x16 scur[NKB];
-  W::scores(Kb[0], of, qreg, scur);
+  // scores of the current and the next tile; the loop is unrolled by two so
+  // that the two sets swap roles instead of being copied
+  f32x16 sa[NKB], sb[NKB];
+  W::scores(Kb[0], of, qreg, sa);
   // iteration 0 reloads Kb[0] (with K(NBUF)): every wave's reads of K(0)
   // must be complete first
   wait_vm_lds<63>();
   barrier_keep_loads();
 
-  for (int kt = 0; kt < nkt; ++kt) {
+  auto iteration = [&](int kt, f32x16(&scur)[NKB], f32x16(&snext)[NKB]) {
     n_last = issue(kt);
     __builtin_amdgcn_sched_barrier(0);  // keep the load issue out of the compute schedule
-
     if (kt < nkt_w) {
       if (kt < nfull)
-        W::template step<false>(Kb[(kt + 1) % NBUF], Vb[kt % NBUF], of, qreg, scur, oacc, m_run, l_part, kt * BC,
-                                lim, hh, C, tau);
+        W::template step<false>(Kb[(kt + 1) % NBUF], Vb[kt % NBUF], of, qreg, scur, snext, oacc, m_run, l_part,
+                                kt * BC, lim, hh, C, tau);
       else
-        W::template step<true>(Kb[(kt + 1) % NBUF], Vb[kt % NBUF], of, qreg, scur, oacc, m_run, l_part, kt * BC,
-                               lim, hh, C, tau);
+        W::template step<true>(Kb[(kt + 1) % NBUF], Vb[kt % NBUF], of, qreg, scur, snext, oacc, m_run, l_part,
+                               kt * BC, lim, hh, C, tau);
     }
     wait_loads(n_last);
     barrier_keep_loads();
+  };
+  for (int kt = 0; kt < nkt; kt += 2) {
+    iteration(kt, sa, sb);
+    if (kt + 1 < nkt) iteration(kt + 1, sb, sa);
   }
 
 // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l) ----------------------
