@@ -113,6 +113,29 @@ def cpu_baseline(q, k, v, do, budget_s=15.0, max_heads=32):
     }
 
 
+def gemm_reference(torch, dev, M=16384, N=16384, K=8192, reps=10):
+    """Throughput of a large plain bf16 GEMM through torch.matmul (hipBLASLt) on the same GPU.
+
+    Context for the roofline: what a vendor-tuned dense contraction sustains on
+    this part under its power limit, beside the published peak.
+    """
+    a = torch.randn(M, K, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(K, N, device=dev, dtype=torch.bfloat16)
+    for _ in range(2):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    return {"tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1), "shape": f"{M}x{N}x{K} bf16",
+            "library": "torch.matmul (hipBLASLt)", "frac_of_peak": round(2.0 * M * N * K / (ms * 1e-3) / 1e12 / PEAK_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,6 +268,7 @@ def main():
         "breakdown": breakdown,
         "kernels_noncausal_avg_ms": {k2: round(v2["avg_ms"], 4) for k2, v2 in kern.items()},
         "roofline": roofline,
+        "gemm_reference": gemm_reference(torch, dev),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(q, k, v, do)

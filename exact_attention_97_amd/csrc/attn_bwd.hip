@@ -153,24 +153,27 @@ struct BwdOffsets {
 
 // Load rows r0.. of a [S, D] bf16 matrix into a swizzled LDS tile with
 // global_load_lds; rows past S are clamped to S-1 (finite data, masked
-// later).  `loff` are this lane's logical element offsets inside the tile.
+// later).  `loff` are this lane's logical element offsets inside the tile;
+// dma_row_part issues this wave's n-th 1 KiB piece only.
+template <int D, int NPW>
+__device__ __forceinline__ void dma_row_part(const uint16_t* __restrict__ src, int r0, int rows, int S, uint16_t* dst,
+                                             int wave, const uint32_t (&loff)[NPW], int n) {
+  const uint16_t* tile = src + (size_t)r0 * D;
+  uint32_t off = loff[n];
+  if (r0 + rows > S) {
+    const uint32_t row = off / D;
+    const uint32_t last = (uint32_t)(S - 1 - r0);
+    off = (row > last ? last : row) * D + off % D;
+  }
+  __builtin_amdgcn_global_load_lds(tile + off, (__attribute__((address_space(3))) void*)(dst + 512 * (wave * NPW + n)),
+                                   16, 0, 0);
+}
+
 template <int D, int NPW>
 __device__ __forceinline__ void dma_rows(const uint16_t* __restrict__ src, int r0, int rows, int S, uint16_t* dst,
                                          int wave, const uint32_t (&loff)[NPW]) {
-  const uint16_t* tile = src + (size_t)r0 * D;
-  const bool ragged = r0 + rows > S;
 #pragma unroll
-  for (int n = 0; n < NPW; ++n) {
-    uint32_t off = loff[n];
-    if (ragged) {
-      const uint32_t row = off / D;
-      const uint32_t last = (uint32_t)(S - 1 - r0);
-      off = (row > last ? last : row) * D + off % D;
-    }
-    __builtin_amdgcn_global_load_lds(tile + off,
-                                     (__attribute__((address_space(3))) void*)(dst + 512 * (wave * NPW + n)), 16, 0,
-                                     0);
-  }
+  for (int n = 0; n < NPW; ++n) dma_row_part<D, NPW>(src, r0, rows, S, dst, wave, loff, n);
 }
 
 // One query tile against one wavefront's 32 keys: S = Q K^T and dP = dO V^T,
@@ -446,7 +449,7 @@ __device__ __forceinline__ void dkdv_tile(BwdSmem<Cfg, false, false>& sm, int bu
 // kernel (attn_bwd_dq.hip) forms dQ.  VLDS (split mode only) reads the V
 // operand from an LDS tile instead of registers; OCC is the target number of
 // workgroups per compute unit.
-template <int D, int BQ_, bool CAUSAL, bool WITH_DQ, bool VLDS, int OCC>
+template <int D, int BQ_, bool CAUSAL, bool WITH_DQ, bool VLDS, int OCC, bool KV_AGPR = true>
 __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ nlse2, const float* __restrict__ delta,
@@ -514,6 +517,15 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
       const uint32_t off = (uint32_t)keyc * D + 16 * ks + 8 * hh;
       kreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(Kh + off));
       if constexpr (!VLDS) vreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(Vh + off));
+      if constexpr (KV_AGPR && !WITH_DQ && !VLDS) {
+        // The pipelined tile needs more than the 256 arch VGPRs; K and V are
+        // read only as MFMA operands, which gfx950 takes from AGPRs, so they
+        // are placed there once instead of being spilled and reloaded.
+        u32x4 kk = __builtin_bit_cast(u32x4, kreg[ks]), vv = __builtin_bit_cast(u32x4, vreg[ks]);
+        asm volatile("" : "+a"(kk), "+a"(vv));
+        kreg[ks] = __builtin_bit_cast(bf16x8, kk);
+        vreg[ks] = __builtin_bit_cast(bf16x8, vv);
+      }
     }
   }
   const uint16_t* Vw = nullptr;  // this wave's 32 rows of the V tile
@@ -663,13 +675,13 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict
 
 bool bwd_supported(int D) { return D == 64 || D == 128; }
 
-template <int D, int BQ, bool CAUSAL, bool WITH_DQ, bool VLDS, int OCC>
+template <int D, int BQ, bool CAUSAL, bool WITH_DQ, bool VLDS, int OCC, bool KV_AGPR = true>
 static hipError_t launch_main_t(const BwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   const int nkt = (a.S + BwdCfg<D, BQ>::BK - 1) / BwdCfg<D, BQ>::BK;
   const int kid = WITH_DQ ? KID_BWD_MAIN : KID_BWD_DKDV;
   prof_begin(kid, st);
-  hipLaunchKernelGGL((bwd_main_kernel<D, BQ, CAUSAL, WITH_DQ, VLDS, OCC>), dim3(nkt * BH), dim3(256), 0, st,
+  hipLaunchKernelGGL((bwd_main_kernel<D, BQ, CAUSAL, WITH_DQ, VLDS, OCC, KV_AGPR>), dim3(nkt * BH), dim3(256), 0, st,
                      (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                      (const uint16_t*)a.dO, a.nlse2, a.delta, a.dq32, (uint16_t*)a.dK,
                      (uint16_t*)a.dV, BH, a.S, a.scale, a.scale * kLog2e);
@@ -707,6 +719,7 @@ static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
       case 1: return launch_main_t<D, 32, CAUSAL, false, true, 2>(a, st);
       case 2: return launch_main_t<D, 32, CAUSAL, false, false, 1>(a, st);
       case 3: return launch_main_t<D, 64, CAUSAL, false, true, 1>(a, st);
+      case 4: return launch_main_t<D, 64, CAUSAL, false, false, 1, false>(a, st);  // K, V left to the allocator
       default: break;
     }
     return launch_main_t<D, 64, CAUSAL, false, false, 1>(a, st);

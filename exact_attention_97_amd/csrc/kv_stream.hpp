@@ -41,23 +41,29 @@ struct FwdCfg {
 // logical element offset inside the tile (row * D + 8 * chunk), fixed per
 // lane.  In a ragged last tile, rows past S are clamped to S-1 (finite data;
 // the scores of those keys are masked).
+// dma_tile_part issues only this wave's n-th 1 KiB piece: a kernel can spread
+// a tile's pieces over its MFMA work (issued back to back they fill the
+// memory pipeline and stall the wavefront).
+template <class Cfg>
+__device__ __forceinline__ void dma_tile_part(const uint16_t* __restrict__ src, int k0, int S, uint16_t* dst,
+                                              int wave, const uint32_t (&loff)[Cfg::DMA_PER_WAVE], int n) {
+  constexpr int NPW = Cfg::DMA_PER_WAVE, BC = Cfg::BC, D = Cfg::D;
+  const uint16_t* tile = src + (size_t)k0 * D;
+  uint32_t off = loff[n];
+  if (k0 + BC > S) {
+    const uint32_t row = off / D;
+    const uint32_t last = (uint32_t)(S - 1 - k0);
+    off = (row > last ? last : row) * D + off % D;
+  }
+  __builtin_amdgcn_global_load_lds(tile + off, (__attribute__((address_space(3))) void*)(dst + 512 * (wave * NPW + n)),
+                                   16, 0, 0);
+}
+
 template <class Cfg>
 __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, int k0, int S, uint16_t* dst,
                                          int wave, const uint32_t (&loff)[Cfg::DMA_PER_WAVE]) {
-  constexpr int NPW = Cfg::DMA_PER_WAVE, BC = Cfg::BC, D = Cfg::D;
-  const uint16_t* tile = src + (size_t)k0 * D;
-  const bool ragged = k0 + BC > S;
 #pragma unroll
-  for (int n = 0; n < NPW; ++n) {
-    uint32_t off = loff[n];
-    if (ragged) {
-      const uint32_t row = off / D;
-      const uint32_t last = (uint32_t)(S - 1 - k0);
-      off = (row > last ? last : row) * D + off % D;
-    }
-    __builtin_amdgcn_global_load_lds(tile + off, (__attribute__((address_space(3))) void*)(dst + 512 * (wave * NPW + n)),
-                                     16, 0, 0);
-  }
+  for (int n = 0; n < Cfg::DMA_PER_WAVE; ++n) dma_tile_part<Cfg>(src, k0, S, dst, wave, loff, n);
 }
 
 // Round eight probabilities to bf16 as four packed 32-bit words for the MFMA
