@@ -145,25 +145,25 @@ struct FwdWave {
     }
   }
 
-  // One tile.  Region 1 (no branches): row max and the rescale decision,
+  // Region 1 of one tile (no branches): row max and the rescale decision,
   // the next tile's scores on the MFMA unit interleaved with this tile's
-  // exponentials on the VALU.  Then the (rare) rescale of the output
-  // accumulator, and region 2: P V with its transpose loads.  The next
-  // tile's scores are computed even after the wave's last tile (from a
-  // stale but finite buffer) so that region 1 has no branch.
+  // exponentials on the VALU.  Returns P (bf16) and the rescale decision for
+  // region 2.  The next tile's scores are computed even after the wave's
+  // last tile (from a stale buffer, never used) so that region 1 has no
+  // branch.
   template <bool MASK>
-  __device__ __forceinline__ static void step(const uint16_t* knext, const uint16_t* vcur, const FwdOffsets<Cfg>& of,
-                                              const bf16x8 (&qreg)[NKS], f32x16 (&scur)[NKB],
-                                              f32x16 (&snext)[NKB], f32x16 (&oacc)[NDB], float& m_run,
-                                              float& l_part, int k0, int lim, int hh, float C, float tau) {
-    bf16x8 pb[2 * NKB];
+  __device__ __forceinline__ static void region1(const uint16_t* knext, const FwdOffsets<Cfg>& of,
+                                                 const bf16x8 (&qreg)[NKS], f32x16 (&scur)[NKB],
+                                                 f32x16 (&snext)[NKB], float& m_run, float& l_part, int k0, int lim,
+                                                 int hh, float C, float tau, bf16x8 (&pb)[2 * NKB], bool& grow,
+                                                 float& alpha) {
     const float mx = tile_max<MASK>(scur, k0, lim, hh);
     const float mxs = (mx == kNegInf) ? kNegInf : mx * C;
     const float m_new = __builtin_fmaxf(m_run, mxs);
     // conditional rescale: the wave moves its running max only when some
     // row's max grew by more than tau (always on the first tile)
-    const bool grow = __any((m_new - m_run) > tau);
-    const float alpha = (grow && m_new != kNegInf) ? exp2_native(m_run - m_new) : 1.0f;
+    grow = __any((m_new - m_run) > tau);
+    alpha = (grow && m_new != kNegInf) ? exp2_native(m_run - m_new) : 1.0f;
     m_run = grow ? m_new : m_run;
     l_part *= alpha;
     // Region 1 runs at raised wave priority: of the two wavefronts sharing a
@@ -192,11 +192,18 @@ struct FwdWave {
 #pragma unroll
     for (int t = 0; t < 2 * NKB; ++t) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pb[t])));
     asm volatile("" ::"v"(l_part));
+    __builtin_amdgcn_s_setprio(0);
+  }
+
+  // Region 2: the (rare) rescale of the output accumulator, then P V with
+  // its transpose loads.
+  __device__ __forceinline__ static void region2(const uint16_t* vcur, const FwdOffsets<Cfg>& of,
+                                                 const bf16x8 (&pb)[2 * NKB], f32x16 (&oacc)[NDB], bool grow,
+                                                 float alpha) {
     if (grow) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
     }
-    __builtin_amdgcn_s_setprio(0);
     pv(vcur, of, pb, oacc);
     // PV: transpose reads run four ahead (two per MFMA operand).
     constexpr int NP = 2 * NKB * NDB;
@@ -207,6 +214,19 @@ struct FwdWave {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+  }
+
+  // One whole tile: region 1 then region 2.
+  template <bool MASK>
+  __device__ __forceinline__ static void step(const uint16_t* knext, const uint16_t* vcur, const FwdOffsets<Cfg>& of,
+                                              const bf16x8 (&qreg)[NKS], f32x16 (&scur)[NKB],
+                                              f32x16 (&snext)[NKB], f32x16 (&oacc)[NDB], float& m_run,
+                                              float& l_part, int k0, int lim, int hh, float C, float tau) {
+    bf16x8 pb[2 * NKB];
+    bool grow;
+    float alpha;
+    region1<MASK>(knext, of, qreg, scur, snext, m_run, l_part, k0, lim, hh, C, tau, pb, grow, alpha);
+    region2(vcur, of, pb, oacc, grow, alpha);
   }
 };
 
