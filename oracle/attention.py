@@ -56,17 +56,22 @@ def _f64(x) -> np.ndarray:
 def scores(q, k, scale: float, causal: bool) -> np.ndarray:
     """Scaled scores of one head: S = scale * Q K^T, with the causal mask.
 
-    q: [Sq, D], k: [Sk, D].  Causal masking uses 0-based indices and hides
-    key j from query i when j > i.
+    q: [Sq, D], k: [Sk, D] with Sk >= Sq when causal.  Causal masking uses
+    0-based indices; the queries are the last Sq of the Sk positions (the
+    plain reading for a query block that continues a longer key sequence),
+    so key j is hidden from query i when j > i + (Sk - Sq).  With Sq == Sk
+    this is j > i.
     """
     q = _f64(q)
     k = _f64(k)
     s = scale * (q @ k.T)
     if causal:
         sq, sk = s.shape
+        if sk < sq:
+            raise ValueError("causal attention needs at least as many keys as queries")
         i = np.arange(sq)[:, None]
         j = np.arange(sk)[None, :]
-        s = np.where(j > i, -np.inf, s)
+        s = np.where(j > i + (sk - sq), -np.inf, s)
     return s
 
 
@@ -87,9 +92,11 @@ def attention_probs(q, k, scale: float, causal: bool) -> np.ndarray:
 
 
 def attention_fwd(q, k, v, scale: float, causal: bool):
-    """Forward pass over [B, H, S, D] inputs.  Returns (O, LSE), float64.
+    """Forward pass over [B, H, Sq, D] queries and [B, H, Sk, D] keys/values.
 
-    O has shape [B, H, S, D]; LSE has shape [B, H, S] (natural log).
+    Returns (O, LSE), float64: O has shape [B, H, Sq, D]; LSE has shape
+    [B, H, Sq] (natural log).  Sq == Sk is the square case of the rest of the
+    path; Sq != Sk serves the split-KV forward (same definition, see scores).
     """
     q = _f64(q)
     k = _f64(k)
@@ -134,10 +141,12 @@ def attention_fwd_rows(q, k, v, scale: float, causal: bool, rows):
     """Forward output for selected rows only, float64.
 
     ``rows`` is an iterable of (b, h, i).  Rows of attention are independent
-    of one another, so each is the full definition applied to one query.
-    Returns (O_rows [n, D], LSE_rows [n]) in the order of ``rows``.
+    of one another, so each is the full definition applied to one query
+    (causal: keys j <= i + Sk - Sq, as in ``scores``).  Returns
+    (O_rows [n, D], LSE_rows [n]) in the order of ``rows``.
     """
     rows = list(rows)
+    off = k.shape[2] - q.shape[2]
     dv = v.shape[-1]
     o = np.zeros((len(rows), dv))
     lse = np.zeros(len(rows))
@@ -151,7 +160,7 @@ def attention_fwd_rows(q, k, v, scale: float, causal: bool, rows):
             qi = _f64(q[b, h, i : i + 1])
             s = scale * (qi @ kk.T)
             if causal:
-                s[:, i + 1 :] = -np.inf
+                s[:, i + off + 1 :] = -np.inf
             p, l = softmax_rows(s)
             o[n] = (p @ vv)[0]
             lse[n] = l[0]
@@ -168,7 +177,7 @@ def _rows_block_f32(q_blk, k, scale, causal, r0):
     import torch
 
     s = (q_blk @ k.T) * scale
-    if causal:
+    if causal:  # r0 is the row's position among the keys (see scores)
         nr, sk = s.shape
         i = torch.arange(r0, r0 + nr).unsqueeze(1)
         j = torch.arange(sk).unsqueeze(0)
@@ -200,7 +209,7 @@ def attention_fwd_f32(q, k, v, scale: float, causal: bool, heads=None, block_row
         vv = v[b, h].to(torch.float32)
         for r0 in range(0, sq, block_rows):
             qb = q[b, h, r0 : r0 + block_rows].to(torch.float32)
-            p, l = _rows_block_f32(qb, kk, scale, causal, r0)
+            p, l = _rows_block_f32(qb, kk, scale, causal, r0 + kk.shape[0] - sq)
             o[n, r0 : r0 + qb.shape[0]] = p @ vv
             lse[n, r0 : r0 + qb.shape[0]] = l
     return o, lse

@@ -375,3 +375,98 @@ def test_forward_pins_catch_planted_mistakes(kind):
 def test_backward_pins_catch_planted_mistakes(kind):
     bwd = _mut_bwd_factory(kind)
     assert bwd_pin_failures(oracle.attention_fwd, bwd), f"planted mistake {kind} went unnoticed"
+
+
+# ----------------------------------------------------------------------------
+# queries shorter than keys (split-KV forward): pinned to the square case
+# ----------------------------------------------------------------------------
+
+
+def _suffix_pin_failures(fwd):
+    """Causal attention of the last Sq query positions over Sk keys equals the
+    last Sq rows of the square problem whose earlier rows are any queries."""
+    fails = []
+    sk, dd = 37, 8
+    qf = _rand((1, 2, sk, dd), 21)
+    k = _rand((1, 2, sk, dd), 22)
+    v = _rand((1, 2, sk, dd), 23)
+    of, lf = fwd(qf, k, v, 0.45, True)
+    for sq in (1, 5, 36):
+        o, l = fwd(qf[:, :, sk - sq :], k, v, 0.45, True)
+        if np.max(np.abs(o - of[:, :, sk - sq :])) > 1e-13 or np.max(np.abs(l - lf[:, :, sk - sq :])) > 1e-13:
+            fails.append(f"suffix Sq={sq}")
+    return fails
+
+
+def test_rectangular_causal_is_suffix_of_square():
+    assert not _suffix_pin_failures(oracle.attention_fwd)
+
+
+def test_single_query_causal_sees_every_key():
+    q = _rand((2, 2, 1, 8), 31)
+    k = _rand((2, 2, 50, 8), 32)
+    v = _rand((2, 2, 50, 8), 33)
+    oc, lc = oracle.attention_fwd(q, k, v, 0.3, True)
+    on, ln = oracle.attention_fwd(q, k, v, 0.3, False)
+    assert np.max(np.abs(oc - on)) == 0.0 and np.max(np.abs(lc - ln)) == 0.0
+
+
+def test_key_chunk_merge_identity():
+    """Attention over all keys equals the log-sum-exp weighted merge of the
+    attentions over disjoint key chunks (the decomposition split-KV uses):
+    LSE = ln sum_c exp(LSE_c),  O = sum_c exp(LSE_c - LSE) O_c."""
+    q = _rand((1, 2, 9, 8), 41)
+    k = _rand((1, 2, 70, 8), 42)
+    v = _rand((1, 2, 70, 8), 43)
+    o, l = oracle.attention_fwd(q, k, v, 0.5, False)
+    bounds = [0, 13, 40, 41, 70]
+    parts = [oracle.attention_fwd(q, k[:, :, a:b], v[:, :, a:b], 0.5, False) for a, b in zip(bounds, bounds[1:])]
+    lse = np.log(sum(np.exp(lc) for _, lc in parts))
+    om = sum(np.exp(lc - lse)[..., None] * oc for oc, lc in parts)
+    assert np.max(np.abs(lse - l)) < 1e-13
+    assert np.max(np.abs(om - o)) < 1e-13
+
+
+def test_rectangular_rows_and_float32_paths_agree():
+    torch = pytest.importorskip("torch")
+    g = torch.Generator().manual_seed(12)
+    q = torch.randn((1, 2, 70, 16), generator=g).to(torch.bfloat16)
+    k = torch.randn((1, 2, 300, 16), generator=g).to(torch.bfloat16)
+    v = torch.randn((1, 2, 300, 16), generator=g).to(torch.bfloat16)
+    o64, l64 = oracle.attention_fwd(q, k, v, 0.25, True)
+    o32, l32 = oracle.attention_fwd_f32(q, k, v, 0.25, True, block_rows=32)
+    assert np.max(np.abs(o32.numpy() - o64[0])) < 1e-5
+    assert np.max(np.abs(l32.numpy() - l64[0])) < 1e-5
+    rows = [(0, 0, 0), (0, 1, 33), (0, 0, 69)]
+    ro, rl = oracle.attention_fwd_rows(q, k, v, 0.25, True, rows)
+    for n, (b, h, i) in enumerate(rows):
+        assert np.max(np.abs(ro[n] - o64[b, h, i])) < 1e-13
+        assert abs(rl[n] - l64[b, h, i]) < 1e-13
+
+
+def test_causal_needs_enough_keys():
+    with pytest.raises(ValueError):
+        oracle.attention_fwd(_rand((1, 1, 5, 4), 1), _rand((1, 1, 3, 4), 2), _rand((1, 1, 3, 4), 3), 1.0, True)
+
+
+def test_suffix_pin_catches_top_left_alignment():
+    """A planted mistake -- aligning short query blocks at the first key
+    position -- fails the suffix pin."""
+
+    def fwd_top_left(q, k, v, scale, causal):
+        q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+        bsz, nh, sq, _ = q.shape
+        o = np.zeros((bsz, nh, sq, v.shape[-1]))
+        l = np.zeros((bsz, nh, sq))
+        for b in range(bsz):
+            for h in range(nh):
+                s = scale * (q[b, h] @ k[b, h].T)
+                if causal:
+                    i = np.arange(sq)[:, None]
+                    j = np.arange(k.shape[2])[None, :]
+                    s = np.where(j > i, -np.inf, s)
+                p, l[b, h] = A.softmax_rows(s)
+                o[b, h] = p @ v[b, h]
+        return o, l
+
+    assert _suffix_pin_failures(fwd_top_left)
