@@ -136,6 +136,59 @@ def gemm_reference(torch, dev, M=16384, N=16384, K=8192, reps=10):
             "library": "torch.matmul (hipBLASLt)", "frac_of_peak": round(2.0 * M * N * K / (ms * 1e-3) / 1e12 / PEAK_TFLOPS, 4)}
 
 
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def splitkv_measure(torch, attn, dev, reps=20):
+    """Split-KV forward on its two workloads (outside the headline step).
+
+    decode32k reads all of K and V for one query per sequence, so its bound
+    is HBM bandwidth (minimal bytes: Q, K, V, O, LSE once); prefill32k (512
+    queries continuing a 32k context, causal) is an MFMA-bound contraction.
+    Algorithmic flops: 4 * D per visible (query, key) pair; with the queries
+    the last Sq of the Sk positions a causal row i sees i + Sk - Sq + 1 keys.
+    """
+    from exact_attention_97_amd.inputs import SPLITKV_WORKLOADS, make_qkv_rect
+
+    out = {}
+    for name, w in sorted(SPLITKV_WORKLOADS.items()):
+        q, k, v = (t.to(dev) for t in make_qkv_rect(w.B, w.H, w.Sq, w.Sk, w.D, w.seed, std=w.std))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, attn.fwd_splitkv_workspace_bytes(w.B, w.H, w.Sq, w.Sk, w.D, w.causal)),
+                         dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            attn.attn_fwd_splitkv(q, k, v, scale=w.scale, causal=w.causal, workspace=ws, out=o, lse=lse)
+        torch.cuda.synchronize()
+        attn.prof_reset()
+        attn.prof_enable(True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            attn.attn_fwd_splitkv(q, k, v, scale=w.scale, causal=w.causal, workspace=ws, out=o, lse=lse)
+        e1.record()
+        torch.cuda.synchronize()
+        attn.prof_enable(False)
+        ms = e0.elapsed_time(e1) / reps
+        n1, ms1 = attn.prof_collect("fwd_splitkv")
+        n2, ms2 = attn.prof_collect("splitkv_merge")
+        pairs = (w.Sq * (w.Sk - w.Sq) + w.Sq * (w.Sq + 1) // 2) if w.causal else w.Sq * w.Sk
+        flops = 4.0 * w.B * w.H * pairs * w.D
+        nbytes = 2.0 * w.B * w.H * (2 * w.Sq + 2 * w.Sk) * w.D + 4.0 * w.B * w.H * w.Sq
+        r = {"B": w.B, "H": w.H, "Sq": w.Sq, "Sk": w.Sk, "D": w.D, "causal": w.causal, "ms": round(ms, 4),
+             "tflops": round(flops / (ms * 1e-3) / 1e12, 1), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+             "kernel_avg_ms": {"fwd_splitkv": round(ms1 / max(n1, 1), 4), "splitkv_merge": round(ms2 / max(n2, 1), 4)}}
+        if w.Sq == 1:
+            r["roofline"] = {"bound": "hbm", "achieved": r["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(r["gbs"] / HBM_PEAK_GBS, 4), "bytes_per_call": nbytes}
+        else:
+            r["roofline"] = {"bound": "mfma", "achieved": r["tflops"], "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(r["tflops"] / PEAK_TFLOPS, 4), "flops_per_call": flops}
+        out[name] = r
+        del q, k, v, o, lse, ws
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -269,6 +322,7 @@ def main():
         "kernels_noncausal_avg_ms": {k2: round(v2["avg_ms"], 4) for k2, v2 in kern.items()},
         "roofline": roofline,
         "gemm_reference": gemm_reference(torch, dev),
+        "splitkv": splitkv_measure(torch, attn, dev),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(q, k, v, do)

@@ -3,14 +3,17 @@
 The compute lives in hand-written HIP kernels behind the C ABI of
 ``include/attn97.h`` (libattn97.so).  This package only loads that library
 and marshals arguments: ``attn_fwd`` returns (O, LSE), ``attn_bwd`` returns
-(dQ, dK, dV).
+(dQ, dK, dV), ``attn_fwd_splitkv`` returns (O, LSE) for queries and keys of
+different lengths by splitting the keys.
 """
 
 from ._lib import (  # noqa: F401
     AttnError,
     attn_bwd,
     attn_fwd,
+    attn_fwd_splitkv,
     bwd_workspace_bytes,
+    fwd_splitkv_workspace_bytes,
     exp2_eval,
     load,
     prof_collect,

@@ -27,6 +27,7 @@ BWD_MODES = {"atomic": 0, "split": 1}
 EXPORTS = (
     "attn_default_opts", "attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd", "attn_strerror",
     "attn_exp2_eval", "attn_prof_enable", "attn_prof_reset", "attn_prof_collect", "attn_version",
+    "attn_fwd_splitkv_workspace_bytes", "attn_fwd_splitkv",
 )
 
 
@@ -75,6 +76,10 @@ def load():
     lib.attn_prof_collect.restype = i
     lib.attn_version.argtypes = []
     lib.attn_version.restype = ctypes.c_char_p
+    lib.attn_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.attn_fwd_splitkv_workspace_bytes.restype = sz
+    lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i, optp, vp]
+    lib.attn_fwd_splitkv.restype = i
     _lib = lib
     return lib
 
@@ -128,6 +133,40 @@ def attn_fwd(q, k, v, scale=None, causal=False, exp_mode="native", rescale_tau=8
     _check("attn_fwd", lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                     lse.data_ptr(), B, H, S, D, float(scale), int(bool(causal)),
                                     ctypes.byref(opts), _stream_ptr(stream)))
+    return out, lse
+
+
+def fwd_splitkv_workspace_bytes(B, H, Sq, Sk, D, causal=False, num_splits=0):
+    return int(load().attn_fwd_splitkv_workspace_bytes(B, H, Sq, Sk, D, int(bool(causal)), int(num_splits)))
+
+
+def attn_fwd_splitkv(q, k, v, scale=None, causal=False, num_splits=0, exp_mode="native", rescale_tau=8.0,
+                     workspace=None, out=None, lse=None, stream=None):
+    """Split-KV forward: q [B,H,Sq,D], k/v [B,H,Sk,D]; returns (O bf16 [B,H,Sq,D], LSE fp32 [B,H,Sq])."""
+    import torch
+
+    lib = load()
+    for t in (q, k, v):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("attention tensors must be contiguous 4-d bfloat16 CUDA/HIP tensors")
+    B, H, Sq, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != H or k.shape[3] != D:
+        raise ValueError(f"k and v must be [B,H,Sk,D] matching q {tuple(q.shape)}, got {tuple(k.shape)}")
+    Sk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    need = fwd_splitkv_workspace_bytes(B, H, Sq, Sk, D, causal, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    opts = make_opts(exp_mode, rescale_tau)
+    _check("attn_fwd_splitkv", lib.attn_fwd_splitkv(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), B, H, Sq, Sk, D, float(scale), int(bool(causal)),
+        int(num_splits), ctypes.byref(opts), _stream_ptr(stream)))
     return out, lse
 
 

@@ -138,6 +138,94 @@ attn_status attn_fwd(const void* Q, const void* K, const void* V, void* O, float
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+}  // extern "C"
+
+namespace {
+
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Validated shape of a split-KV call and its split plan (shared by the
+// workspace query and the call, so both always agree).
+struct SplitPlan {
+  int nsplit = 0, kchunk = 0;
+  size_t opart_bytes = 0, lpart_bytes = 0;
+};
+
+attn_status plan_splitkv(int B, int H, int Sq, int Sk, int D, int causal, int num_splits, SplitPlan* p) {
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return ATTN_ERR_SHAPE;
+  if (D != 64 && D != 128 && D != 256) return ATTN_ERR_UNSUPPORTED;
+  if ((double)B * H * Sq * D > 2147483647.0 || (double)B * H * Sk * D > 2147483647.0) return ATTN_ERR_SHAPE;
+  if (causal && Sk < Sq) return ATTN_ERR_SHAPE;  // the queries are the last Sq of the Sk positions
+  if (num_splits < 0) return ATTN_ERR_VALUE;
+  const int bc = attn97::fwd_tile_keys(D), br = attn97::fwd_tile_queries(D);
+  const long ntiles = (Sk + bc - 1) / bc;
+  long ns = num_splits;
+  if (ns == 0) {  // enough workgroups for two per compute unit
+    const long wgs = (long)((Sq + br - 1) / br) * B * H;
+    ns = (512 + wgs - 1) / wgs;
+  }
+  ns = ns < 1 ? 1 : (ns > ntiles ? ntiles : ns);
+  const long tiles_per = (ntiles + ns - 1) / ns;
+  p->kchunk = (int)(tiles_per * bc);
+  p->nsplit = (int)((Sk + p->kchunk - 1) / p->kchunk);
+  const double parts = (double)p->nsplit * B * H * Sq;
+  if (parts * D > 9.0e15) return ATTN_ERR_SHAPE;
+  p->opart_bytes = round256((size_t)p->nsplit * B * H * Sq * D * sizeof(float));
+  p->lpart_bytes = round256((size_t)p->nsplit * B * H * Sq * sizeof(float));
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_fwd_splitkv_workspace_bytes(int B, int H, int Sq, int Sk, int D, int causal, int num_splits) {
+  SplitPlan p;
+  if (plan_splitkv(B, H, Sq, Sk, D, causal, num_splits, &p) != ATTN_OK) return 0;
+  return p.opart_bytes + p.lpart_bytes;
+}
+
+attn_status attn_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE, void* workspace,
+                             size_t workspace_bytes, int B, int H, int Sq, int Sk, int D, float scale, int causal,
+                             int num_splits, const attn_opts* opts, void* stream) {
+  if (!Q || !K || !V || !O || !LSE) return ATTN_ERR_NULL;
+  SplitPlan p;
+  attn_status st = plan_splitkv(B, H, Sq, Sk, D, causal ? 1 : 0, num_splits, &p);
+  if (st != ATTN_OK) return st;
+  if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(V, 16) || misaligned(O, 16) || misaligned(LSE, 16))
+    return ATTN_ERR_ALIGN;
+  if (!isfinite(scale)) return ATTN_ERR_VALUE;
+  attn_opts o;
+  st = read_opts(opts, &o);
+  if (st != ATTN_OK) return st;
+  if (workspace == nullptr || workspace_bytes < p.opart_bytes + p.lpart_bytes || misaligned(workspace, 256))
+    return ATTN_ERR_WORKSPACE;
+
+  attn97::FwdArgs a;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.LSE = LSE;
+  a.B = B;
+  a.H = H;
+  a.S = Sq;
+  a.D = D;
+  a.causal = causal ? 1 : 0;
+  a.exp_mode = o.exp_mode;
+  a.C = fabsf(scale) * kLog2eHost;
+  a.qsign = (scale < 0.0f) ? 0x80008000u : 0u;
+  a.tau = o.rescale_tau;
+  attn97::SplitKvLaunch l;
+  l.Sk = Sk;
+  l.nsplit = p.nsplit;
+  l.kchunk = p.kchunk;
+  l.Opart = static_cast<float*>(workspace);
+  l.Lpart = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.opart_bytes);
+  hipError_t e = attn97::launch_fwd_splitkv(a, l, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 size_t attn_bwd_workspace_bytes(int B, int H, int S, int D, int causal, const attn_opts* opts) {
   (void)causal;
   if (check_shape(B, H, S, D) != ATTN_OK) return 0;
@@ -217,7 +305,8 @@ attn_status attn_prof_reset(void) {
 
 attn_status attn_prof_collect(const char* kernel, int* count, double* total_ms) {
   if (!kernel || !count || !total_ms) return ATTN_ERR_NULL;
-  static const char* names[attn97::KID_COUNT] = {"fwd", "bwd_pre", "bwd_main", "dq_convert", "bwd_dkdv", "bwd_dq"};
+  static const char* names[attn97::KID_COUNT] = {"fwd",      "bwd_pre", "bwd_main",     "dq_convert",
+                                                "bwd_dkdv", "bwd_dq",  "fwd_splitkv", "splitkv_merge"};
   int kid = -1;
   for (int i = 0; i < attn97::KID_COUNT; ++i)
     if (strcmp(kernel, names[i]) == 0) kid = i;

@@ -230,15 +230,28 @@ struct FwdWave {
   }
 };
 
+// Split-KV (SPLITKV): the keys are split into chunks of kchunk (a multiple
+// of the tile) and workgroup (query tile, head, split) attends to one chunk,
+// writing the chunk's normalised output (fp32) and log-sum-exp to
+// workspace arrays that a merge kernel combines.  Queries and keys may then
+// differ in length: S queries, Sk keys, and a causal query i sees keys up to
+// i + Sk - S (the queries are the last S positions).
+struct SplitKv {
+  int Sk;        // number of keys (== S without SPLITKV)
+  int kchunk;    // keys per split
+  float* Opart;  // [nsplit, B*H, S, D] fp32
+  float* Lpart;  // [nsplit, B*H, S] fp32, natural log; -inf for a row with no visible key
+};
+
 // `causal` is a run-time argument: it only moves a few scalar bounds (tile
 // order, tile counts, the last visible key), and one instantiation for both
 // settings keeps the compiler from restructuring the non-causal loop into a
 // version that spills registers.
-template <class Cfg, int EXPMODE>
+template <class Cfg, int EXPMODE, bool SPLITKV = false>
 __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 : 2) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int S, float C, uint32_t qsign, float tau, int nqt,
-    int causal) {
+    int causal, SplitKv sk) {
   using W = FwdWave<Cfg, EXPMODE>;
   constexpr int D = Cfg::D, BC = Cfg::BC, BR = Cfg::BR, NKB = Cfg::NKB, NKS = Cfg::NKS, NDB = Cfg::NDB;
   constexpr int NBUF = Cfg::NBUF, DPW = Cfg::DMA_PER_WAVE;
@@ -251,12 +264,18 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
   // B*H a multiple of 8 every workgroup of one head lands on the same XCD.
   const int id = blockIdx.x;
   const int bh = id % BH;
-  const int rank = id / BH;
+  const int rank = SPLITKV ? (id / BH) % nqt : id / BH;
+  const int split = SPLITKV ? id / BH / nqt : 0;
   const int qt = causal ? (nqt - 1 - rank) : rank;
   const int q0 = qt * BR;
+  const int Sk = SPLITKV ? sk.Sk : S;
+  const int coff = Sk - S;                        // causal offset (0 when square)
+  const int kb = SPLITKV ? split * sk.kchunk : 0;  // first key of this split
+  const int ke = SPLITKV ? min(Sk, kb + sk.kchunk) : Sk;
   const size_t base = (size_t)bh * (size_t)S * D;
-  const uint16_t* Kh = K + base;
-  const uint16_t* Vh = V + base;
+  const size_t kbase = (size_t)bh * (size_t)Sk * D;
+  const uint16_t* Kh = K + kbase;
+  const uint16_t* Vh = V + kbase;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -278,15 +297,34 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
     }
   }
 
-  const int kend = causal ? min(S, q0 + BR) : S;
-  const int nkt = (kend + BC - 1) / BC;                                  // tiles of the workgroup
-  const int nkt_w = causal ? min(nkt, (qw0 + 32 + BC - 1) / BC) : nkt;  // tiles this wave needs
+  // keys [kb, kend) are visible to some row of the workgroup; tile t covers
+  // keys kb + t*BC ..
+  const int kend = causal ? min(ke, q0 + BR + coff) : ke;
+  const int nkt = kend > kb ? (kend - kb + BC - 1) / BC : 0;  // tiles of the workgroup
+  const int wend = causal ? min(kend, qw0 + 32 + coff) : kend;
+  // tiles this wave needs (none when all its rows are past the last query:
+  // it still issues its share of the loads and takes part in the barriers)
+  const int nkt_w = (wend > kb && qw0 < S) ? (wend - kb + BC - 1) / BC : 0;
   // Tiles [0, nfull) need no mask for this wave; the rest (diagonal or ragged) do.
-  int nfull = causal ? (qw0 + 1) / BC : nkt_w;
-  nfull = min(nfull, S / BC);
+  int nfull = causal ? (qw0 + coff + 1 - kb) / BC : nkt_w;
+  nfull = max(0, min(nfull, (ke - kb) / BC));
 
-  // last key this lane's row may see (causal diagonal and/or end of sequence)
-  const int lim = causal ? min(qrow, S - 1) : (S - 1);
+  // last key this lane's row may see (causal diagonal, end of split / sequence)
+  const int lim = causal ? min(qrow + coff, ke - 1) : (ke - 1);
+
+  if constexpr (SPLITKV) {
+    if (nkt == 0) {  // no key of this split is visible to the workgroup (uniform)
+      if (qrow < S) {
+        float* orow = sk.Opart + (((size_t)split * BH + bh) * S + qrow) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * g + 4 * hh) = f32x4{};
+        if (hh == 0) sk.Lpart[((size_t)split * BH + bh) * S + qrow] = kNegInf;
+      }
+      return;
+    }
+  }
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -304,11 +342,11 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
   auto issue = [&](int j) {  // loads of "iteration" j; returns the number of ops issued
     int n = 0;
     if (j + NBUF < nkt) {
-      dma_tile<Cfg>(Kh, (j + NBUF) * BC, S, Kb[(j + NBUF) % NBUF], wave, of.dma);
+      dma_tile<Cfg>(Kh, kb + (j + NBUF) * BC, Sk, Kb[(j + NBUF) % NBUF], wave, of.dma);
       n += DPW;
     }
     if (j + NBUF - 1 >= 0 && j + NBUF - 1 < nkt) {
-      dma_tile<Cfg>(Vh, (j + NBUF - 1) * BC, S, Vb[(j + NBUF - 1) % NBUF], wave, of.dma);
+      dma_tile<Cfg>(Vh, kb + (j + NBUF - 1) * BC, Sk, Vb[(j + NBUF - 1) % NBUF], wave, of.dma);
       n += DPW;
     }
     return n;
@@ -344,10 +382,10 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
     if (kt < nkt_w) {
       if (kt < nfull)
         W::template step<false>(Kb[(kt + 1) % NBUF], Vb[kt % NBUF], of, qreg, scur, snext, oacc, m_run, l_part,
-                                kt * BC, lim, hh, C, tau);
+                                kb + kt * BC, lim, hh, C, tau);
       else
         W::template step<true>(Kb[(kt + 1) % NBUF], Vb[kt % NBUF], of, qreg, scur, snext, oacc, m_run, l_part,
-                               kt * BC, lim, hh, C, tau);
+                               kb + kt * BC, lim, hh, C, tau);
     }
     wait_loads(n_last);
     barrier_keep_loads();
@@ -359,6 +397,22 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
 
 // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l) ----------------------
   const float l_tot = l_part + wave_swap_halves(l_part);
+  if constexpr (SPLITKV) {  // a row may see no key of this split: O = 0, LSE = -inf
+    const bool any = l_tot > 0.0f;
+    const float inv = any ? 1.0f / l_tot : 0.0f;
+    if (qrow < S) {
+      float* orow = sk.Opart + (((size_t)split * BH + bh) * S + qrow) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * g + 4 * hh) =
+              f32x4{oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv,
+                    oacc[db][4 * g + 3] * inv};
+      if (hh == 0) sk.Lpart[((size_t)split * BH + bh) * S + qrow] = any ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+    }
+    return;
+  }
   const float inv = 1.0f / l_tot;
   if (qrow < S) {
     uint16_t* orow = O + base + (size_t)qrow * D;
@@ -374,6 +428,37 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
     }
     if (hh == 0) LSE[(size_t)bh * S + qrow] = (m_run + __log2f(l_tot)) * kLn2;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Split-KV merge: per row, LSE = ln sum_c exp(LSE_c) and
+// O = sum_c exp(LSE_c - LSE) O_c, rounded to bf16 (the decomposition of the
+// softmax over disjoint key sets that also makes LSE an output of the
+// forward pass).  D/4 threads per row, four columns each; HBM-bound.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void splitkv_merge_kernel(const float* __restrict__ Opart,
+                                                            const float* __restrict__ Lpart, uint16_t* __restrict__ O,
+                                                            float* __restrict__ LSE, long rows, int nsplit) {
+  constexpr int TPR = D / 4;
+  const long row = ((long)blockIdx.x * 256 + threadIdx.x) / TPR;
+  const int c = threadIdx.x % TPR;
+  if (row >= rows) return;
+  float m = kNegInf;
+  for (int sp = 0; sp < nsplit; ++sp) m = __builtin_fmaxf(m, Lpart[(size_t)sp * rows + row]);
+  f32x4 acc = f32x4{};
+  float wsum = 0.0f;
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float l = Lpart[(size_t)sp * rows + row];
+    const float w = (l == kNegInf) ? 0.0f : exp2_native((l - m) * kLog2e);  // the largest term has w = 1
+    const f32x4 o = *reinterpret_cast<const f32x4*>(Opart + ((size_t)sp * rows + row) * D + 4 * c);
+    acc += w * o;
+    wsum += w;
+  }
+  const float inv = 1.0f / wsum;
+  *reinterpret_cast<u32x2*>(O + (size_t)row * D + 4 * c) =
+      pack_bf16x4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  if (c == 0) LSE[row] = m + __log2f(wsum) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -395,7 +480,8 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   dim3 grid(nqt * BH), block(64 * Cfg::NW);
   prof_begin(KID_FWD, st);
   hipLaunchKernelGGL((fwd_kernel<Cfg, EXPMODE>), grid, block, 0, st, (const uint16_t*)a.Q, (const uint16_t*)a.K,
-                     (const uint16_t*)a.V, (uint16_t*)a.O, a.LSE, BH, a.S, a.C, a.qsign, a.tau, nqt, a.causal);
+                     (const uint16_t*)a.V, (uint16_t*)a.O, a.LSE, BH, a.S, a.C, a.qsign, a.tau, nqt, a.causal,
+                     SplitKv{a.S, 0, nullptr, nullptr});
   prof_end(KID_FWD, st);
   return hipGetLastError();
 }
@@ -432,6 +518,62 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
         default: return launch_fwd_e<FwdDefault<128>::type>(a, st);
       }
     case 256: return launch_fwd_e<FwdDefault<256>::type>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int fwd_tile_keys(int D) {
+  switch (D) {
+    case 64: return FwdDefault<64>::type::BC;
+    case 128: return FwdDefault<128>::type::BC;
+    case 256: return FwdDefault<256>::type::BC;
+    default: return 0;
+  }
+}
+
+int fwd_tile_queries(int D) {
+  switch (D) {
+    case 64: return FwdDefault<64>::type::BR;
+    case 128: return FwdDefault<128>::type::BR;
+    case 256: return FwdDefault<256>::type::BR;
+    default: return 0;
+  }
+}
+
+template <class Cfg, int EXPMODE>
+static hipError_t launch_splitkv_t(const FwdArgs& a, const SplitKvLaunch& p, hipStream_t st) {
+  const int nqt = (a.S + Cfg::BR - 1) / Cfg::BR;
+  const int BH = a.B * a.H;
+  prof_begin(KID_FWD_SPLITKV, st);
+  hipLaunchKernelGGL((fwd_kernel<Cfg, EXPMODE, true>), dim3(nqt * BH * p.nsplit), dim3(64 * Cfg::NW), 0, st,
+                     (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V, (uint16_t*)a.O, a.LSE, BH,
+                     a.S, a.C, a.qsign, a.tau, nqt, a.causal, SplitKv{p.Sk, p.kchunk, p.Opart, p.Lpart});
+  prof_end(KID_FWD_SPLITKV, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long rows = (long)BH * a.S;
+  const long threads = rows * (Cfg::D / 4);
+  prof_begin(KID_SPLITKV_MERGE, st);
+  hipLaunchKernelGGL((splitkv_merge_kernel<Cfg::D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+                     (const float*)p.Opart, (const float*)p.Lpart, (uint16_t*)a.O, a.LSE, rows, p.nsplit);
+  prof_end(KID_SPLITKV_MERGE, st);
+  return hipGetLastError();
+}
+
+template <class Cfg>
+static hipError_t launch_splitkv_e(const FwdArgs& a, const SplitKvLaunch& p, hipStream_t st) {
+  switch (a.exp_mode) {
+    case 1: return launch_splitkv_t<Cfg, 1>(a, p, st);
+    case 2: return launch_splitkv_t<Cfg, 2>(a, p, st);
+    default: return launch_splitkv_t<Cfg, 0>(a, p, st);
+  }
+}
+
+hipError_t launch_fwd_splitkv(const FwdArgs& a, const SplitKvLaunch& p, hipStream_t st) {
+  switch (a.D) {
+    case 64: return launch_splitkv_e<FwdDefault<64>::type>(a, p, st);
+    case 128: return launch_splitkv_e<FwdDefault<128>::type>(a, p, st);
+    case 256: return launch_splitkv_e<FwdDefault<256>::type>(a, p, st);
     default: return hipErrorInvalidValue;
   }
 }

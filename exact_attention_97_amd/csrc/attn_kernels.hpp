@@ -49,14 +49,36 @@ inline size_t bwd_dq32_bytes(int B, int H, int S, int D) {
   return (size_t)B * H * S * D * sizeof(float);
 }
 
+// Split-KV forward: per-split partial results in the workspace, then a merge.
+struct SplitKvLaunch {
+  int Sk;        // keys (the queries are FwdArgs::S)
+  int nsplit;    // number of key chunks
+  int kchunk;    // keys per chunk, a multiple of fwd_tile_keys(D)
+  float* Opart;  // [nsplit, B*H, S, D] fp32
+  float* Lpart;  // [nsplit, B*H, S] fp32
+};
+
 // Kernel names used by the timing hooks.
-enum KernelId { KID_FWD = 0, KID_BWD_PRE, KID_BWD_MAIN, KID_DQ_CONVERT, KID_BWD_DKDV, KID_BWD_DQ, KID_COUNT };
+enum KernelId {
+  KID_FWD = 0,
+  KID_BWD_PRE,
+  KID_BWD_MAIN,
+  KID_DQ_CONVERT,
+  KID_BWD_DKDV,
+  KID_BWD_DQ,
+  KID_FWD_SPLITKV,
+  KID_SPLITKV_MERGE,
+  KID_COUNT
+};
 
 // Called by the launchers around each kernel launch (no-ops unless timing is on).
 void prof_begin(int kid, hipStream_t st);
 void prof_end(int kid, hipStream_t st);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
+hipError_t launch_fwd_splitkv(const FwdArgs& a, const SplitKvLaunch& p, hipStream_t st);
+int fwd_tile_keys(int D);     // keys per tile of the forward kernel for head dim D
+int fwd_tile_queries(int D);  // queries per workgroup of the forward kernel
 hipError_t launch_exp2_eval(const float* x, float* y, long n, int mode, hipStream_t st);
 hipError_t launch_bwd_atomic(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_split(const BwdArgs& a, hipStream_t st);

@@ -80,3 +80,45 @@ def make_qkvdo(B, H, S, D, seed, std=1.0, outlier_frac=0.0, outlier_scale=20.0):
 def make_workload(w: Workload):
     """Inputs of a named workload (CPU bf16 tensors)."""
     return make_qkvdo(w.B, w.H, w.S, w.D, w.seed, w.std, w.outlier_frac, w.outlier_scale)
+
+
+def make_qkv_rect(B, H, Sq, Sk, D, seed, std=1.0):
+    """Draw Q [B, H, Sq, D] and K, V [B, H, Sk, D] (in that order) as CPU bfloat16
+    tensors, for queries and keys of different lengths (split-KV forward)."""
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((B, H, Sq, D), generator=g, dtype=torch.float32)
+    k = torch.randn((B, H, Sk, D), generator=g, dtype=torch.float32)
+    v = torch.randn((B, H, Sk, D), generator=g, dtype=torch.float32)
+    if std != 1.0:
+        q.mul_(std)
+        k.mul_(std)
+        v.mul_(std)
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
+@dataclass(frozen=True)
+class RectWorkload:
+    """A forward workload with Sq queries over Sk keys (split-KV forward)."""
+
+    name: str
+    B: int
+    H: int
+    Sq: int
+    Sk: int
+    D: int
+    causal: bool
+    seed: int
+    std: float = 1.0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+
+# Long key sequences with few queries: one decoding step per sequence, and a
+# 512-query chunk of prefill continuing a 32k context (causal, the queries
+# being the last 512 positions).
+SPLITKV_WORKLOADS = {
+    "decode32k": RectWorkload("decode32k", B=4, H=32, Sq=1, Sk=32768, D=128, causal=True, seed=8, std=0.5),
+    "prefill32k": RectWorkload("prefill32k", B=1, H=32, Sq=512, Sk=32768, D=128, causal=True, seed=9, std=0.5),
+}

@@ -125,6 +125,38 @@ attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O,
                      int B, int H, int S, int D, float scale, int causal,
                      const attn_opts* opts, void* stream);
 
+/*
+ * Split-KV forward pass: the same O and LSE as attn_fwd, computed by splitting
+ * the keys into chunks that run as separate workgroups and merging the
+ * per-chunk results by their log-sum-exp,
+ *     LSE = ln sum_c exp(LSE_c),   O = sum_c exp(LSE_c - LSE) O_c,
+ * which is exact for softmax over disjoint key sets.  It gives a long key
+ * sequence with few query rows (decoding, chunked prefill) enough
+ * workgroups to fill the GPU.  The pages motivate the LSE output by long
+ * sequences (page "FlashAttention-4: Algorithm and Kernel Pipelining
+ * Co-Design for Asymmetric Hardware Scaling", abstract; page
+ * "FlashAttention-3 и FlashAttention-4", section "Режим 2-CTA MMA"); the
+ * split itself is not on the pages.
+ *   in : Q bf16 [B,H,Sq,D]; K, V bf16 [B,H,Sk,D]
+ *   out: O bf16 [B,H,Sq,D]; LSE fp32 [B,H,Sq]
+ *   Sq and Sk may differ.  causal != 0 reads the queries as the last Sq of
+ *   the Sk positions: key j is hidden from query i when j > i + Sk - Sq
+ *   (requires Sk >= Sq, else ATTN_ERR_SHAPE; Sq == Sk is attn_fwd's mask).
+ *   num_splits: number of key chunks, >= 1, clamped to the number of key
+ *   tiles; 0 chooses one that gives about two workgroups per compute unit.
+ *   workspace: caller-owned device memory of at least
+ *   attn_fwd_splitkv_workspace_bytes(...) bytes (same arguments), 256-byte
+ *   aligned, holding the per-chunk fp32 outputs and LSEs; contents on entry
+ *   do not matter.  Two calls in flight at once must not share it.
+ *   Errors: as attn_fwd, plus ATTN_ERR_VALUE for num_splits < 0 and
+ *   ATTN_ERR_WORKSPACE for a missing, small or misaligned workspace.
+ */
+size_t attn_fwd_splitkv_workspace_bytes(int B, int H, int Sq, int Sk, int D, int causal, int num_splits);
+attn_status attn_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                             void* workspace, size_t workspace_bytes,
+                             int B, int H, int Sq, int Sk, int D, float scale, int causal,
+                             int num_splits, const attn_opts* opts, void* stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* attn_strerror(attn_status s);
 
@@ -142,7 +174,8 @@ attn_status attn_exp2_eval(const float* x, float* y, long n, int mode, void* str
  * every kernel launch is bracketed by two hipEvents recorded on the launch
  * stream.  attn_prof_collect synchronises on those events and returns, for
  * the kernel named `kernel` ("fwd", "bwd_pre", "bwd_main", "bwd_dq", "bwd_dkdv",
- * "dq_convert"), the number of launches and the summed milliseconds since the
+ * "dq_convert", "fwd_splitkv", "splitkv_merge"), the number of launches and the
+ * summed milliseconds since the
  * last reset.  Events are created on first use and kept; at most 65536
  * launches are recorded between resets (later ones are not timed).
  * Not thread-safe; meant for single-threaded benchmark drivers.

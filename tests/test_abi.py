@@ -159,3 +159,31 @@ def test_product_path_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "import oracle" not in text and "from oracle" not in text, f
+
+
+def test_splitkv_workspace_and_rejects():
+    lib = L.load()
+    # Sq=10, Sk=1000, D=128: 64-key tiles -> 16 tiles; 3 splits -> 6 tiles (384 keys) per split -> 3 splits
+    B, H, Sq, Sk, D = 2, 3, 10, 1000, 128
+    per = B * H * Sq
+    want = ((3 * per * D * 4 + 255) // 256 * 256) + ((3 * per * 4 + 255) // 256 * 256)
+    assert lib.attn_fwd_splitkv_workspace_bytes(B, H, Sq, Sk, D, 0, 3) == want
+    # more splits than key tiles are clamped to one split per tile (16)
+    want16 = ((16 * per * D * 4 + 255) // 256 * 256) + ((16 * per * 4 + 255) // 256 * 256)
+    assert lib.attn_fwd_splitkv_workspace_bytes(B, H, Sq, Sk, D, 0, 1000) == want16
+    assert lib.attn_fwd_splitkv_workspace_bytes(B, H, Sq, Sk, D, 0, 0) > 0
+    assert lib.attn_fwd_splitkv_workspace_bytes(B, H, 20, 10, D, 1, 0) == 0  # causal, Sk < Sq
+    assert lib.attn_fwd_splitkv_workspace_bytes(B, H, Sq, Sk, 80, 0, 0) == 0
+    assert lib.attn_fwd_splitkv_workspace_bytes(B, H, Sq, Sk, D, 0, -1) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Sq=0), SHAPE), (dict(D=48), UNSUP), (dict(O=P + 8), ALIGN), (dict(scale=float("nan")), VALUE),
+    (dict(splits=-2), VALUE), (dict(causal=1, Sq=50, Sk=40), SHAPE), (dict(ws=None), WS), (dict(wsb=16), WS),
+])
+def test_splitkv_rejects(kw, code):
+    lib = L.load()
+    a = dict(Q=P, K=P, V=P, O=P, LSE=P, ws=P, wsb=1 << 40, B=1, H=1, Sq=4, Sk=40, D=64, scale=0.1, causal=0, splits=0)
+    a.update(kw)
+    assert lib.attn_fwd_splitkv(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["ws"], a["wsb"], a["B"], a["H"], a["Sq"],
+                                a["Sk"], a["D"], a["scale"], a["causal"], a["splits"], None, None) == code
