@@ -30,6 +30,8 @@
 // 128 keys and adds it to an fp32 accumulator in global memory.
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "attn_kernels.hpp"
 #include "device_common.hpp"
 #include "tile_layout.hpp"
@@ -317,18 +319,18 @@ __device__ __forceinline__ void dkdv_elem(const f32x16& sacc, const f32x16& dpac
   ds = pv * (dpacc[r] - dl);
 }
 
-template <int D, class Cfg, bool CAUSAL, bool MASK>
-__device__ __forceinline__ void dkdv_tile(BwdSmem<Cfg, false, false>& sm, int buf, const BwdOffsets<D, Cfg>& of,
-                                          const bf16x8 (&kreg)[D / 16], const bf16x8 (&vreg)[D / 16],
-                                          f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], int q0, int key, int S,
-                                          float C, int hh) {
+// Qb, dOb, nl, dl: this tile's Q and dO tiles and -LSE log2e / Delta rows in
+// LDS.  issue_part(p) issues piece p of the next tile's loads; the pieces go
+// out over phases A and B, one every other step (issued back to back they
+// fill the memory pipeline and stall the wavefront for hundreds of cycles).
+template <int D, class Cfg, bool CAUSAL, bool MASK, class IssuePart>
+__device__ __forceinline__ void dkdv_tile(const uint16_t* Qb, const uint16_t* dOb, const float* nl, const float* dl,
+                                          const BwdOffsets<D, Cfg>& of, const bf16x8 (&kreg)[D / 16],
+                                          const bf16x8 (&vreg)[D / 16], f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32],
+                                          int q0, int key, int S, float C, int hh, IssuePart&& issue_part) {
   static_assert(Cfg::NQB == 2 && D / 16 == 8 && D / 32 == 4, "two 32-query blocks, D = 128");
   constexpr int NKS = Cfg::NKS, NDB = Cfg::NDB, CPR = Cfg::CPR;
   tile_marker<MASK>();
-  const uint16_t* Qb = sm.Qs[buf];
-  const uint16_t* dOb = sm.dOs[buf];
-  const float* nl = sm.lse[buf];
-  const float* dl = sm.dlt[buf];
   int mlo = 0, mhi = 0;
   if constexpr (MASK) {  // register (qb, g, e) holds query q0 + 4 hh + 32 qb + 8 g + e
     const int mt = q0 + 4 * hh;
@@ -358,6 +360,7 @@ __device__ __forceinline__ void dkdv_tile(BwdSmem<Cfg, false, false>& sm, int bu
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       if (ks + 2 < NKS) { qa[ks + 2] = qfrag(0, ks + 2); da[ks + 2] = dofrag(0, ks + 2); }
+      if ((ks & 1) == 0) issue_part(ks / 2);
       s0 = mfma32(qa[ks], kreg[ks], s0);
       dp0 = mfma32(da[ks], vreg[ks], dp0);
       __builtin_amdgcn_sched_barrier(0);
@@ -380,6 +383,8 @@ __device__ __forceinline__ void dkdv_tile(BwdSmem<Cfg, false, false>& sm, int bu
         l4[g] = *reinterpret_cast<const f32x4*>(&nl[8 * g + 4 * hh]);
         d4[g] = *reinterpret_cast<const f32x4*>(&dl[8 * g + 4 * hh]);
       }
+      if ((ks & 1) == 0) issue_part(NKS / 2 + ks / 2);
+      if (ks == NKS - 1) issue_part(NKS);
       s1 = mfma32(qa[ks], kreg[ks], s1);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -449,7 +454,7 @@ __device__ __forceinline__ void dkdv_tile(BwdSmem<Cfg, false, false>& sm, int bu
 // kernel (attn_bwd_dq.hip) forms dQ.  VLDS (split mode only) reads the V
 // operand from an LDS tile instead of registers; OCC is the target number of
 // workgroups per compute unit.
-template <int D, int BQ_, bool CAUSAL, bool WITH_DQ, bool VLDS, int OCC, bool KV_AGPR = true>
+template <int D, int BQ_, bool CAUSAL, bool WITH_DQ, bool VLDS, int OCC>
 __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ nlse2, const float* __restrict__ delta,
@@ -517,15 +522,6 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
       const uint32_t off = (uint32_t)keyc * D + 16 * ks + 8 * hh;
       kreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(Kh + off));
       if constexpr (!VLDS) vreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(Vh + off));
-      if constexpr (KV_AGPR && !WITH_DQ && !VLDS) {
-        // The pipelined tile needs more than the 256 arch VGPRs; K and V are
-        // read only as MFMA operands, which gfx950 takes from AGPRs, so they
-        // are placed there once instead of being spilled and reloaded.
-        u32x4 kk = __builtin_bit_cast(u32x4, kreg[ks]), vv = __builtin_bit_cast(u32x4, vreg[ks]);
-        asm volatile("" : "+a"(kk), "+a"(vv));
-        kreg[ks] = __builtin_bit_cast(bf16x8, kk);
-        vreg[ks] = __builtin_bit_cast(bf16x8, vv);
-      }
     }
   }
   const uint16_t* Vw = nullptr;  // this wave's 32 rows of the V tile
@@ -554,15 +550,8 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
     const bool active = !CAUSAL || (q0 + BQ - 1 >= kw0);  // wave-uniform
     if (active) {
       const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > S) || (q0 + BQ > S);
-      if constexpr (!WITH_DQ && !VLDS && Cfg::NQB == 2) {
-        if (need_mask)
-          dkdv_tile<D, Cfg, CAUSAL, true>(sm, buf, of, kreg, vreg, dk, dv, q0, key, S, C, hh);
-        else
-          dkdv_tile<D, Cfg, CAUSAL, false>(sm, buf, of, kreg, vreg, dk, dv, q0, key, S, C, hh);
-      } else {
-        bwd_tile<D, Cfg, CAUSAL, WITH_DQ, VLDS>(sm, buf, of, kreg, vreg, Vw, dk, dv, q0, key, S, C, c32, hh, dsw,
-                                                need_mask);
-      }
+      bwd_tile<D, Cfg, CAUSAL, WITH_DQ, VLDS>(sm, buf, of, kreg, vreg, Vw, dk, dv, q0, key, S, C, c32, hh, dsw,
+                                              need_mask);
     } else {
       if constexpr (WITH_DQ) {
 #pragma unroll
@@ -626,6 +615,212 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
   }
 }
 
+// Split-mode dK/dV kernel for D = 128: the software-pipelined tile of
+// dkdv_tile over 64-query tiles.  One workgroup of four wavefronts owns 128
+// keys; each wavefront keeps its 32 keys' K and V rows and dK, dV
+// accumulators in registers.  The two query-tile buffers are separate
+// __shared__ arrays and the loop is unrolled by two, so that every buffer a
+// tile reads or loads into is known at compile time: the compiler then sees
+// that the next tile's loads cannot alias this tile's LDS transpose reads and
+// does not make those reads wait for the loads, which lets the loads be
+// spread over the tile's MFMA work (SPREAD; otherwise they are issued
+// together at the tile's start).
+//
+// Only unmasked tiles sit in the loop (two copies of the tile code, one per
+// buffer set; four would not fit the register budget): with S a multiple of
+// 128 a non-causal tile never needs the mask, and a causal one only in the
+// workgroup's first two query tiles (queries k0 .. k0 + 127, the diagonal
+// block), which are peeled off before the loop.  RAGGED (S not a multiple of
+// 128) masks every tile instead.
+template <bool CAUSAL, bool RAGGED, bool SPREAD = true>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ nlse2, const float* __restrict__ delta,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int S, float scale, float C) {
+  constexpr int D = 128;
+  using Cfg = BwdCfg<D, 64>;
+  constexpr int BK = Cfg::BK, BQ = Cfg::BQ, NKS = Cfg::NKS, NDB = Cfg::NDB, DMA_Q = Cfg::DMA_Q;
+  constexpr int NPIECE = 2 * DMA_Q + 1;  // Q pieces, dO pieces, then -LSE log2e / Delta
+  static_assert(NPIECE == NKS + 1, "pieces are issued over phases A and B");
+
+  __shared__ __attribute__((aligned(1024))) uint16_t Qs0[Cfg::QTILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t Qs1[Cfg::QTILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t dOs0[Cfg::QTILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t dOs1[Cfg::QTILE];
+  __shared__ __attribute__((aligned(256))) float nl0[Cfg::LROWS];
+  __shared__ __attribute__((aligned(256))) float nl1[Cfg::LROWS];
+  __shared__ __attribute__((aligned(256))) float dl0[Cfg::LROWS];
+  __shared__ __attribute__((aligned(256))) float dl1[Cfg::LROWS];
+
+  const int id = blockIdx.x;
+  const int bh = id % BH;
+  const int ktile = id / BH;  // causal: lowest keys (most work) first
+  const int k0 = ktile * BK;
+  const size_t base = (size_t)bh * (size_t)S * D;
+  const uint16_t* Qh = Q + base;
+  const uint16_t* Kh = K + base;
+  const uint16_t* Vh = V + base;
+  const uint16_t* dOh = dO + base;
+  const float* NLh = nlse2 + (size_t)bh * S;
+  const float* DLh = delta + (size_t)bh * S;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int hh = lane >> 5;
+  const int c32 = lane & 31;
+  const int kw0 = k0 + 32 * wave;
+  const int key = kw0 + c32;
+
+  BwdOffsets<D, Cfg> of;
+  of.init(wave, lane);
+
+  // piece p of query tile qt's loads into buffer set P (0: Qs0 ..., 1: Qs1 ...)
+  auto piece = [&](int qt, auto P, int p) {
+    constexpr int set = decltype(P)::value;
+    uint16_t* qd = set ? Qs1 : Qs0;
+    uint16_t* dd = set ? dOs1 : dOs0;
+    const int q0 = qt * BQ;
+    if (p < DMA_Q) {
+      dma_row_part<D, DMA_Q>(Qh, q0, BQ, S, qd, wave, of.dmaq, p);
+    } else if (p < 2 * DMA_Q) {
+      dma_row_part<D, DMA_Q>(dOh, q0, BQ, S, dd, wave, of.dmaq, p - DMA_Q);
+    } else if (p == 2 * DMA_Q && wave < 2) {
+      const float* src = (wave == 0 ? NLh : DLh) + min(q0 + lane, S - 1);
+      float* dst = (wave == 0) ? (set ? nl1 : nl0) : (set ? dl1 : dl0);
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+    }
+  };
+
+  const int nqt = (S + BQ - 1) / BQ;
+  const int qt0 = CAUSAL ? (k0 / BQ) : 0;
+#pragma unroll
+  for (int p = 0; p < NPIECE; ++p) piece(qt0, std::integral_constant<int, 0>{}, p);
+
+  // K / V rows of this lane's key as MFMA operands (rows past the end are
+  // clamped; their P is masked).  The pipelined tile needs more than the 256
+  // arch VGPRs; K and V are read only as MFMA operands, which gfx950 takes
+  // from AGPRs, so they are placed there once instead of being spilled and
+  // reloaded.
+  bf16x8 kreg[NKS], vreg[NKS];
+  {
+    const int keyc = min(key, S - 1);
+    u32x4 kk[NKS], vv[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const uint32_t off = (uint32_t)keyc * D + 16 * ks + 8 * hh;
+      kk[ks] = *reinterpret_cast<const u32x4*>(Kh + off);
+      vv[ks] = *reinterpret_cast<const u32x4*>(Vh + off);
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      asm volatile("" : "+a"(kk[ks]), "+a"(vv[ks]));
+      kreg[ks] = __builtin_bit_cast(bf16x8, kk[ks]);
+      vreg[ks] = __builtin_bit_cast(bf16x8, vv[ks]);
+    }
+  }
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+  wait_vm_lds<0>();
+  barrier_keep_loads();
+
+  // one tile: reads buffer set P, loads the next tile into set 1 - P.  M:
+  // masked tile (diagonal or ragged), where a causal wave may also have no
+  // query at or after its keys (inactive: it only issues its loads).
+  auto tile = [&](int qt, auto P, auto M) {
+    constexpr int set = decltype(P)::value;
+    constexpr bool MASK = decltype(M)::value;
+    using Next = std::integral_constant<int, 1 - set>;
+    const int q0 = qt * BQ;
+    const bool has_next = qt + 1 < nqt;
+    const bool active = !(CAUSAL && MASK) || (q0 + BQ - 1 >= kw0);  // wave-uniform
+    if (active) {
+      // after the last tile the pieces reload it into the free set (in bounds,
+      // never read), which keeps the tile branch-free
+      auto part = [&](int p) {
+        if (SPREAD && p < NPIECE) piece(has_next ? qt + 1 : qt, Next{}, p);
+      };
+      if constexpr (!SPREAD) {
+        if (has_next) {
+#pragma unroll
+          for (int p = 0; p < NPIECE; ++p) piece(qt + 1, Next{}, p);
+        }
+      }
+      const uint16_t* Qb = set ? Qs1 : Qs0;
+      const uint16_t* dOb = set ? dOs1 : dOs0;
+      const float* nl = set ? nl1 : nl0;
+      const float* dl = set ? dl1 : dl0;
+      // The read offsets are made opaque per tile: otherwise each buffer set's
+      // full addresses are loop-invariant, get hoisted and held in registers
+      // (twice the offsets); this way every read is offset register + the
+      // array's constant LDS address, which folds into the instruction.
+      BwdOffsets<D, Cfg> ot = of;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(ot.arow[ks]));
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(ot.trq[db][0]), "+v"(ot.trq[db][1]));
+      dkdv_tile<D, Cfg, CAUSAL, MASK>(Qb, dOb, nl, dl, ot, kreg, vreg, dk, dv, q0, key, S, C, hh, part);
+    } else if (has_next) {
+#pragma unroll
+      for (int p = 0; p < NPIECE; ++p) piece(qt + 1, Next{}, p);
+    }
+    // the next tile's loads landed (this wave's) and all LDS reads done; the
+    // barrier publishes the tile and frees this one
+    __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (0 << 14));  // vmcnt(0) lgkmcnt(0)
+    barrier_keep_loads();
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using M = std::integral_constant<bool, RAGGED>;
+  int qt = qt0;
+  if constexpr (CAUSAL && !RAGGED) {  // diagonal block: qt0 even, nqt >= qt0 + 2
+    tile(qt, P0{}, std::true_type{});
+    tile(qt + 1, P1{}, std::true_type{});
+    qt += 2;
+  }
+  for (; qt < nqt; qt += 2) {
+    tile(qt, P0{}, M{});
+    if (RAGGED && qt + 1 >= nqt) break;  // without RAGGED the tile count is even
+    tile(qt + 1, P1{}, M{});
+  }
+
+  // ---- epilogue: dK = scale * acc, dV = acc (bf16) -------------------------
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int d = 32 * db + c32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kk = kw0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      if (kk < S) {
+        dK[base + (size_t)kk * D + d] = __builtin_bit_cast(uint16_t, (__bf16)(dk[db][r] * scale));
+        dV[base + (size_t)kk * D + d] = __builtin_bit_cast(uint16_t, (__bf16)dv[db][r]);
+      }
+    }
+  }
+}
+
+template <bool CAUSAL, bool RAGGED, bool SPREAD>
+static hipError_t launch_dkdv_pipe_rt(const BwdArgs& a, hipStream_t st) {
+  const int BH = a.B * a.H;
+  const int nkt = (a.S + 127) / 128;
+  prof_begin(KID_BWD_DKDV, st);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<CAUSAL, RAGGED, SPREAD>), dim3(nkt * BH), dim3(256), 0, st, (const uint16_t*)a.Q,
+                     (const uint16_t*)a.K, (const uint16_t*)a.V, (const uint16_t*)a.dO, a.nlse2, a.delta,
+                     (uint16_t*)a.dK, (uint16_t*)a.dV, BH, a.S, a.scale, a.scale * kLog2e);
+  prof_end(KID_BWD_DKDV, st);
+  return hipGetLastError();
+}
+
+template <bool CAUSAL, bool SPREAD = true>
+static hipError_t launch_dkdv_pipe_t(const BwdArgs& a, hipStream_t st) {
+  return (a.S % 128 == 0) ? launch_dkdv_pipe_rt<CAUSAL, false, SPREAD>(a, st)
+                          : launch_dkdv_pipe_rt<CAUSAL, true, SPREAD>(a, st);
+}
+
 // Delta_i = sum_d dO_id O_id (fp32), nlse2_i = -LSE_i log2(e), and zero the
 // fp32 dQ accumulator (atomic mode).  D/8 lanes share one row; each lane
 // takes eight columns.
@@ -675,13 +870,13 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict
 
 bool bwd_supported(int D) { return D == 64 || D == 128; }
 
-template <int D, int BQ, bool CAUSAL, bool WITH_DQ, bool VLDS, int OCC, bool KV_AGPR = true>
+template <int D, int BQ, bool CAUSAL, bool WITH_DQ, bool VLDS, int OCC>
 static hipError_t launch_main_t(const BwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   const int nkt = (a.S + BwdCfg<D, BQ>::BK - 1) / BwdCfg<D, BQ>::BK;
   const int kid = WITH_DQ ? KID_BWD_MAIN : KID_BWD_DKDV;
   prof_begin(kid, st);
-  hipLaunchKernelGGL((bwd_main_kernel<D, BQ, CAUSAL, WITH_DQ, VLDS, OCC, KV_AGPR>), dim3(nkt * BH), dim3(256), 0, st,
+  hipLaunchKernelGGL((bwd_main_kernel<D, BQ, CAUSAL, WITH_DQ, VLDS, OCC>), dim3(nkt * BH), dim3(256), 0, st,
                      (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                      (const uint16_t*)a.dO, a.nlse2, a.delta, a.dq32, (uint16_t*)a.dK,
                      (uint16_t*)a.dV, BH, a.S, a.scale, a.scale * kLog2e);
@@ -719,10 +914,11 @@ static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
       case 1: return launch_main_t<D, 32, CAUSAL, false, true, 2>(a, st);
       case 2: return launch_main_t<D, 32, CAUSAL, false, false, 1>(a, st);
       case 3: return launch_main_t<D, 64, CAUSAL, false, true, 1>(a, st);
-      case 4: return launch_main_t<D, 64, CAUSAL, false, false, 1, false>(a, st);  // K, V left to the allocator
+      case 4: return launch_main_t<D, 64, CAUSAL, false, false, 1>(a, st);  // one-pass tile, no pipeline
+      case 5: return launch_dkdv_pipe_t<CAUSAL, false>(a, st);              // next tile loaded at tile start
       default: break;
     }
-    return launch_main_t<D, 64, CAUSAL, false, false, 1>(a, st);
+    return launch_dkdv_pipe_t<CAUSAL>(a, st);
   }
   return launch_main_t<D, 32, CAUSAL, false, false, 2>(a, st);
 }
