@@ -11,10 +11,15 @@ from ._lib import (  # noqa: F401
     AttnError,
     attn_bwd,
     attn_fwd,
+    attn_fwd_fp8,
+    attn_fwd_fp8_quantized,
     attn_fwd_splitkv,
     bwd_workspace_bytes,
     fwd_splitkv_workspace_bytes,
     exp2_eval,
+    fp8_buffer_bytes,
+    fp8_buffer_views,
+    fp8_quantize,
     load,
     prof_collect,
     prof_enable,

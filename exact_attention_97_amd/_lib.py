@@ -28,7 +28,9 @@ EXPORTS = (
     "attn_default_opts", "attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd", "attn_strerror",
     "attn_exp2_eval", "attn_prof_enable", "attn_prof_reset", "attn_prof_collect", "attn_version",
     "attn_fwd_splitkv_workspace_bytes", "attn_fwd_splitkv",
+    "attn_fp8_buffer_bytes", "attn_fp8_buffer_offsets", "attn_fp8_quantize", "attn_fwd_fp8",
 )
+FP8_REGIONS = ("q8", "k8", "v8t", "qs", "ks", "vs", "scratch")
 
 
 class AttnOpts(ctypes.Structure):
@@ -80,6 +82,14 @@ def load():
     lib.attn_fwd_splitkv_workspace_bytes.restype = sz
     lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i, optp, vp]
     lib.attn_fwd_splitkv.restype = i
+    lib.attn_fp8_buffer_bytes.argtypes = [i, i, i, i]
+    lib.attn_fp8_buffer_bytes.restype = sz
+    lib.attn_fp8_buffer_offsets.argtypes = [i, i, i, i, ctypes.POINTER(sz)]
+    lib.attn_fp8_buffer_offsets.restype = i
+    lib.attn_fp8_quantize.argtypes = [vp, vp, vp, vp, vp, sz, i, i, i, i, vp]
+    lib.attn_fp8_quantize.restype = i
+    lib.attn_fwd_fp8.argtypes = [vp, sz, vp, vp, i, i, i, i, f, i, optp, vp]
+    lib.attn_fwd_fp8.restype = i
     _lib = lib
     return lib
 
@@ -168,6 +178,73 @@ def attn_fwd_splitkv(q, k, v, scale=None, causal=False, num_splits=0, exp_mode="
         workspace.numel() * workspace.element_size(), B, H, Sq, Sk, D, float(scale), int(bool(causal)),
         int(num_splits), ctypes.byref(opts), _stream_ptr(stream)))
     return out, lse
+
+
+def fp8_buffer_bytes(B, H, S, D):
+    return int(load().attn_fp8_buffer_bytes(B, H, S, D))
+
+
+def fp8_buffer_views(buf, B, H, S, D):
+    """Views of the regions of an FP8 buffer (layout of include/attn97.h): dict name -> tensor."""
+    import torch
+
+    offs = (ctypes.c_size_t * 7)()
+    _check("attn_fp8_buffer_offsets", load().attn_fp8_buffer_offsets(B, H, S, D, offs))
+    Sp = (S + 127) // 128 * 128
+    BH = B * H
+    shapes = {"q8": ((BH, Sp, D), torch.uint8), "k8": ((BH, Sp, D), torch.uint8), "v8t": ((BH, D, Sp), torch.uint8),
+              "qs": ((BH, Sp), torch.float32), "ks": ((BH, Sp // 64), torch.float32), "vs": ((BH, D), torch.float32)}
+    out = {}
+    for n, name in enumerate(FP8_REGIONS[:6]):
+        shape, dt = shapes[name]
+        nbytes = math.prod(shape) * (4 if dt == torch.float32 else 1)
+        out[name] = buf[offs[n]:offs[n] + nbytes].view(dt).view(shape)
+    return out
+
+
+def fp8_quantize(q, k, v, signs=None, buf=None, stream=None):
+    """Transform (with signs, a float32 [D] device tensor of +-1) and quantize Q, K, V to E4M3; returns the buffer."""
+    import torch
+
+    lib = load()
+    B, H, S, D = _check_qkv(q, k, v)
+    need = fp8_buffer_bytes(B, H, S, D)
+    if buf is None:
+        buf = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if signs is not None and (signs.dtype != torch.float32 or not signs.is_cuda or signs.numel() != D):
+        raise ValueError("signs must be a float32 device tensor of D elements")
+    _check("attn_fp8_quantize", lib.attn_fp8_quantize(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), None if signs is None else signs.data_ptr(), buf.data_ptr(),
+        buf.numel(), B, H, S, D, _stream_ptr(stream)))
+    return buf
+
+
+def attn_fwd_fp8_quantized(buf, B, H, S, D, scale=None, causal=False, rescale_tau=8.0, out=None, lse=None,
+                           device=None, stream=None):
+    """FP8 forward from a quantized buffer; returns (O bf16 [B,H,S,D], LSE fp32 [B,H,S])."""
+    import torch
+
+    lib = load()
+    dev = buf.device if device is None else device
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, H, S, D), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    opts = make_opts(rescale_tau=rescale_tau)
+    _check("attn_fwd_fp8", lib.attn_fwd_fp8(buf.data_ptr(), buf.numel(), out.data_ptr(), lse.data_ptr(), B, H, S, D,
+                                            float(scale), int(bool(causal)), ctypes.byref(opts),
+                                            _stream_ptr(stream)))
+    return out, lse
+
+
+def attn_fwd_fp8(q, k, v, signs=None, scale=None, causal=False, rescale_tau=8.0, buf=None, out=None, lse=None,
+                 stream=None):
+    """FP8 forward with incoherent processing: quantize then attend; returns (O, LSE)."""
+    B, H, S, D = _check_qkv(q, k, v)
+    buf = fp8_quantize(q, k, v, signs, buf, stream)
+    return attn_fwd_fp8_quantized(buf, B, H, S, D, scale, causal, rescale_tau, out, lse, q.device, stream)
 
 
 def bwd_workspace_bytes(B, H, S, D, causal=False, bwd_mode="split"):

@@ -282,6 +282,56 @@ attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O,
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+size_t attn_fp8_buffer_bytes(int B, int H, int S, int D) {
+  if (check_shape(B, H, S, D) != ATTN_OK || D != 128) return 0;
+  return attn97::fp8_layout(B, H, S, D, nullptr, nullptr);
+}
+
+attn_status attn_fp8_buffer_offsets(int B, int H, int S, int D, size_t offsets[7]) {
+  if (!offsets) return ATTN_ERR_NULL;
+  attn_status st = check_shape(B, H, S, D);
+  if (st != ATTN_OK) return st;
+  if (D != 128) return ATTN_ERR_UNSUPPORTED;
+  attn97::Fp8Buf f;
+  attn97::fp8_layout(B, H, S, D, nullptr, &f);
+  for (int i = 0; i < 7; ++i) offsets[i] = f.offsets[i];
+  return ATTN_OK;
+}
+
+attn_status attn_fp8_quantize(const void* Q, const void* K, const void* V, const float* signs, void* buf,
+                              size_t buf_bytes, int B, int H, int S, int D, void* stream) {
+  if (!Q || !K || !V) return ATTN_ERR_NULL;
+  attn_status st = check_shape(B, H, S, D);
+  if (st != ATTN_OK) return st;
+  if (D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(V, 16) || misaligned(signs, 4)) return ATTN_ERR_ALIGN;
+  attn97::Fp8Buf f;
+  const size_t need = attn97::fp8_layout(B, H, S, D, buf, &f);
+  if (buf == nullptr || buf_bytes < need || misaligned(buf, 256)) return ATTN_ERR_WORKSPACE;
+  hipError_t e = attn97::launch_fp8_quantize(Q, K, V, signs, f, B, H, S, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_fwd_fp8(const void* buf, size_t buf_bytes, void* O, float* LSE, int B, int H, int S, int D,
+                         float scale, int causal, const attn_opts* opts, void* stream) {
+  if (!O || !LSE) return ATTN_ERR_NULL;
+  attn_status st = check_shape(B, H, S, D);
+  if (st != ATTN_OK) return st;
+  if (D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (misaligned(O, 16) || misaligned(LSE, 16)) return ATTN_ERR_ALIGN;
+  if (!isfinite(scale)) return ATTN_ERR_VALUE;
+  attn_opts o;
+  st = read_opts(opts, &o);
+  if (st != ATTN_OK) return st;
+  attn97::Fp8Buf f;
+  const size_t need = attn97::fp8_layout(B, H, S, D, const_cast<void*>(buf), &f);
+  if (buf == nullptr || buf_bytes < need || misaligned(buf, 256)) return ATTN_ERR_WORKSPACE;
+  hipError_t e = attn97::launch_fwd_fp8(f, O, LSE, B, H, S, fabsf(scale) * kLog2eHost,
+                                        (scale < 0.0f) ? 0x80808080u : 0u, o.rescale_tau, causal ? 1 : 0,
+                                        (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 attn_status attn_exp2_eval(const float* x, float* y, long n, int mode, void* stream) {
   if (n < 0) return ATTN_ERR_SHAPE;
   if (mode != ATTN_EXP_NATIVE && mode != ATTN_EXP_POLY) return ATTN_ERR_UNSUPPORTED;
@@ -305,8 +355,9 @@ attn_status attn_prof_reset(void) {
 
 attn_status attn_prof_collect(const char* kernel, int* count, double* total_ms) {
   if (!kernel || !count || !total_ms) return ATTN_ERR_NULL;
-  static const char* names[attn97::KID_COUNT] = {"fwd",      "bwd_pre", "bwd_main",     "dq_convert",
-                                                "bwd_dkdv", "bwd_dq",  "fwd_splitkv", "splitkv_merge"};
+  static const char* names[attn97::KID_COUNT] = {"fwd",         "bwd_pre",       "bwd_main",     "dq_convert",
+                                                "bwd_dkdv",    "bwd_dq",        "fwd_splitkv", "splitkv_merge",
+                                                "fp8_quantize", "fwd_fp8"};
   int kid = -1;
   for (int i = 0; i < attn97::KID_COUNT; ++i)
     if (strcmp(kernel, names[i]) == 0) kid = i;

@@ -1,0 +1,504 @@
+// attn_fp8.hip - FP8 (OCP E4M3) forward attention with incoherent processing,
+// D = 128.
+//
+// Page "FlashAttention-3 и FlashAttention-4", section "Поддержка FP8 с
+// контролем ошибок": before the rounding to FP8, Q and K pass through a
+// cheap transform that spreads outliers over the coordinates.  Here the
+// transform is x -> (x * s) H / sqrt(D) with H the Sylvester-Hadamard matrix
+// and s caller-given random signs; it is orthogonal, so Q K^T is unchanged.
+//
+// Two steps:
+//  * quantize: Q and K rows transformed (a 128-point fast Walsh-Hadamard
+//    transform in float64 registers, one row per four lanes) and rounded to E4M3 with one
+//    scale per Q row and one per 64-key K tile; V rounded with one scale per
+//    column (two small kernels find the column maxima first) and stored
+//    transposed, keys permuted inside each 64-key group so that the PV
+//    operand of a lane is 32 contiguous bytes.
+//  * forward: the online-softmax kernel of the bf16 path with both products
+//    on v_mfma_f32_32x32x64_f8f6f4 (twice the bf16 MFMA rate): S^T = K Q^T
+//    and O^T += V^T P^T with P rounded to E4M3 in registers.  The product
+//    contracts lane half h and byte j of both operands against each other,
+//    so any assignment of the 64 contraction indices to (h, j) works as long
+//    as both operands use it: K and Q use d = 64 t + 32 h + j, P and V^T use
+//    the key order in which the score MFMA leaves P in its accumulators.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "attn_kernels.hpp"
+#include "device_common.hpp"
+#include "tile_layout.hpp"
+
+namespace attn97 {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int FD = 128;   // head dim
+constexpr int FBC = 64;   // keys per tile
+constexpr int FBR = 128;  // queries per workgroup (four wavefronts of 32)
+constexpr float kE4M3Max = 448.0f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+// clamp to the finite E4M3 range (the conversion turns larger values into NaN)
+__device__ __forceinline__ float clamp448(float x) { return __builtin_fminf(__builtin_fmaxf(x, -kE4M3Max), kE4M3Max); }
+
+// four floats to four E4M3 bytes (round to nearest even), byte i = x_i
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  // format codes 0 / 0: both operands E4M3; no block scales
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ i32x8 lds_frag32(const uint8_t* p0, const uint8_t* p1) {
+  const u32x4 a = *reinterpret_cast<const u32x4*>(p0);
+  const u32x4 b = *reinterpret_cast<const u32x4*>(p1);
+  return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+}
+
+// ---------------------------------------------------------------------------
+// Quantize Q and K.  Grid (Sp / 64, B*H, 2): z = 0 Q, z = 1 K; four
+// wavefronts of 16 rows; lane l handles quarter qd = l >> 4 (elements
+// 32 qd .. 32 qd + 31) of row l & 15.  Rows past S are zero (Q scale 1).
+//
+// The transform runs in float64: its outputs are sums of 128 bf16 values
+// with signs, which float64 holds exactly (float32 would round them once
+// outliers widen the range of the summands), so the codes depend on the
+// exact transform only.  Its butterfly stages commute; the two across
+// quarters are exchanges between lanes (H_2n x = [H_n (a + b); H_n (a - b)]
+// for x = [a; b]), the other five run inside each lane.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fp8_qk_quant_kernel(const uint16_t* __restrict__ Q,
+                                                           const uint16_t* __restrict__ K,
+                                                           const float* __restrict__ signs, Fp8Buf f, int S) {
+  __shared__ double wave_max[4];
+  const int which = blockIdx.z;
+  const int bh = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int qd = lane >> 4;
+  const int row = blockIdx.x * 64 + 16 * wave + (lane & 15);
+  const int Sp = f.Sp;
+  const uint16_t* src = (which ? K : Q) + (size_t)bh * S * FD;
+
+  double x[32];
+  if (row < S) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(src + (size_t)row * FD + 32 * qd);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 w = p[c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[8 * c + 2 * e] = (double)bf16_lo(w[e]);
+        x[8 * c + 2 * e + 1] = (double)bf16_hi(w[e]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = 0.0;
+  }
+
+  double norm = 1.0;
+  if (signs != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] *= (double)signs[32 * qd + i];
+    // stage 64 (partner quarter qd ^ 2), then stage 32 (partner qd ^ 1): the
+    // lane holding the upper part keeps (other - own), the lower one (own + other)
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int m = st == 0 ? 32 : 16;
+      const bool upper = (lane & m) != 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const double other = __shfl_xor(x[i], m);
+        x[i] = upper ? (other - x[i]) : (x[i] + other);
+      }
+    }
+#pragma unroll
+    for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if ((i & h) == 0) {
+          const double a = x[i], b = x[i + h];
+          x[i] = a + b;
+          x[i + h] = a - b;
+        }
+      }
+    }
+    norm = 0.088388347648318440550;  // 1 / sqrt(128)
+  }
+
+  double amax = 0.0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = __builtin_fmax(amax, __builtin_fabs(x[i]));
+  amax = __builtin_fmax(amax, __shfl_xor(amax, 16));  // the row's four quarters
+  amax = __builtin_fmax(amax, __shfl_xor(amax, 32));
+  if (which == 1) {  // K: one scale per 64-key tile (all four wavefronts)
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) amax = __builtin_fmax(amax, __shfl_xor(amax, o));
+    if (lane == 0) wave_max[wave] = amax;
+    __syncthreads();
+    amax = __builtin_fmax(__builtin_fmax(wave_max[0], wave_max[1]), __builtin_fmax(wave_max[2], wave_max[3]));
+  }
+  // the transformed row is x * norm; its scale is max|x * norm| / 448 and its
+  // codes are E4M3(x * norm / scale) = E4M3(x * 448 / max|x|), formed with one
+  // correctly rounded division, so a value exactly halfway between two codes
+  // stays halfway (and goes to the even code)
+  const float sc = amax > 0.0 ? (float)(amax * norm / (double)kE4M3Max) : 1.0f;
+  const double den = amax > 0.0 ? amax : 1.0;
+
+  uint8_t* dst = (which ? f.k8 : f.q8) + ((size_t)bh * Sp + row) * FD + 32 * qd;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int d = 16 * c + 4 * e;
+      float y[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) y[u] = clamp448((float)(x[d + u] * (double)kE4M3Max / den));
+      w[e] = pack_e4m3x4(y[0], y[1], y[2], y[3]);
+    }
+    *reinterpret_cast<u32x4*>(dst + 16 * c) = w;
+  }
+  if (which == 0) {
+    if (qd == 0) f.qs[(size_t)bh * Sp + row] = sc;
+  } else if (tid == 0) {
+    f.ks[(size_t)bh * (Sp / FBC) + blockIdx.x] = sc;
+  }
+}
+
+// Column maxima of V over 128-row chunks.  Grid (Sp / 128, B*H), 128 threads (d).
+__global__ __launch_bounds__(128) void fp8_v_amax_kernel(const uint16_t* __restrict__ V, Fp8Buf f, int S) {
+  const int chunk = blockIdx.x, bh = blockIdx.y, d = threadIdx.x;
+  const uint16_t* src = V + (size_t)bh * S * FD + d;
+  const int r0 = chunk * 128, r1 = min(S, r0 + 128);
+  float m = 0.0f;
+  for (int r = r0; r < r1; ++r) m = __builtin_fmaxf(m, __builtin_fabsf(bf16_lo((uint32_t)src[(size_t)r * FD])));
+  f.vpart[((size_t)bh * (f.Sp / 128) + chunk) * FD + d] = m;
+}
+
+// V column scales from the chunk maxima.  Grid B*H, 128 threads (d).  The
+// column maximum itself is left in the first chunk slot for the quantizer.
+__global__ __launch_bounds__(128) void fp8_v_scale_kernel(Fp8Buf f) {
+  const int bh = blockIdx.x, d = threadIdx.x;
+  const int nch = f.Sp / 128;
+  float m = 0.0f;
+  for (int c = 0; c < nch; ++c) m = __builtin_fmaxf(m, f.vpart[((size_t)bh * nch + c) * FD + d]);
+  f.vs[(size_t)bh * FD + d] = m > 0.0f ? m / kE4M3Max : 1.0f;
+  f.vpart[(size_t)bh * nch * FD + d] = m;
+}
+
+// V to E4M3, transposed: row d of head bh holds the Sp keys, and inside each
+// 64-key group key 32 kb + 8 r4 + 4 h + e sits at byte 32 h + 16 kb + 4 r4 + e
+// (h, kb in {0, 1}; r4, e in 0..3).  Grid (Sp / 64, B*H), 128 threads (d).
+__global__ __launch_bounds__(128) void fp8_v_quant_kernel(const uint16_t* __restrict__ V, Fp8Buf f, int S) {
+  const int tile = blockIdx.x, bh = blockIdx.y, d = threadIdx.x;
+  const int k0 = tile * FBC;
+  const uint16_t* src = V + (size_t)bh * S * FD + d;
+  const float m = f.vpart[(size_t)bh * (f.Sp / 128) * FD + d];  // column max (see fp8_v_scale_kernel)
+  const float den = m > 0.0f ? m : 1.0f;
+  uint32_t w[16];
+#pragma unroll
+  for (int g = 0; g < 16; ++g) {  // keys 4 g .. 4 g + 3 of the tile
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int key = k0 + 4 * g + e;
+      v[e] = key < S ? clamp448(bf16_lo((uint32_t)src[(size_t)key * FD]) * kE4M3Max / den) : 0.0f;
+    }
+    const int h = g & 1, kb = g >> 3, r4 = (g >> 1) & 3;
+    w[8 * h + 4 * kb + r4] = pack_e4m3x4(v[0], v[1], v[2], v[3]);
+  }
+  uint8_t* dst = f.v8t + ((size_t)bh * FD + d) * f.Sp + k0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    *reinterpret_cast<u32x4*>(dst + 16 * c) = u32x4{w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]};
+}
+
+// ---------------------------------------------------------------------------
+// Forward.  One workgroup of four wavefronts per 128 queries of one head;
+// 64-key tiles of K (64 rows x 128 B) and V^T (128 rows x 64 B) stream
+// through two LDS buffers each with global_load_lds.  16-byte chunks are
+// XOR-swizzled (K: chunk ^ ((key >> 1) & 7); V^T: chunk ^ ((d >> 2) & 3)) so
+// that each 16-lane group of a 128-bit operand read hits 16 distinct bank
+// groups.
+// ---------------------------------------------------------------------------
+struct Fp8Wave {
+  // LDS byte offsets of this lane's operand chunks (block 0 / d-block 0)
+  int kfrag[2][2];  // [t][half]: key row c32, chunks 4 t + 2 hh + half
+  int vfrag[2];     // [half]: row c32 of V^T, chunks 2 hh + half
+  uint32_t kdma[2], vdma[2];  // DMA source offsets (bytes) of this lane's chunks
+
+  __device__ __forceinline__ void init(int wave, int lane, int Sp) {
+    const int hh = lane >> 5, c32 = lane & 31;
+    const int kx = (c32 >> 1) & 7, vx = (c32 >> 2) & 3;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) kfrag[t][h] = c32 * FD + (((4 * t + 2 * hh + h) ^ kx) * 16);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) vfrag[h] = c32 * FBC + (((2 * hh + h) ^ vx) * 16);
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int P = 64 * (2 * wave + n) + lane;  // physical 16-byte chunk of the tile
+      const int krow = P >> 3, kc = (P & 7) ^ ((krow >> 1) & 7);
+      kdma[n] = (uint32_t)(krow * FD + kc * 16);
+      const int vrow = P >> 2, vc = (P & 3) ^ ((vrow >> 2) & 3);
+      vdma[n] = (uint32_t)vrow * (uint32_t)Sp + (uint32_t)(vc * 16);
+    }
+  }
+};
+
+template <bool MASK>
+__device__ __forceinline__ float fp8_tile_max(f32x16 (&s)[2], int k0, int lim, int hh) {
+  float mx = kNegInf;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (MASK) {
+        const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (key > lim) s[kb][r] = kNegInf;
+      }
+      mx = __builtin_fmaxf(mx, s[kb][r]);
+    }
+  }
+  return __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+}
+
+__global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8Buf f, uint16_t* __restrict__ O, float* __restrict__ LSE,
+                                                         int BH, int S, int nqt, float C, uint32_t qsign, float tau,
+                                                         int causal) {
+  __shared__ __attribute__((aligned(1024))) uint8_t Kb[2][FBC * FD];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vb[2][FD * FBC];
+
+  const int Sp = f.Sp;
+  const int id = blockIdx.x;
+  const int bh = id % BH;
+  const int rank = id / BH;
+  const int qt = causal ? (nqt - 1 - rank) : rank;  // heaviest causal tiles first
+  const int q0 = qt * FBR;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int hh = lane >> 5;
+  const int c32 = lane & 31;
+  const int qw0 = q0 + 32 * wave;
+  const int qrow = qw0 + c32;  // < Sp always
+  const uint8_t* Kh = f.k8 + (size_t)bh * Sp * FD;
+  const uint8_t* Vh = f.v8t + (size_t)bh * FD * Sp;
+  const float* ksh = f.ks + (size_t)bh * (Sp / FBC);
+
+  // Q^T operand: lane holds bytes 64 t + 32 hh .. + 31 of row qrow
+  i32x8 qreg[2];
+  {
+    const uint8_t* qp = f.q8 + ((size_t)bh * Sp + qrow) * FD;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      u32x4 a = *reinterpret_cast<const u32x4*>(qp + 64 * t + 32 * hh);
+      u32x4 b = *reinterpret_cast<const u32x4*>(qp + 64 * t + 32 * hh + 16);
+      a ^= qsign;  // a negative scale flips the sign of every Q code
+      b ^= qsign;
+      qreg[t] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+    }
+  }
+  const float cq = C * f.qs[(size_t)bh * Sp + qrow];  // scale * log2(e) * this row's Q scale
+
+  const int kend = causal ? min(S, q0 + FBR) : S;
+  const int nkt = (kend + FBC - 1) / FBC;
+  const int wend = causal ? min(kend, qw0 + 32) : kend;
+  const int nkt_w = qw0 < S ? (wend + FBC - 1) / FBC : 0;
+  int nfull = causal ? (qw0 + 1) / FBC : nkt_w;
+  nfull = max(0, min(nfull, S / FBC));
+  const int lim = causal ? min(qrow, S - 1) : (S - 1);
+
+  Fp8Wave of;
+  of.init(wave, lane, Sp);
+
+  auto dma = [&](const uint8_t* src, uint8_t* dst, const uint32_t (&off)[2]) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+      __builtin_amdgcn_global_load_lds(src + off[n], (__attribute__((address_space(3))) void*)(dst + 1024 * (2 * wave + n)),
+                                       16, 0, 0);
+  };
+  // iteration j issues K(j + 2) and V(j + 1) into the buffers the barrier of
+  // iteration j - 1 freed; it reads K(j + 1) (scores of the next tile) and V(j)
+  auto issue = [&](int j) {
+    if (j + 2 < nkt) dma(Kh + (size_t)(j + 2) * FBC * FD, Kb[j & 1], of.kdma);
+    if (j + 1 >= 0 && j + 1 < nkt) dma(Vh + (size_t)(j + 1) * FBC, Vb[(j + 1) & 1], of.vdma);
+  };
+  auto scores = [&](const uint8_t* kb_, f32x16 (&s)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        s[kb] = mfma_fp8(lds_frag32(kb_ + 32 * kb * FD + of.kfrag[t][0], kb_ + 32 * kb * FD + of.kfrag[t][1]), qreg[t],
+                         s[kb]);
+    }
+  };
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
+  float m_run = kNegInf;  // running max in log2 units
+  float l_part = 0.0f;    // this lane's partial row sum (unrounded P)
+
+  issue(-2);
+  issue(-1);
+  wait_vm_lds<0>();
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  scores(Kb[0], sa);
+  wait_vm_lds<63>();
+  barrier_keep_loads();
+
+  auto step = [&](auto maskc, int kt, f32x16(&scur)[2], f32x16(&snext)[2]) {
+    constexpr bool MASK = decltype(maskc)::value;
+    const float ct = cq * ksh[kt];  // score factor of this tile (log2 units)
+    const float mx = fp8_tile_max<MASK>(scur, kt * FBC, lim, hh);
+    const float mxs = (mx == kNegInf) ? kNegInf : mx * ct;
+    const float m_new = __builtin_fmaxf(m_run, mxs);
+    const bool grow = __any((m_new - m_run) > tau);
+    const float alpha = (grow && m_new != kNegInf) ? exp2_native(m_run - m_new) : 1.0f;
+    m_run = grow ? m_new : m_run;
+    l_part *= alpha;
+    __builtin_amdgcn_s_setprio(1);
+    scores(Kb[(kt + 1) & 1], snext);
+    // P = exp2(S ct - m) to E4M3: byte 16 kb + r of the operand is register r
+    // of block kb, the key order of V^T in LDS
+    i32x8 pf;
+    const float negm = -m_run;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) {
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * w4 + e;
+          float x = exp2_native(__builtin_fmaf(scur[kb][r], ct, negm));
+          if (MASK && scur[kb][r] == kNegInf) x = 0.0f;
+          p[e] = x;
+          l_part += x;
+        }
+        pf[4 * kb + w4] = (int)pack_e4m3x4(p[0], p[1], p[2], p[3]);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    if (grow) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+    }
+    const uint8_t* vb = Vb[kt & 1];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      oacc[db] = mfma_fp8(lds_frag32(vb + 32 * db * FBC + of.vfrag[0], vb + 32 * db * FBC + of.vfrag[1]), pf, oacc[db]);
+  };
+
+  auto iteration = [&](int kt, f32x16(&scur)[2], f32x16(&snext)[2]) {
+    issue(kt);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt < nkt_w) {
+      if (kt < nfull)
+        step(std::false_type{}, kt, scur, snext);
+      else
+        step(std::true_type{}, kt, scur, snext);
+    }
+    wait_vm_lds<0>();
+    barrier_keep_loads();
+  };
+  for (int kt = 0; kt < nkt; kt += 2) {
+    iteration(kt, sa, sb);
+    if (kt + 1 < nkt) iteration(kt + 1, sb, sa);
+  }
+
+  // ---- epilogue: O = acc * vs / l, LSE = ln2 * (m + log2 l) ----------------
+  const float l_tot = l_part + __shfl_xor(l_part, 32);
+  const float inv = 1.0f / l_tot;
+  if (qrow < S) {
+    const float* vsh = f.vs + (size_t)bh * FD;
+    uint16_t* orow = O + ((size_t)bh * S + qrow) * FD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * hh;
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(vsh + d) * inv;
+        *reinterpret_cast<u32x2*>(orow + d) = pack_bf16x4(oacc[db][4 * g] * s4[0], oacc[db][4 * g + 1] * s4[1],
+                                                          oacc[db][4 * g + 2] * s4[2], oacc[db][4 * g + 3] * s4[3]);
+      }
+    }
+    if (hh == 0) LSE[(size_t)bh * S + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+  }
+}
+
+}  // namespace
+
+size_t fp8_layout(int B, int H, int S, int D, void* base, Fp8Buf* f) {
+  (void)D;
+  auto r256 = [](size_t n) { return (n + 255) & ~(size_t)255; };
+  const size_t BH = (size_t)B * H;
+  const int Sp = (S + FBR - 1) / FBR * FBR;
+  const size_t sz[7] = {r256(BH * Sp * FD),                      // q8
+                        r256(BH * Sp * FD),                      // k8
+                        r256(BH * FD * Sp),                      // v8t
+                        r256(BH * Sp * sizeof(float)),           // qs
+                        r256(BH * (Sp / FBC) * sizeof(float)),   // ks
+                        r256(BH * FD * sizeof(float)),           // vs
+                        r256(BH * (Sp / 128) * FD * sizeof(float))};  // vpart
+  size_t off[7], total = 0;
+  for (int i = 0; i < 7; ++i) {
+    off[i] = total;
+    total += sz[i];
+  }
+  if (f != nullptr) {
+    char* p = static_cast<char*>(base);
+    f->Sp = Sp;
+    f->q8 = reinterpret_cast<uint8_t*>(p + off[0]);
+    f->k8 = reinterpret_cast<uint8_t*>(p + off[1]);
+    f->v8t = reinterpret_cast<uint8_t*>(p + off[2]);
+    f->qs = reinterpret_cast<float*>(p + off[3]);
+    f->ks = reinterpret_cast<float*>(p + off[4]);
+    f->vs = reinterpret_cast<float*>(p + off[5]);
+    f->vpart = reinterpret_cast<float*>(p + off[6]);
+    for (int i = 0; i < 7; ++i) f->offsets[i] = off[i];
+  }
+  return total;
+}
+
+hipError_t launch_fp8_quantize(const void* Q, const void* K, const void* V, const float* signs, const Fp8Buf& f,
+                               int B, int H, int S, hipStream_t st) {
+  const int BH = B * H;
+  prof_begin(KID_FP8_QUANT, st);
+  hipLaunchKernelGGL(fp8_qk_quant_kernel, dim3(f.Sp / 64, BH, 2), dim3(256), 0, st, (const uint16_t*)Q,
+                     (const uint16_t*)K, signs, f, S);
+  hipLaunchKernelGGL(fp8_v_amax_kernel, dim3(f.Sp / 128, BH), dim3(128), 0, st, (const uint16_t*)V, f, S);
+  hipLaunchKernelGGL(fp8_v_scale_kernel, dim3(BH), dim3(128), 0, st, f);
+  hipLaunchKernelGGL(fp8_v_quant_kernel, dim3(f.Sp / 64, BH), dim3(128), 0, st, (const uint16_t*)V, f, S);
+  prof_end(KID_FP8_QUANT, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_fp8(const Fp8Buf& f, void* O, float* LSE, int B, int H, int S, float C, uint32_t qsign,
+                          float tau, int causal, hipStream_t st) {
+  const int BH = B * H;
+  const int nqt = f.Sp / FBR;
+  prof_begin(KID_FWD_FP8, st);
+  hipLaunchKernelGGL(fwd_fp8_kernel, dim3(nqt * BH), dim3(256), 0, st, f, (uint16_t*)O, LSE, BH, S, nqt, C, qsign,
+                     tau, causal);
+  prof_end(KID_FWD_FP8, st);
+  return hipGetLastError();
+}
+
+}  // namespace attn97

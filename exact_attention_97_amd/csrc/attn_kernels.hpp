@@ -58,6 +58,27 @@ struct SplitKvLaunch {
   float* Lpart;  // [nsplit, B*H, S] fp32
 };
 
+// FP8 forward: the quantized operands and their scales in one caller-owned
+// buffer (regions in this order, each rounded up to 256 bytes); Sp is S
+// rounded up to 128, rows past S are zero.
+struct Fp8Buf {
+  int Sp;
+  uint8_t* q8;   // [B*H, Sp, 128] E4M3, transformed Q
+  uint8_t* k8;   // [B*H, Sp, 128] E4M3, transformed K
+  uint8_t* v8t;  // [B*H, 128, Sp] E4M3, V transposed, keys permuted in 64-groups
+  float* qs;     // [B*H, Sp] per-row Q scales
+  float* ks;     // [B*H, Sp / 64] per-tile K scales
+  float* vs;     // [B*H, 128] per-column V scales
+  float* vpart;  // [B*H, Sp / 128, 128] column maxima of V per 128 rows (scratch)
+  size_t offsets[7];
+};
+// Byte size of the buffer; fills *f from `base` when f is not null.
+size_t fp8_layout(int B, int H, int S, int D, void* base, Fp8Buf* f);
+hipError_t launch_fp8_quantize(const void* Q, const void* K, const void* V, const float* signs, const Fp8Buf& f,
+                               int B, int H, int S, hipStream_t st);
+hipError_t launch_fwd_fp8(const Fp8Buf& f, void* O, float* LSE, int B, int H, int S, float C, uint32_t qsign,
+                          float tau, int causal, hipStream_t st);
+
 // Kernel names used by the timing hooks.
 enum KernelId {
   KID_FWD = 0,
@@ -68,6 +89,8 @@ enum KernelId {
   KID_BWD_DQ,
   KID_FWD_SPLITKV,
   KID_SPLITKV_MERGE,
+  KID_FP8_QUANT,
+  KID_FWD_FP8,
   KID_COUNT
 };
 

@@ -122,3 +122,11 @@ SPLITKV_WORKLOADS = {
     "decode32k": RectWorkload("decode32k", B=4, H=32, Sq=1, Sk=32768, D=128, causal=True, seed=8, std=0.5),
     "prefill32k": RectWorkload("prefill32k", B=1, H=32, Sq=512, Sk=32768, D=128, causal=True, seed=9, std=0.5),
 }
+
+
+def hadamard_signs(D, seed):
+    """The random signs of the FP8 path's transform: float32 [D] of +1 / -1 (CPU),
+    from an independent seeded generator (one uniform draw per element)."""
+    g = torch.Generator().manual_seed(seed)
+    u = torch.rand((D,), generator=g, dtype=torch.float64)
+    return torch.where(u < 0.5, -1.0, 1.0).to(torch.float32)

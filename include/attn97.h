@@ -161,6 +161,62 @@ attn_status attn_fwd_splitkv(const void* Q, const void* K, const void* V, void* 
 const char* attn_strerror(attn_status s);
 
 /*
+ * FP8 forward pass with incoherent processing (D = 128 only).  Page
+ * "FlashAttention-3 и FlashAttention-4", section "Поддержка FP8 с контролем
+ * ошибок": before the rounding to FP8, Q and K pass a cheap transform that
+ * spreads outlier values over the coordinates, which lowers the FP8 error.
+ * The transform here is x -> (x * signs) H / sqrt(128), H the 128 x 128
+ * Sylvester-Hadamard matrix (orthogonal, so Q K^T is unchanged).  The
+ * format is OCP FP8 E4M3 (largest value 448, round to nearest even).
+ *
+ * Two calls: attn_fp8_quantize fills a caller-owned buffer with the
+ * quantized operands, attn_fwd_fp8 computes O and LSE from it.  A buffer
+ * can serve several attn_fwd_fp8 calls (e.g. both causal settings).
+ *
+ * Buffer: attn_fp8_buffer_bytes(B, H, S, D) bytes, 256-byte aligned, holding
+ * seven regions at the byte offsets attn_fp8_buffer_offsets writes (each
+ * rounded up to 256 bytes); Sp = S rounded up to 128, rows past S are zero:
+ *   [0] q8  uint8 [B*H, Sp, 128]  E4M3 codes of the transformed Q
+ *   [1] k8  uint8 [B*H, Sp, 128]  E4M3 codes of the transformed K
+ *   [2] v8t uint8 [B*H, 128, Sp]  E4M3 codes of V, transposed; inside each
+ *           group of 64 keys, key 32 kb + 8 r + 4 h + e (kb, h in {0,1};
+ *           r, e in 0..3) is stored at position 32 h + 16 kb + 4 r + e
+ *   [3] qs  fp32 [B*H, Sp]        one scale per Q row
+ *   [4] ks  fp32 [B*H, Sp / 64]   one scale per tile of 64 keys
+ *   [5] vs  fp32 [B*H, 128]       one scale per V column
+ *   [6] scratch (column maxima of V per 128 rows)
+ * A value x is represented as scale * e4m3(code); each scale is the
+ * group's max |x| / 448 (1 for an all-zero group).
+ */
+size_t attn_fp8_buffer_bytes(int B, int H, int S, int D);
+attn_status attn_fp8_buffer_offsets(int B, int H, int S, int D, size_t offsets[7]);
+
+/*
+ *   in : Q, K, V bf16 [B,H,S,D] (D = 128); signs: device fp32 [128] of +1 / -1
+ *        (the random signs of the transform), or NULL for no transform
+ *        (plain FP8 quantization of Q and K)
+ *   out: buf as above (its previous contents do not matter)
+ *   Errors: ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_UNSUPPORTED (D != 128),
+ *   ATTN_ERR_ALIGN (inputs not 16-byte aligned), ATTN_ERR_WORKSPACE (buf
+ *   missing, small or not 256-byte aligned), ATTN_ERR_HIP.
+ */
+attn_status attn_fp8_quantize(const void* Q, const void* K, const void* V, const float* signs, void* buf,
+                              size_t buf_bytes, int B, int H, int S, int D, void* stream);
+
+/*
+ * Forward pass from a quantized buffer: the online softmax of attn_fwd with
+ * S = scale * Q8 K8^T and O += P8 V8, P rounded to E4M3 per key tile of 64
+ * (relative to the running row max), the row sum taken over the unrounded P;
+ * O = acc / l (bf16), LSE = m + ln l (fp32, natural log).
+ *   in : buf from attn_fp8_quantize with the same B, H, S, D
+ *   out: O bf16 [B,H,S,D]; LSE fp32 [B,H,S]
+ *   opts: rescale_tau as in attn_fwd; exp_mode and bwd_mode are ignored.
+ *   Errors: as attn_fp8_quantize, plus ATTN_ERR_VALUE for a non-finite scale.
+ */
+attn_status attn_fwd_fp8(const void* buf, size_t buf_bytes, void* O, float* LSE, int B, int H, int S, int D,
+                         float scale, int causal, const attn_opts* opts, void* stream);
+
+/*
  * Diagnostic: evaluate the kernels' exp2 on n fp32 values, y[i] = 2^x[i],
  * with the same device code the forward kernel uses for mode (an
  * attn_exp_mode).  x and y are device pointers of n floats (n >= 0; n = 0
@@ -174,7 +230,8 @@ attn_status attn_exp2_eval(const float* x, float* y, long n, int mode, void* str
  * every kernel launch is bracketed by two hipEvents recorded on the launch
  * stream.  attn_prof_collect synchronises on those events and returns, for
  * the kernel named `kernel` ("fwd", "bwd_pre", "bwd_main", "bwd_dq", "bwd_dkdv",
- * "dq_convert", "fwd_splitkv", "splitkv_merge"), the number of launches and the
+ * "dq_convert", "fwd_splitkv", "splitkv_merge", "fp8_quantize" (all four
+ * kernels of attn_fp8_quantize), "fwd_fp8"), the number of launches and the
  * summed milliseconds since the
  * last reset.  Events are created on first use and kept; at most 65536
  * launches are recorded between resets (later ones are not timed).

@@ -121,30 +121,40 @@ def _scale_of(amax):
     return np.where(amax > 0, amax / E4M3_MAX, 1.0)
 
 
-def quantize_rows(x):
-    """One scale per row: codes [S, D] (uint8) and scales [S]."""
+def _codes(x, amax):
+    """E4M3 codes of x / (amax / 448), formed as x * 448 / amax: one rounding,
+    so a value exactly halfway between two codes stays exactly halfway (and
+    goes to the even code).  amax = 0 gives code 0."""
+    amax = np.asarray(amax, dtype=np.float64)
+    safe = np.where(amax > 0, amax, 1.0)
+    return quantize_e4m3(np.where(amax > 0, x * E4M3_MAX / safe, 0.0))
+
+
+def quantize_rows(x, norm: float = 1.0):
+    """One scale per row: codes [S, D] (uint8) and scales [S] of the rows x * norm."""
     x = np.asarray(x, dtype=np.float64)
-    sc = _scale_of(np.abs(x).max(axis=-1))
-    return quantize_e4m3(x / sc[:, None]), sc
+    amax = np.abs(x).max(axis=-1)
+    return _codes(x, amax[:, None]), _scale_of(amax * norm)
 
 
-def quantize_tiles(x, tile: int = TILE):
-    """One scale per tile of `tile` rows (the last tile may be shorter): codes and scales [ceil(S / tile)]."""
+def quantize_tiles(x, tile: int = TILE, norm: float = 1.0):
+    """One scale per tile of `tile` rows (the last tile may be shorter): codes and scales
+    [ceil(S / tile)] of the rows x * norm."""
     x = np.asarray(x, dtype=np.float64)
     n = x.shape[0]
     nt = (n + tile - 1) // tile
-    sc = np.array([_scale_of(np.abs(x[t * tile:(t + 1) * tile]).max()) for t in range(nt)])
+    amax = np.array([np.abs(x[t * tile:(t + 1) * tile]).max() for t in range(nt)])
     codes = np.empty(x.shape, dtype=np.uint8)
     for t in range(nt):
-        codes[t * tile:(t + 1) * tile] = quantize_e4m3(x[t * tile:(t + 1) * tile] / sc[t])
-    return codes, sc
+        codes[t * tile:(t + 1) * tile] = _codes(x[t * tile:(t + 1) * tile], amax[t])
+    return codes, _scale_of(amax * norm)
 
 
 def quantize_cols(x):
     """One scale per column: codes [S, D] and scales [D]."""
     x = np.asarray(x, dtype=np.float64)
-    sc = _scale_of(np.abs(x).max(axis=0))
-    return quantize_e4m3(x / sc[None, :]), sc
+    amax = np.abs(x).max(axis=0)
+    return _codes(x, amax[None, :]), _scale_of(amax)
 
 
 def quantize_head(q, k, v, signs=None, tile: int = TILE):
@@ -152,15 +162,26 @@ def quantize_head(q, k, v, signs=None, tile: int = TILE):
 
     Returns dict with codes (q8, k8, v8) and scales (qs [S], ks [ceil(S/tile)],
     vs [D]) and the dequantized float64 matrices (qh, kh, vh).
+
+    The codes of a transformed row y = (x * s) H / sqrt(D) are the rounding of
+    y * 448 / max|y|, in which the factor 1 / sqrt(D) cancels; they are formed
+    from (x * s) H, which is exact in float64 for bf16 inputs, so that no
+    rounding of that factor can move a value that lies exactly halfway
+    between two codes.  The scales carry the factor.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
+    norm = 1.0
     if signs is not None:
-        q = rotate(q, signs)
-        k = rotate(k, signs)
-    q8, qs = quantize_rows(q)
-    k8, ks = quantize_tiles(k, tile)
+        d = q.shape[-1]
+        h = hadamard(d)
+        s_ = np.asarray(signs, dtype=np.float64)
+        q = (q * s_) @ h
+        k = (k * s_) @ h
+        norm = 1.0 / math.sqrt(d)
+    q8, qs = quantize_rows(q, norm)
+    k8, ks = quantize_tiles(k, tile, norm)
     v8, vs = quantize_cols(v)
     kt = np.repeat(ks, tile)[: k.shape[0]]
     return {
@@ -171,26 +192,32 @@ def quantize_head(q, k, v, signs=None, tile: int = TILE):
     }
 
 
-def online_softmax_fwd(qh, kh, vh, scale: float, causal: bool, round_p=round_e4m3, tile: int = TILE):
+def online_softmax_fwd(qh, kh, vh, scale: float, causal: bool, round_p=round_e4m3, tile: int = TILE,
+                       q_rows=None):
     """Tiled online-softmax forward of one head on given (dequantized) operands.
 
     For each tile of `tile` keys: S = scale * Q K_t^T (causal: key j > query i
     is -inf), m_new = max(m, rowmax S), P~ = exp(S - m_new), acc = acc *
     exp(m - m_new) + round_p(P~) V_t, l = l * exp(m - m_new) + rowsum P~.
     Returns O = acc / l and LSE = m + ln l.  With round_p the identity this is
-    exactly the softmax attention of the operands.
+    exactly the softmax attention of the operands.  q_rows: the positions of
+    the given query rows among all Sq queries (for the causal mask), when qh
+    holds only some rows; the default is all of them in order.
     """
     qh = np.asarray(qh, dtype=np.float64)
     kh = np.asarray(kh, dtype=np.float64)
     vh = np.asarray(vh, dtype=np.float64)
-    sq, sk = qh.shape[0], kh.shape[0]
-    m = np.full(sq, -np.inf)
-    l = np.zeros(sq)
-    acc = np.zeros((sq, vh.shape[1]))
-    i = np.arange(sq)[:, None]
+    n, sk = qh.shape[0], kh.shape[0]
+    sq = n if q_rows is None else None
+    m = np.full(n, -np.inf)
+    l = np.zeros(n)
+    acc = np.zeros((n, vh.shape[1]))
+    i = (np.arange(n) if q_rows is None else np.asarray(q_rows))[:, None]
     for t0 in range(0, sk, tile):
         s = scale * (qh @ kh[t0:t0 + tile].T)
         if causal:
+            if sq is None:  # rows of a square problem
+                sq = sk
             j = np.arange(t0, min(sk, t0 + tile))[None, :]
             s = np.where(j > i + (sk - sq), -np.inf, s)
         m_new = np.maximum(m, s.max(axis=1))
@@ -206,10 +233,15 @@ def online_softmax_fwd(qh, kh, vh, scale: float, causal: bool, round_p=round_e4m
     return o, lse
 
 
-def fp8_attention_fwd(q, k, v, scale: float, causal: bool, signs=None, tile: int = TILE):
-    """FP8 forward of one head ([S, D] each): transform, quantize, online softmax with P in E4M3."""
+def fp8_attention_fwd(q, k, v, scale: float, causal: bool, signs=None, tile: int = TILE, rows=None):
+    """FP8 forward of one head ([S, D] each): transform, quantize, online softmax with P in E4M3.
+
+    rows: compute only these query rows (of a square problem); Q is quantized
+    per row, so the result is the same as those rows of the full call.
+    """
     qd = quantize_head(q, k, v, signs, tile)
-    return online_softmax_fwd(qd["qh"], qd["kh"], qd["vh"], scale, causal, round_e4m3, tile)
+    qh = qd["qh"] if rows is None else qd["qh"][np.asarray(rows)]
+    return online_softmax_fwd(qh, qd["kh"], qd["vh"], scale, causal, round_e4m3, tile, rows)
 
 
 def fp8_attention_fwd_heads(q, k, v, scale: float, causal: bool, signs=None, heads=None, tile: int = TILE):

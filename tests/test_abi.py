@@ -187,3 +187,43 @@ def test_splitkv_rejects(kw, code):
     a.update(kw)
     assert lib.attn_fwd_splitkv(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["ws"], a["wsb"], a["B"], a["H"], a["Sq"],
                                 a["Sk"], a["D"], a["scale"], a["causal"], a["splits"], None, None) == code
+
+
+def test_fp8_buffer_layout():
+    lib = L.load()
+    B, H, S, D = 2, 3, 200, 128
+    Sp, BH = 256, 6
+    r = lambda n: (n + 255) // 256 * 256
+    sizes = [r(BH * Sp * D), r(BH * Sp * D), r(BH * D * Sp), r(BH * Sp * 4), r(BH * (Sp // 64) * 4), r(BH * D * 4),
+             r(BH * (Sp // 128) * D * 4)]
+    assert lib.attn_fp8_buffer_bytes(B, H, S, D) == sum(sizes)
+    offs = (ctypes.c_size_t * 7)()
+    assert lib.attn_fp8_buffer_offsets(B, H, S, D, offs) == OK
+    assert list(offs) == [sum(sizes[:i]) for i in range(7)]
+    assert lib.attn_fp8_buffer_bytes(B, H, S, 64) == 0
+    assert lib.attn_fp8_buffer_offsets(B, H, S, 64, offs) == UNSUP
+    assert lib.attn_fp8_buffer_offsets(B, H, S, D, None) == NULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), NULL), (dict(S=0), SHAPE), (dict(D=64), UNSUP), (dict(K=P + 4), ALIGN), (dict(signs=P + 2), ALIGN),
+    (dict(buf=None), WS), (dict(bufb=1024), WS), (dict(buf=P + 16), WS),
+])
+def test_fp8_quantize_rejects(kw, code):
+    lib = L.load()
+    a = dict(Q=P, K=P, V=P, signs=None, buf=P, bufb=1 << 40, B=1, H=2, S=100, D=128)
+    a.update(kw)
+    assert lib.attn_fp8_quantize(a["Q"], a["K"], a["V"], a["signs"], a["buf"], a["bufb"], a["B"], a["H"], a["S"], a["D"],
+                                 None) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(O=None), NULL), (dict(B=0), SHAPE), (dict(D=256), UNSUP), (dict(LSE=P + 4), ALIGN),
+    (dict(scale=float("inf")), VALUE), (dict(buf=None), WS), (dict(bufb=100), WS),
+])
+def test_fwd_fp8_rejects(kw, code):
+    lib = L.load()
+    a = dict(buf=P, bufb=1 << 40, O=P, LSE=P, B=1, H=2, S=100, D=128, scale=0.1, causal=0)
+    a.update(kw)
+    assert lib.attn_fwd_fp8(a["buf"], a["bufb"], a["O"], a["LSE"], a["B"], a["H"], a["S"], a["D"], a["scale"],
+                            a["causal"], None, None) == code
