@@ -189,6 +189,61 @@ def splitkv_measure(torch, attn, dev, reps=20):
     return out
 
 
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, published
+
+
+def fp8_measure(torch, attn, dev, B, H, S, D, reps=20):
+    """FP8 forward with incoherent processing at the headline shape (outside the headline step).
+
+    Same inputs as the headline forward (Q, K with 1% x20 outliers); the
+    transform's signs are a seeded draw.  Algorithmic flops as for the bf16
+    forward (4 B H S^2 D, half causal) against the FP8 MFMA peak.  The
+    quantizer is HBM-bound: its minimal traffic reads Q, K, V (bf16) once and
+    writes the three E4M3 arrays once (scales are negligible).
+    """
+    from exact_attention_97_amd.inputs import hadamard_signs, make_qkvdo
+
+    q, k, v, _ = (t.to(dev) for t in make_qkvdo(B, H, S, D, seed=2, outlier_frac=0.01, outlier_scale=20.0))
+    sg = hadamard_signs(D, 11).to(dev)
+    buf = attn.fp8_quantize(q, k, v, sg)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    out = {"workload": f"B={B} H={H} S={S} D={D}, Q and K with 1% x20 outliers, random-sign Hadamard transform"}
+    for causal in (False, True):
+        for _ in range(3):
+            attn.attn_fwd_fp8_quantized(buf, B, H, S, D, causal=causal, out=o, lse=lse)
+        torch.cuda.synchronize()
+        attn.prof_reset()
+        attn.prof_enable(True)
+        for _ in range(reps):
+            attn.attn_fwd_fp8_quantized(buf, B, H, S, D, causal=causal, out=o, lse=lse)
+        torch.cuda.synchronize()
+        attn.prof_enable(False)
+        n, ms = attn.prof_collect("fwd_fp8")
+        ms /= max(n, 1)
+        flops = 4.0 * B * H * S * S * D * (0.5 if causal else 1.0)
+        tf = flops / (ms * 1e-3) / 1e12
+        out["fwd_causal" if causal else "fwd_noncausal"] = {
+            "ms": round(ms, 4), "tflops": round(tf, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / FP8_PEAK_TFLOPS, 4), "flops_per_launch": flops}}
+    attn.prof_reset()
+    attn.prof_enable(True)
+    for _ in range(reps):
+        attn.fp8_quantize(q, k, v, sg, buf=buf)
+    torch.cuda.synchronize()
+    attn.prof_enable(False)
+    n, ms = attn.prof_collect("fp8_quantize")
+    ms /= max(n, 1)
+    nbytes = 3.0 * B * H * S * D * 2 + 3.0 * B * H * S * D
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out["quantize"] = {"ms": round(ms, 4), "gbs": round(gbs, 1),
+                       "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                    "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_call": nbytes}}
+    del q, k, v, o, lse, buf
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -323,6 +378,7 @@ def main():
         "roofline": roofline,
         "gemm_reference": gemm_reference(torch, dev),
         "splitkv": splitkv_measure(torch, attn, dev),
+        "fp8": fp8_measure(torch, attn, dev, B, H, S, D),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(q, k, v, do)

@@ -363,18 +363,26 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8Buf f, uint16_t* __r
   wait_vm_lds<63>();
   barrier_keep_loads();
 
-  auto step = [&](auto maskc, int kt, f32x16(&scur)[2], f32x16(&snext)[2]) {
+  auto step = [&](auto maskc, int kt, float ks_t, f32x16(&scur)[2], f32x16(&snext)[2]) {
     constexpr bool MASK = decltype(maskc)::value;
-    const float ct = cq * ksh[kt];  // score factor of this tile (log2 units)
+    // distinct code at the top of each copy: keeps the compiler from hoisting
+    // the two copies' common reads out of the masked / unmasked branch
+    tile_marker<MASK>();
+    const float ct = cq * ks_t;  // score factor of this tile (log2 units)
+    // Region 1 (raised wave priority): the next tile's four score MFMAs
+    // interleaved with this tile's softmax.  Back to back, each MFMA would
+    // hold the wavefront until the previous one leaves the matrix pipe.
+    __builtin_amdgcn_s_setprio(1);
+    scores(Kb[(kt + 1) & 1], snext);
     const float mx = fp8_tile_max<MASK>(scur, kt * FBC, lim, hh);
     const float mxs = (mx == kNegInf) ? kNegInf : mx * ct;
     const float m_new = __builtin_fmaxf(m_run, mxs);
     const bool grow = __any((m_new - m_run) > tau);
-    const float alpha = (grow && m_new != kNegInf) ? exp2_native(m_run - m_new) : 1.0f;
+    // no branch here: exp2(0) = 1 when the max does not move (a branch would
+    // split the region and stop the scheduler from interleaving it)
+    const float alpha = exp2_native((grow && m_new != kNegInf) ? (m_run - m_new) : 0.0f);
     m_run = grow ? m_new : m_run;
     l_part *= alpha;
-    __builtin_amdgcn_s_setprio(1);
-    scores(Kb[(kt + 1) & 1], snext);
     // P = exp2(S ct - m) to E4M3: byte 16 kb + r of the operand is register r
     // of block kb, the key order of V^T in LDS
     i32x8 pf;
@@ -395,6 +403,20 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8Buf f, uint16_t* __r
         pf[4 * kb + w4] = (int)pack_e4m3x4(p[0], p[1], p[2], p[3]);
       }
     }
+    // the K fragment reads first, the tile max under their latency, then
+    // each MFMA followed by a share of the softmax (VALU and exponentials)
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x402, 40, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 26, 0);
+    }
+    // keep P and the row sum above the (rare) rescale branch: otherwise the
+    // compiler sinks them next to the PV products, out of this schedule
+#pragma unroll
+    for (int w = 0; w < 8; ++w) asm volatile("" ::"v"(pf[w]));
+    asm volatile("" ::"v"(l_part));
     __builtin_amdgcn_s_setprio(0);
     if (grow) {
 #pragma unroll
@@ -407,13 +429,14 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8Buf f, uint16_t* __r
   };
 
   auto iteration = [&](int kt, f32x16(&scur)[2], f32x16(&snext)[2]) {
+    const float ks_t = ksh[kt];  // this tile's K scale, loaded ahead of the tile loads
     issue(kt);
     __builtin_amdgcn_sched_barrier(0);
     if (kt < nkt_w) {
       if (kt < nfull)
-        step(std::false_type{}, kt, scur, snext);
+        step(std::false_type{}, kt, ks_t, scur, snext);
       else
-        step(std::true_type{}, kt, scur, snext);
+        step(std::true_type{}, kt, ks_t, scur, snext);
     }
     wait_vm_lds<0>();
     barrier_keep_loads();
