@@ -150,11 +150,13 @@ __global__ __launch_bounds__(256) void fp8_qk_quant_kernel(const uint16_t* __res
     amax = __builtin_fmax(__builtin_fmax(wave_max[0], wave_max[1]), __builtin_fmax(wave_max[2], wave_max[3]));
   }
   // the transformed row is x * norm; its scale is max|x * norm| / 448 and its
-  // codes are E4M3(x * norm / scale) = E4M3(x * 448 / max|x|), formed with one
-  // correctly rounded division, so a value exactly halfway between two codes
-  // stays halfway (and goes to the even code)
+  // codes are E4M3(x * norm / scale) = E4M3(x * 448 / max|x|).  The quotient
+  // is formed in float64 as x * (448 / max|x|) and then rounded to float32:
+  // a quotient exactly halfway between two codes has at most 5 significant
+  // bits, and the float64 error (below 2^-52 relative) cannot move it off
+  // that float32 value, so it stays halfway (and goes to the even code)
   const float sc = amax > 0.0 ? (float)(amax * norm / (double)kE4M3Max) : 1.0f;
-  const double den = amax > 0.0 ? amax : 1.0;
+  const double r = amax > 0.0 ? (double)kE4M3Max / amax : 0.0;
 
   uint8_t* dst = (which ? f.k8 : f.q8) + ((size_t)bh * Sp + row) * FD + 32 * qd;
 #pragma unroll
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(256) void fp8_qk_quant_kernel(const uint16_t* __res
       const int d = 16 * c + 4 * e;
       float y[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) y[u] = clamp448((float)(x[d + u] * (double)kE4M3Max / den));
+      for (int u = 0; u < 4; ++u) y[u] = clamp448((float)(x[d + u] * r));
       w[e] = pack_e4m3x4(y[0], y[1], y[2], y[3]);
     }
     *reinterpret_cast<u32x4*>(dst + 16 * c) = w;
@@ -206,7 +208,9 @@ __global__ __launch_bounds__(128) void fp8_v_quant_kernel(const uint16_t* __rest
   const int k0 = tile * FBC;
   const uint16_t* src = V + (size_t)bh * S * FD + d;
   const float m = f.vpart[(size_t)bh * (f.Sp / 128) * FD + d];  // column max (see fp8_v_scale_kernel)
-  const float den = m > 0.0f ? m : 1.0f;
+  // v * 448 / m as in the Q / K quantizer: float64 product with the
+  // reciprocal, then float32 (exact halfway cases stay exact)
+  const double r = m > 0.0f ? (double)kE4M3Max / (double)m : 0.0;
   uint32_t w[16];
 #pragma unroll
   for (int g = 0; g < 16; ++g) {  // keys 4 g .. 4 g + 3 of the tile
@@ -214,7 +218,7 @@ __global__ __launch_bounds__(128) void fp8_v_quant_kernel(const uint16_t* __rest
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int key = k0 + 4 * g + e;
-      v[e] = key < S ? clamp448(bf16_lo((uint32_t)src[(size_t)key * FD]) * kE4M3Max / den) : 0.0f;
+      v[e] = key < S ? clamp448((float)((double)bf16_lo((uint32_t)src[(size_t)key * FD]) * r)) : 0.0f;
     }
     const int h = g & 1, kb = g >> 3, r4 = (g >> 1) & 3;
     w[8 * h + 4 * kb + r4] = pack_e4m3x4(v[0], v[1], v[2], v[3]);

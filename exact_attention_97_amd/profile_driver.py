@@ -23,7 +23,7 @@ from .inputs import make_qkvdo
 
 def main() -> None:
     ap = argparse.ArgumentParser()
-    ap.add_argument("--passes", default="fwd,bwd", help="comma list of fwd, bwd")
+    ap.add_argument("--passes", default="fwd,bwd", help="comma list of fwd, bwd, fp8 (quantize + FP8 forward)")
     ap.add_argument("--causal", type=int, default=0)
     ap.add_argument("--B", type=int, default=2)
     ap.add_argument("--H", type=int, default=16)
@@ -57,6 +57,14 @@ def main() -> None:
         if p == "fwd":
             for _ in range(a.iters):
                 L.attn_fwd(q, k, v, scale=scale, causal=causal, out=o, lse=lse)
+        elif p == "fp8":
+            from .inputs import hadamard_signs
+
+            sg = hadamard_signs(a.D, 11).to(dev)
+            buf = L.fp8_quantize(q, k, v, sg)
+            for _ in range(a.iters):
+                L.fp8_quantize(q, k, v, sg, buf=buf)
+                L.attn_fwd_fp8_quantized(buf, a.B, a.H, a.S, a.D, scale=scale, causal=causal, out=o, lse=lse)
         elif p == "bwd":
             ws = torch.empty(L.bwd_workspace_bytes(a.B, a.H, a.S, a.D, causal, bwd_mode=a.bwd_mode),
                              dtype=torch.uint8, device=dev)
