@@ -24,5 +24,6 @@ from ._lib import (  # noqa: F401
     prof_collect,
     prof_enable,
     prof_reset,
+    set_variant,
     version,
 )

@@ -29,6 +29,7 @@ EXPORTS = (
     "attn_exp2_eval", "attn_prof_enable", "attn_prof_reset", "attn_prof_collect", "attn_version",
     "attn_fwd_splitkv_workspace_bytes", "attn_fwd_splitkv",
     "attn_fp8_buffer_bytes", "attn_fp8_buffer_offsets", "attn_fp8_quantize", "attn_fwd_fp8",
+    "attn_set_variant",
 )
 FP8_REGIONS = ("q8", "k8", "v8t", "qs", "ks", "vs", "scratch")
 
@@ -90,6 +91,8 @@ def load():
     lib.attn_fp8_quantize.restype = i
     lib.attn_fwd_fp8.argtypes = [vp, sz, vp, vp, i, i, i, i, f, i, optp, vp]
     lib.attn_fwd_fp8.restype = i
+    lib.attn_set_variant.argtypes = [ctypes.c_char_p, i]
+    lib.attn_set_variant.restype = i
     _lib = lib
     return lib
 
@@ -288,6 +291,11 @@ def exp2_eval(x, mode="native", stream=None):
     m = EXP_MODES[mode] if isinstance(mode, str) else int(mode)
     _check("attn_exp2_eval", load().attn_exp2_eval(x.data_ptr(), y.data_ptr(), x.numel(), m, _stream_ptr(stream)))
     return y
+
+
+def set_variant(kernel, variant):
+    """Select a measured kernel variant ("fwd", "bwd_dkdv", "bwd_dq"); -1 = back to the environment's choice."""
+    _check("attn_set_variant", load().attn_set_variant(kernel.encode(), int(variant)))
 
 
 def prof_enable(on=True):

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+#include <stdlib.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -48,9 +49,25 @@ std::vector<ProfRec> g_prof_pool;  // events, created on first use and reused
 size_t g_prof_used = 0;
 size_t g_prof_open = (size_t)-1;
 
+// kernel variant overrides (-1: not set, use the environment)
+int g_variant[attn97::VAR_COUNT] = {-1, -1, -1};
+int g_variant_env[attn97::VAR_COUNT] = {-1, -1, -1};
+
 }  // namespace
 
 namespace attn97 {
+
+int kernel_variant(int slot) {
+  if (slot < 0 || slot >= VAR_COUNT) return 0;
+  if (g_variant[slot] >= 0) return g_variant[slot];
+  if (g_variant_env[slot] < 0) {
+    static const char* names[VAR_COUNT] = {"ATTN97_FWD_VARIANT", "ATTN97_DKDV_VARIANT", "ATTN97_DQ_VARIANT"};
+    const char* e = getenv(names[slot]);
+    const int v = e ? atoi(e) : 0;
+    g_variant_env[slot] = v < 0 ? 0 : v;
+  }
+  return g_variant_env[slot];
+}
 
 void prof_begin(int kid, hipStream_t st) {
   g_prof_open = (size_t)-1;
@@ -340,6 +357,19 @@ attn_status attn_exp2_eval(const float* x, float* y, long n, int mode, void* str
   if (misaligned(x, 4) || misaligned(y, 4)) return ATTN_ERR_ALIGN;
   hipError_t e = attn97::launch_exp2_eval(x, y, n, mode, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_set_variant(const char* kernel, int variant) {
+  if (!kernel) return ATTN_ERR_NULL;
+  static const char* names[attn97::VAR_COUNT] = {"fwd", "bwd_dkdv", "bwd_dq"};
+  static const int count[attn97::VAR_COUNT] = {5, 6, 3};  // variants 0 .. count-1
+  for (int i = 0; i < attn97::VAR_COUNT; ++i) {
+    if (strcmp(kernel, names[i]) != 0) continue;
+    if (variant < -1 || variant >= count[i]) return ATTN_ERR_VALUE;
+    g_variant[i] = variant;
+    return ATTN_OK;
+  }
+  return ATTN_ERR_UNSUPPORTED;
 }
 
 attn_status attn_prof_enable(int on) {

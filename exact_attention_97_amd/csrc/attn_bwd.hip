@@ -896,16 +896,9 @@ static hipError_t launch_pre_t(const BwdArgs& a, hipStream_t st) {
 }
 
 // Tile-configuration variants of the split-mode dK/dV kernel, selectable
-// for tuning through the environment variable ATTN97_DKDV_VARIANT
-// (0 = default).
-static int dkdv_variant() {
-  static int v = -1;
-  if (v < 0) {
-    const char* e = getenv("ATTN97_DKDV_VARIANT");
-    v = e ? atoi(e) : 0;
-  }
-  return v;
-}
+// for measurement (attn_set_variant("bwd_dkdv", v) or ATTN97_DKDV_VARIANT;
+// 0 = default).
+static int dkdv_variant() { return kernel_variant(VAR_DKDV); }
 
 template <int D, bool CAUSAL>
 static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {

@@ -315,17 +315,12 @@ static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Tile-configuration variants of the D = 128 kernel, selectable for tuning
-// through the environment variable ATTN97_DQ_VARIANT (0 = default: 64-key
-// tiles in the pipelined step, two workgroups of four wavefronts per CU).
-static int dq_variant() {
-  static int v = -1;
-  if (v < 0) {
-    const char* e = getenv("ATTN97_DQ_VARIANT");
-    v = e ? atoi(e) : 0;
-  }
-  return v;
-}
+// Tile-configuration variants of the D = 128 kernel, selectable for
+// measurement (attn_set_variant("bwd_dq", v) or ATTN97_DQ_VARIANT; 0 =
+// default: 64-key tiles in the pipelined step, two workgroups of four
+// wavefronts per CU).  Variant 2 is the cooperative big tile: one workgroup
+// of eight wavefronts (256 queries) shares each K / V tile in LDS.
+static int dq_variant() { return kernel_variant(VAR_DQ); }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
   switch (a.D) {

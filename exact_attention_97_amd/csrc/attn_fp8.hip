@@ -11,7 +11,7 @@
 //  * quantize: Q and K rows transformed (a 128-point fast Walsh-Hadamard
 //    transform in float64 registers, one row per four lanes) and rounded to E4M3 with one
 //    scale per Q row and one per 64-key K tile; V rounded with one scale per
-//    column (two small kernels find the column maxima first) and stored
+//    column (a column-maximum kernel runs first) and stored
 //    transposed, keys permuted inside each 64-key group so that the PV
 //    operand of a lane is 32 contiguous bytes.
 //  * forward: the online-softmax kernel of the bf16 path with both products
@@ -89,6 +89,8 @@ __global__ __launch_bounds__(256) void fp8_qk_quant_kernel(const uint16_t* __res
   const int row = blockIdx.x * 64 + 16 * wave + (lane & 15);
   const int Sp = f.Sp;
   const uint16_t* src = (which ? K : Q) + (size_t)bh * S * FD;
+  // the V column maxima start at zero (fp8_v_amax_kernel runs after this kernel)
+  if (blockIdx.x == 0 && which == 0 && tid < FD) f.vpart[(size_t)bh * FD + tid] = 0.0f;
 
   double x[32];
   if (row < S) {
@@ -179,54 +181,80 @@ __global__ __launch_bounds__(256) void fp8_qk_quant_kernel(const uint16_t* __res
   }
 }
 
-// Column maxima of V over 128-row chunks.  Grid (Sp / 128, B*H), 128 threads (d).
-__global__ __launch_bounds__(128) void fp8_v_amax_kernel(const uint16_t* __restrict__ V, Fp8Buf f, int S) {
-  const int chunk = blockIdx.x, bh = blockIdx.y, d = threadIdx.x;
-  const uint16_t* src = V + (size_t)bh * S * FD + d;
-  const int r0 = chunk * 128, r1 = min(S, r0 + 128);
-  float m = 0.0f;
-  for (int r = r0; r < r1; ++r) m = __builtin_fmaxf(m, __builtin_fabsf(bf16_lo((uint32_t)src[(size_t)r * FD])));
-  f.vpart[((size_t)bh * (f.Sp / 128) + chunk) * FD + d] = m;
-}
-
-// V column scales from the chunk maxima.  Grid B*H, 128 threads (d).  The
-// column maximum itself is left in the first chunk slot for the quantizer.
-__global__ __launch_bounds__(128) void fp8_v_scale_kernel(Fp8Buf f) {
-  const int bh = blockIdx.x, d = threadIdx.x;
-  const int nch = f.Sp / 128;
-  float m = 0.0f;
-  for (int c = 0; c < nch; ++c) m = __builtin_fmaxf(m, f.vpart[((size_t)bh * nch + c) * FD + d]);
-  f.vs[(size_t)bh * FD + d] = m > 0.0f ? m / kE4M3Max : 1.0f;
-  f.vpart[(size_t)bh * nch * FD + d] = m;
+// Column maxima of V.  Grid (Sp / 128, B*H), 256 threads: thread t reads
+// the 16-byte chunk t % 16 (columns 8 (t % 16) .. + 7) of rows t / 16 + 16 i
+// of the 128-row chunk; the 16 row groups reduce through LDS, and each
+// column's maximum goes into the scratch region with an integer atomicMax
+// (non-negative floats order like their bit patterns).  fp8_qk_quant_kernel,
+// launched before on the same stream, zeroed those maxima.
+__global__ __launch_bounds__(256) void fp8_v_amax_kernel(const uint16_t* __restrict__ V, Fp8Buf f, int S) {
+  __shared__ float part[16][FD];
+  const int chunk = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int c = t & 15, rg = t >> 4;
+  const uint16_t* src = V + (size_t)bh * S * FD + 8 * c;
+  float m[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m[j] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = chunk * 128 + rg + 16 * i;
+    if (r < S) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(src + (size_t)r * FD);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        m[2 * e] = __builtin_fmaxf(m[2 * e], __builtin_fabsf(bf16_lo(w[e])));
+        m[2 * e + 1] = __builtin_fmaxf(m[2 * e + 1], __builtin_fabsf(bf16_hi(w[e])));
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) part[rg][8 * c + j] = m[j];
+  __syncthreads();
+  if (t < FD) {
+    float mm = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) mm = __builtin_fmaxf(mm, part[g][t]);
+    atomicMax(reinterpret_cast<unsigned int*>(f.vpart) + (size_t)bh * FD + t, __builtin_bit_cast(unsigned int, mm));
+  }
 }
 
 // V to E4M3, transposed: row d of head bh holds the Sp keys, and inside each
 // 64-key group key 32 kb + 8 r4 + 4 h + e sits at byte 32 h + 16 kb + 4 r4 + e
-// (h, kb in {0, 1}; r4, e in 0..3).  Grid (Sp / 64, B*H), 128 threads (d).
-__global__ __launch_bounds__(128) void fp8_v_quant_kernel(const uint16_t* __restrict__ V, Fp8Buf f, int S) {
-  const int tile = blockIdx.x, bh = blockIdx.y, d = threadIdx.x;
+// (h, kb in {0, 1}; r4, e in 0..3).  Grid (Sp / 64, B*H), 256 threads: the
+// 64 x 128 tile comes in with coalesced 16-byte loads through LDS; thread
+// (d, kb) then rounds keys 32 kb .. 32 kb + 31 of column d.  The first tile's
+// workgroup also writes the column scales.
+__global__ __launch_bounds__(256) void fp8_v_quant_kernel(const uint16_t* __restrict__ V, Fp8Buf f, int S) {
+  __shared__ __attribute__((aligned(16))) uint16_t tv[FBC][FD];
+  const int tile = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   const int k0 = tile * FBC;
-  const uint16_t* src = V + (size_t)bh * S * FD + d;
-  const float m = f.vpart[(size_t)bh * (f.Sp / 128) * FD + d];  // column max (see fp8_v_scale_kernel)
+  const uint16_t* src = V + (size_t)bh * S * FD;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = t + 256 * i, row = idx >> 4, ch = idx & 15;
+    const int key = k0 + row;
+    const u32x4 w = key < S ? *reinterpret_cast<const u32x4*>(src + (size_t)key * FD + 8 * ch) : u32x4{0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(&tv[row][8 * ch]) = w;
+  }
+  __syncthreads();
+  const int d = t & 127, kb = t >> 7;
+  const float m = __builtin_bit_cast(float, reinterpret_cast<const unsigned int*>(f.vpart)[(size_t)bh * FD + d]);
+  if (tile == 0 && kb == 0) f.vs[(size_t)bh * FD + d] = m > 0.0f ? m / kE4M3Max : 1.0f;
   // v * 448 / m as in the Q / K quantizer: float64 product with the
   // reciprocal, then float32 (exact halfway cases stay exact)
   const double r = m > 0.0f ? (double)kE4M3Max / (double)m : 0.0;
-  uint32_t w[16];
+  u32x4 w[2];  // [h]: words r4 = 0..3
 #pragma unroll
-  for (int g = 0; g < 16; ++g) {  // keys 4 g .. 4 g + 3 of the tile
+  for (int g8 = 0; g8 < 8; ++g8) {  // key group g = 8 kb + g8: keys 4 g .. 4 g + 3
+    const int h = g8 & 1, r4 = g8 >> 1, key0 = 32 * kb + 4 * g8;
     float v[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = k0 + 4 * g + e;
-      v[e] = key < S ? clamp448((float)((double)bf16_lo((uint32_t)src[(size_t)key * FD]) * r)) : 0.0f;
-    }
-    const int h = g & 1, kb = g >> 3, r4 = (g >> 1) & 3;
-    w[8 * h + 4 * kb + r4] = pack_e4m3x4(v[0], v[1], v[2], v[3]);
+    for (int e = 0; e < 4; ++e) v[e] = clamp448((float)((double)bf16_lo((uint32_t)tv[key0 + e][d]) * r));
+    w[h][r4] = pack_e4m3x4(v[0], v[1], v[2], v[3]);
   }
   uint8_t* dst = f.v8t + ((size_t)bh * FD + d) * f.Sp + k0;
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-    *reinterpret_cast<u32x4*>(dst + 16 * c) = u32x4{w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]};
+  *reinterpret_cast<u32x4*>(dst + 16 * kb) = w[0];
+  *reinterpret_cast<u32x4*>(dst + 32 + 16 * kb) = w[1];
 }
 
 // ---------------------------------------------------------------------------
@@ -510,9 +538,8 @@ hipError_t launch_fp8_quantize(const void* Q, const void* K, const void* V, cons
   prof_begin(KID_FP8_QUANT, st);
   hipLaunchKernelGGL(fp8_qk_quant_kernel, dim3(f.Sp / 64, BH, 2), dim3(256), 0, st, (const uint16_t*)Q,
                      (const uint16_t*)K, signs, f, S);
-  hipLaunchKernelGGL(fp8_v_amax_kernel, dim3(f.Sp / 128, BH), dim3(128), 0, st, (const uint16_t*)V, f, S);
-  hipLaunchKernelGGL(fp8_v_scale_kernel, dim3(BH), dim3(128), 0, st, f);
-  hipLaunchKernelGGL(fp8_v_quant_kernel, dim3(f.Sp / 64, BH), dim3(128), 0, st, (const uint16_t*)V, f, S);
+  hipLaunchKernelGGL(fp8_v_amax_kernel, dim3(f.Sp / 128, BH), dim3(256), 0, st, (const uint16_t*)V, f, S);
+  hipLaunchKernelGGL(fp8_v_quant_kernel, dim3(f.Sp / 64, BH), dim3(256), 0, st, (const uint16_t*)V, f, S);
   prof_end(KID_FP8_QUANT, st);
   return hipGetLastError();
 }

@@ -495,16 +495,12 @@ static hipError_t launch_fwd_e(const FwdArgs& a, hipStream_t st) {
   }
 }
 
-// Tile-configuration variants of the D = 128 kernel, selectable for tuning
-// through the environment variable ATTN97_FWD_VARIANT (0 = default).
-static int fwd_variant() {
-  static int v = -1;
-  if (v < 0) {
-    const char* e = getenv("ATTN97_FWD_VARIANT");
-    v = e ? atoi(e) : 0;
-  }
-  return v;
-}
+// Tile-configuration variants of the D = 128 kernel, selectable for
+// measurement (attn_set_variant("fwd", v) or ATTN97_FWD_VARIANT; 0 = default).
+// The default and variant 1 are the cooperative big tile: eight wavefronts
+// (256 queries) share each K / V tile in LDS, half the tile loads per query;
+// variant 3 is the four-wavefront tile of the split-KV kernel.
+static int fwd_variant() { return kernel_variant(VAR_FWD); }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   switch (a.D) {
@@ -513,9 +509,12 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
       switch (fwd_variant()) {
         case 1: return launch_fwd_e<FwdCfg<128, 64, 8, 3>>(a, st);
         case 2: return launch_fwd_e<FwdCfg<128, 32, 4, 3>>(a, st);
-        case 3: return launch_fwd_e<FwdCfg<128, 64, 8, 2>>(a, st);
+        case 3: return launch_fwd_e<FwdDefault<128>::type>(a, st);  // four wavefronts (the split-KV tile)
         case 4: return launch_fwd_e<FwdCfg<128, 64, 4, 3>>(a, st);
-        default: return launch_fwd_e<FwdDefault<128>::type>(a, st);
+        // default: the cooperative tile, eight wavefronts (256 queries) per
+        // workgroup sharing each K / V tile (0-2 % faster than four at the
+        // headline shape; split-KV keeps four, which suits few query rows)
+        default: return launch_fwd_e<FwdCfg<128, 64, 8, 2>>(a, st);
       }
     case 256: return launch_fwd_e<FwdDefault<256>::type>(a, st);
     default: return hipErrorInvalidValue;

@@ -69,7 +69,7 @@ struct Fp8Buf {
   float* qs;     // [B*H, Sp] per-row Q scales
   float* ks;     // [B*H, Sp / 64] per-tile K scales
   float* vs;     // [B*H, 128] per-column V scales
-  float* vpart;  // [B*H, Sp / 128, 128] column maxima of V per 128 rows (scratch)
+  float* vpart;  // scratch; its first B*H*128 floats hold V's column maxima
   size_t offsets[7];
 };
 // Byte size of the buffer; fills *f from `base` when f is not null.
@@ -93,6 +93,12 @@ enum KernelId {
   KID_FWD_FP8,
   KID_COUNT
 };
+
+// Kernel variants kept for measurement (0 = the default kernel).  The
+// choice comes from attn_set_variant, else from the environment variables
+// ATTN97_FWD_VARIANT, ATTN97_DKDV_VARIANT, ATTN97_DQ_VARIANT (read once).
+enum VariantSlot { VAR_FWD = 0, VAR_DKDV, VAR_DQ, VAR_COUNT };
+int kernel_variant(int slot);
 
 // Called by the launchers around each kernel launch (no-ops unless timing is on).
 void prof_begin(int kid, hipStream_t st);

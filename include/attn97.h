@@ -184,7 +184,7 @@ const char* attn_strerror(attn_status s);
  *   [3] qs  fp32 [B*H, Sp]        one scale per Q row
  *   [4] ks  fp32 [B*H, Sp / 64]   one scale per tile of 64 keys
  *   [5] vs  fp32 [B*H, 128]       one scale per V column
- *   [6] scratch (column maxima of V per 128 rows)
+ *   [6] scratch (V's column maxima)
  * A value x is represented as scale * e4m3(code); each scale is the
  * group's max |x| / 448 (1 for an all-zero group).
  */
@@ -226,11 +226,24 @@ attn_status attn_fwd_fp8(const void* buf, size_t buf_bytes, void* O, float* LSE,
 attn_status attn_exp2_eval(const float* x, float* y, long n, int mode, void* stream);
 
 /*
+ * Diagnostic: select a kernel variant kept for measurement (tile shapes,
+ * wavefronts per workgroup, load schedules), for subsequent calls in this
+ * process.  kernel: "fwd" (D = 128 forward: 0 default, 1..4), "bwd_dkdv"
+ * (D = 128 split-mode dK/dV: 0 default, 1..5), "bwd_dq" (D = 128 dQ: 0
+ * default, 1..2); variant -1 returns to the choice of the environment
+ * variables ATTN97_FWD_VARIANT / ATTN97_DKDV_VARIANT / ATTN97_DQ_VARIANT
+ * (default 0).  Every variant computes the same result.  Not thread-safe.
+ * Errors: ATTN_ERR_NULL, ATTN_ERR_UNSUPPORTED (unknown kernel name),
+ * ATTN_ERR_VALUE (variant out of range).
+ */
+attn_status attn_set_variant(const char* kernel, int variant);
+
+/*
  * Timing of the library's own kernels, for measurement tools.  While enabled,
  * every kernel launch is bracketed by two hipEvents recorded on the launch
  * stream.  attn_prof_collect synchronises on those events and returns, for
  * the kernel named `kernel` ("fwd", "bwd_pre", "bwd_main", "bwd_dq", "bwd_dkdv",
- * "dq_convert", "fwd_splitkv", "splitkv_merge", "fp8_quantize" (all four
+ * "dq_convert", "fwd_splitkv", "splitkv_merge", "fp8_quantize" (all three
  * kernels of attn_fp8_quantize), "fwd_fp8"), the number of launches and the
  * summed milliseconds since the
  * last reset.  Events are created on first use and kept; at most 65536

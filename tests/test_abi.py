@@ -227,3 +227,17 @@ def test_fwd_fp8_rejects(kw, code):
     a.update(kw)
     assert lib.attn_fwd_fp8(a["buf"], a["bufb"], a["O"], a["LSE"], a["B"], a["H"], a["S"], a["D"], a["scale"],
                             a["causal"], None, None) == code
+
+
+def test_set_variant():
+    lib = L.load()
+    assert lib.attn_set_variant(b"fwd", 3) == OK
+    assert lib.attn_set_variant(b"fwd", -1) == OK
+    assert lib.attn_set_variant(b"bwd_dq", 2) == OK
+    assert lib.attn_set_variant(b"bwd_dq", 3) == VALUE
+    assert lib.attn_set_variant(b"bwd_dkdv", 6) == VALUE
+    assert lib.attn_set_variant(b"bwd_dkdv", -2) == VALUE
+    assert lib.attn_set_variant(b"nope", 0) == UNSUP
+    assert lib.attn_set_variant(None, 0) == NULL
+    for k in (b"fwd", b"bwd_dq", b"bwd_dkdv"):
+        assert lib.attn_set_variant(k, -1) == OK

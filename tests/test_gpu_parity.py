@@ -382,3 +382,36 @@ def test_splitkv_workload_full_size(name):
     got_l = np.array([ln[b, h, i] for b, h, i in rows])
     _assert_close("O rows", got_o, ro)
     _assert_lse(got_l, rl)
+
+
+# ----------------------------------------------------------------------------
+# kernel variants kept for measurement (tile shapes, wavefronts per workgroup,
+# load schedules; fwd 1 / 3 and dQ 2 are the eight-wavefront cooperative
+# tiles): each against the float64 oracle, ragged length, both causal settings
+# ----------------------------------------------------------------------------
+
+VARIANTS = [("fwd", v) for v in range(1, 5)] + [("bwd_dkdv", v) for v in range(1, 6)] + \
+           [("bwd_dq", v) for v in range(1, 3)]
+
+
+@pytest.mark.parametrize("kernel,variant", VARIANTS)
+def test_kernel_variants_match_oracle(kernel, variant):
+    print(f"[variant] {kernel} {variant}", flush=True)
+    q, k, v, do = make_qkvdo(1, 2, 333, 128, seed=40 + variant)
+    scale = 1.0 / math.sqrt(128)
+    qg, kg, vg, dog = _gpu(q, k, v, do)
+    L.set_variant(kernel, variant)
+    try:
+        for causal in (False, True):
+            o, lse = L.attn_fwd(qg, kg, vg, scale=scale, causal=causal)
+            ro, rl = oracle.attention_fwd(q, k, v, scale, causal)
+            _assert_close("O", _np(o), ro)
+            _assert_lse(_np(lse), rl)
+            if kernel != "fwd":
+                dq, dk, dv = L.attn_bwd(qg, kg, vg, o, dog, lse, scale=scale, causal=causal, bwd_mode="split")
+                rdq, rdk, rdv = oracle.attention_bwd(q, k, v, do, scale, causal)
+                _assert_close("dQ", _np(dq), rdq)
+                _assert_close("dK", _np(dk), rdk)
+                _assert_close("dV", _np(dv), rdv)
+    finally:
+        L.set_variant(kernel, -1)
