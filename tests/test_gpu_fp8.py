@@ -224,3 +224,44 @@ def test_fwd_fp8_headline_sampled_rows(causal):
               f"(instruction slack up to {ls.max():.1e})", flush=True)
         assert np.all(d.max(axis=1) <= O_MAX + os_) and d.mean() <= O_MEAN
         assert np.all(dl <= LSE_MAX + ls)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3])
+def test_fwd_fp8_unusual_scale(scale):
+    """A negative scale flips the sign of every Q code; scale 0 gives uniform attention."""
+    import torch
+
+    B, H, S, D = 1, 2, 300, 128
+    print(f"[fp8 scale] {scale}", flush=True)
+    q, k, v, _ = make_qkvdo(B, H, S, D, seed=35)
+    sg = _signs(D)
+    for causal in (False, True):
+        o, lse = L.attn_fwd_fp8(q.cuda(), k.cuda(), v.cuda(), sg.cuda(), scale=scale, causal=causal, rescale_tau=0.0)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = F.fp8_attention_fwd_heads(_np(q), _np(k), _np(v), scale, causal, sg.numpy())
+        d = np.abs(_np(o).reshape(B * H, S, D) - o_ref)
+        dl = np.abs(_np(lse).reshape(B * H, S) - lse_ref)
+        qn, kn, vn = _np(q).reshape(B * H, S, D), _np(k).reshape(B * H, S, D), _np(v).reshape(B * H, S, D)
+        slack = [_mfma_slack(qn[n], kn[n], vn[n], abs(scale), sg.numpy()) for n in range(B * H)]
+        ls = np.stack([a for a, _ in slack])
+        os_ = np.stack([b for _, b in slack])
+        print(f"    causal={causal}: O max-abs {d.max():.3e} mean-abs {d.mean():.3e}; LSE {dl.max():.3e}", flush=True)
+        assert np.all(d.max(axis=2) <= O_MAX + os_) and d.mean() <= O_MEAN
+        assert np.all(dl <= LSE_MAX + ls)
+
+
+def test_fwd_fp8_deterministic():
+    import torch
+
+    q, k, v, _ = make_qkvdo(2, 2, 700, 128, seed=36)
+    qg, kg, vg, sg = q.cuda(), k.cuda(), v.cuda(), _signs(128).cuda()
+    b1 = L.fp8_quantize(qg, kg, vg, sg)
+    b2 = L.fp8_quantize(qg, kg, vg, sg)
+    torch.cuda.synchronize()
+    v1, v2 = L.fp8_buffer_views(b1, 2, 2, 700, 128), L.fp8_buffer_views(b2, 2, 2, 700, 128)
+    for name in v1:
+        assert bool((v1[name] == v2[name]).all()), f"quantizer region {name} not repeatable"
+    for causal in (False, True):
+        o1, l1 = L.attn_fwd_fp8_quantized(b1, 2, 2, 700, 128, causal=causal)
+        o2, l2 = L.attn_fwd_fp8_quantized(b1, 2, 2, 700, 128, causal=causal)
+        assert bool((o1 == o2).all()) and bool((l1 == l2).all()), "FP8 forward not bitwise repeatable"
