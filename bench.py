@@ -255,7 +255,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the attention heads shard across GPUs with no communication, so N GPUs would run N "
               "independent copies of this single-GPU workload)", file=sys.stderr)
         sys.exit(2)
