@@ -431,6 +431,135 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
 }
 
 // ---------------------------------------------------------------------------
+// Split-KV decoding: one query row per head (Sq = 1), where the MFMA tiles of
+// fwd_kernel would compute 31 padding rows of every 32 and the work is
+// reading K and V.  Workgroup (split, head), four wavefronts; lane
+// (g, c) holds the 16-byte column chunk c (elements 8 c .. 8 c + 7) of key
+// slot g, so D / 8 lanes cover one key row and a wavefront reads
+// 64 * 8 / D consecutive keys per step, eight steps of K and V loads in flight
+// before any arithmetic.  Scores are fp32 dot products reduced across the
+// row's lanes; the running max and sum are per wavefront (the accumulator is
+// rescaled once per eight steps, exactly, with no threshold); the four
+// wavefronts combine through LDS into the split's normalised output and
+// log-sum-exp, the format the merge kernel reads.  With one query row and
+// the queries read as the last positions, every key is visible, causal or
+// not.  Exponentials are native.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void splitkv_decode_kernel(const uint16_t* __restrict__ Q,
+                                                             const uint16_t* __restrict__ K,
+                                                             const uint16_t* __restrict__ V, int BH, int Sk,
+                                                             int kchunk, float C, uint32_t qsign,
+                                                             float* __restrict__ Opart, float* __restrict__ Lpart) {
+  constexpr int LPK = D / 8;     // lanes per key row
+  constexpr int KPW = 64 / LPK;  // keys per wavefront per step
+  constexpr int U = 8;           // steps loaded before computing
+  __shared__ float wm[4], wl[4];
+  __shared__ float wacc[4][D];
+  const int id = blockIdx.x;
+  const int bh = id % BH, split = id / BH;
+  const int kb = split * kchunk, ke = min(Sk, kb + kchunk);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane / LPK, c = lane % LPK;
+  const uint16_t* Kh = K + (size_t)bh * Sk * D + 8 * c;
+  const uint16_t* Vh = V + (size_t)bh * Sk * D + 8 * c;
+
+  float q[8];
+  {
+    u32x4 w = *reinterpret_cast<const u32x4*>(Q + (size_t)bh * D + 8 * c);
+    w ^= qsign;  // a negative scale flips the sign of q
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      q[2 * e] = __builtin_bit_cast(float, w[e] << 16);
+      q[2 * e + 1] = __builtin_bit_cast(float, w[e] & 0xFFFF0000u);
+    }
+  }
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+  float m_run = kNegInf;  // log2 units
+  float l = 0.0f;         // sum of this lane's key slot's probabilities
+
+  const int nstep = (ke - kb + 4 * KPW - 1) / (4 * KPW);  // steps of the workgroup
+  for (int it0 = 0; it0 < nstep; it0 += U) {
+    u32x4 kw[U], vw[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = kb + ((it0 + u) * 4 + wave) * KPW + g;
+      ok[u] = key < ke;  // covers steps past the end too
+      kw[u] = ok[u] ? *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D) : u32x4{0, 0, 0, 0};
+      vw[u] = ok[u] ? *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D) : u32x4{0, 0, 0, 0};
+    }
+    float sc[U];
+    float mx = kNegInf;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float dot = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dot = __builtin_fmaf(q[2 * e], __builtin_bit_cast(float, kw[u][e] << 16), dot);
+        dot = __builtin_fmaf(q[2 * e + 1], __builtin_bit_cast(float, kw[u][e] & 0xFFFF0000u), dot);
+      }
+#pragma unroll
+      for (int o = 1; o < LPK; o <<= 1) dot += __shfl_xor(dot, o);
+      sc[u] = ok[u] ? dot * C : kNegInf;
+      mx = __builtin_fmaxf(mx, sc[u]);
+    }
+#pragma unroll
+    for (int o = LPK; o < 64; o <<= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, o));
+    const float m_new = __builtin_fmaxf(m_run, mx);
+    if (m_new == kNegInf) continue;  // no key of this wavefront in these steps (wave-uniform)
+    const float alpha = exp2_native(m_run - m_new);  // 0 on the first keys (m_run = -inf)
+    l *= alpha;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= alpha;
+    m_run = m_new;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float p = ok[u] ? exp2_native(sc[u] - m_run) : 0.0f;
+      l += p;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = __builtin_fmaf(p, __builtin_bit_cast(float, vw[u][e] << 16), acc[2 * e]);
+        acc[2 * e + 1] = __builtin_fmaf(p, __builtin_bit_cast(float, vw[u][e] & 0xFFFF0000u), acc[2 * e + 1]);
+      }
+    }
+  }
+  // sum over the key slots of the wavefront (lanes with equal c)
+#pragma unroll
+  for (int o = LPK; o < 64; o <<= 1) {
+    l += __shfl_xor(l, o);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] += __shfl_xor(acc[j], o);
+  }
+  if (lane < LPK) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wacc[wave][8 * lane + j] = acc[j];
+  }
+  if (lane == 0) {
+    wm[wave] = m_run;
+    wl[wave] = l;
+  }
+  __syncthreads();
+  if (tid < D) {
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = __builtin_fmaxf(M, wm[w]);
+    float L = 0.0f, o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = (wm[w] == kNegInf) ? 0.0f : exp2_native(wm[w] - M);
+      L += f * wl[w];
+      o += f * wacc[w][tid];
+    }
+    // the split holds at least one key (kb < Sk), so M is finite and L > 0
+    Opart[((size_t)split * BH + bh) * D + tid] = o / L;
+    if (tid == 0) Lpart[(size_t)split * BH + bh] = (M + __log2f(L)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Split-KV merge: per row, LSE = ln sum_c exp(LSE_c) and
 // O = sum_c exp(LSE_c - LSE) O_c, rounded to bf16 (the decomposition of the
 // softmax over disjoint key sets that also makes LSE an output of the
@@ -568,7 +697,33 @@ static hipError_t launch_splitkv_e(const FwdArgs& a, const SplitKvLaunch& p, hip
   }
 }
 
+template <int D>
+static hipError_t launch_decode_t(const FwdArgs& a, const SplitKvLaunch& p, hipStream_t st) {
+  const int BH = a.B * a.H;
+  prof_begin(KID_FWD_SPLITKV, st);
+  hipLaunchKernelGGL((splitkv_decode_kernel<D>), dim3(BH * p.nsplit), dim3(256), 0, st, (const uint16_t*)a.Q,
+                     (const uint16_t*)a.K, (const uint16_t*)a.V, BH, p.Sk, p.kchunk, a.C, a.qsign, p.Opart, p.Lpart);
+  prof_end(KID_FWD_SPLITKV, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long rows = (long)BH;
+  const long threads = rows * (D / 4);
+  prof_begin(KID_SPLITKV_MERGE, st);
+  hipLaunchKernelGGL((splitkv_merge_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+                     (const float*)p.Opart, (const float*)p.Lpart, (uint16_t*)a.O, a.LSE, rows, p.nsplit);
+  prof_end(KID_SPLITKV_MERGE, st);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd_splitkv(const FwdArgs& a, const SplitKvLaunch& p, hipStream_t st) {
+  if (a.S == 1) {  // decoding: one query row per head
+    switch (a.D) {
+      case 64: return launch_decode_t<64>(a, p, st);
+      case 128: return launch_decode_t<128>(a, p, st);
+      case 256: return launch_decode_t<256>(a, p, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (a.D) {
     case 64: return launch_splitkv_e<FwdDefault<64>::type>(a, p, st);
     case 128: return launch_splitkv_e<FwdDefault<128>::type>(a, p, st);

@@ -144,6 +144,8 @@ attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O,
  *   (requires Sk >= Sq, else ATTN_ERR_SHAPE; Sq == Sk is attn_fwd's mask).
  *   num_splits: number of key chunks, >= 1, clamped to the number of key
  *   tiles; 0 chooses one that gives about two workgroups per compute unit.
+ *   Sq == 1 (decoding) runs a dedicated kernel: fp32 dot products, no
+ *   matrix tiles, native exp2 whatever opts->exp_mode says.
  *   workspace: caller-owned device memory of at least
  *   attn_fwd_splitkv_workspace_bytes(...) bytes (same arguments), 256-byte
  *   aligned, holding the per-chunk fp32 outputs and LSEs; contents on entry
