@@ -64,6 +64,30 @@ __device__ __forceinline__ i32x8 lds_frag32(const uint8_t* p0, const uint8_t* p1
   return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
 }
 
+// The value of lane l ^ 32 (M = 32) or l ^ 16 (M = 16), by the gfx950
+// half-swap instructions (no LDS round trip).  Called with the same register
+// as both operands, v_permlane32_swap returns [0]: the lower 32 lanes' values
+// in the upper lanes (own values below), [1]: the upper lanes' values in the
+// lower lanes; v_permlane16_swap does the same between the 16-lane rows
+// (0, 1) and (2, 3).  The partner's value is [0] in the upper lanes, [1] below.
+template <int M>
+__device__ __forceinline__ double lane_xor_f64(double x, bool upper) {
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t w = __builtin_bit_cast(u32x2_t, x);
+  u32x2_t o;
+  if constexpr (M == 32) {
+    const auto a = __builtin_amdgcn_permlane32_swap(w[0], w[0], false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(w[1], w[1], false, false);
+    o = upper ? u32x2_t{a[0], b[0]} : u32x2_t{a[1], b[1]};
+  } else {
+    static_assert(M == 16, "half or row swap");
+    const auto a = __builtin_amdgcn_permlane16_swap(w[0], w[0], false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(w[1], w[1], false, false);
+    o = upper ? u32x2_t{a[0], b[0]} : u32x2_t{a[1], b[1]};
+  }
+  return __builtin_bit_cast(double, o);
+}
+
 // ---------------------------------------------------------------------------
 // Quantize Q and K.  Grid (Sp / 64, B*H, 2): z = 0 Q, z = 1 K; four
 // wavefronts of 16 rows; lane l handles quarter qd = l >> 4 (elements
@@ -115,13 +139,19 @@ __global__ __launch_bounds__(256) void fp8_qk_quant_kernel(const uint16_t* __res
     for (int i = 0; i < 32; ++i) x[i] *= (double)signs[32 * qd + i];
     // stage 64 (partner quarter qd ^ 2), then stage 32 (partner qd ^ 1): the
     // lane holding the upper part keeps (other - own), the lower one (own + other)
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int m = st == 0 ? 32 : 16;
-      const bool upper = (lane & m) != 0;
+    {
+      const bool upper = (lane & 32) != 0;
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        const double other = __shfl_xor(x[i], m);
+        const double other = lane_xor_f64<32>(x[i], upper);
+        x[i] = upper ? (other - x[i]) : (x[i] + other);
+      }
+    }
+    {
+      const bool upper = (lane & 16) != 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const double other = lane_xor_f64<16>(x[i], upper);
         x[i] = upper ? (other - x[i]) : (x[i] + other);
       }
     }
