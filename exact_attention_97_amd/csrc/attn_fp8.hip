@@ -335,7 +335,7 @@ __device__ __forceinline__ float fp8_tile_max(f32x16 (&s)[2], int k0, int lim, i
       mx = __builtin_fmaxf(mx, s[kb][r]);
     }
   }
-  return __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+  return __builtin_fmaxf(mx, wave_swap_halves(mx));
 }
 
 __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8Buf f, uint16_t* __restrict__ O, float* __restrict__ LSE,
@@ -509,7 +509,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8Buf f, uint16_t* __r
   }
 
   // ---- epilogue: O = acc * vs / l, LSE = ln2 * (m + log2 l) ----------------
-  const float l_tot = l_part + __shfl_xor(l_part, 32);
+  const float l_tot = l_part + wave_swap_halves(l_part);
   const float inv = 1.0f / l_tot;
   if (qrow < S) {
     const float* vsh = f.vs + (size_t)bh * FD;

@@ -109,6 +109,14 @@ __device__ __forceinline__ float exp2_mode(float x, int idx) {
   }
 }
 
-__device__ __forceinline__ float wave_swap_halves(float x) { return __shfl_xor(x, 32); }
+// The value of lane l ^ 32.  v_permlane32_swap (gfx950) called with one
+// register as both operands returns [0]: the lower half's values in the
+// upper lanes, [1]: the upper half's values in the lower lanes; no LDS round
+// trip, unlike a general shuffle.
+__device__ __forceinline__ float wave_swap_halves(float x) {
+  const unsigned int u = __builtin_bit_cast(unsigned int, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+}
 
 }  // namespace attn97
