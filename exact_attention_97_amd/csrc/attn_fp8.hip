@@ -341,8 +341,13 @@ __device__ __forceinline__ float fp8_tile_max(f32x16 (&s)[2], int k0, int lim, i
 __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8Buf f, uint16_t* __restrict__ O, float* __restrict__ LSE,
                                                          int BH, int S, int nqt, float C, uint32_t qsign, float tau,
                                                          int causal) {
-  __shared__ __attribute__((aligned(1024))) uint8_t Kb[2][FBC * FD];
-  __shared__ __attribute__((aligned(1024))) uint8_t Vb[2][FD * FBC];
+  // one __shared__ array per buffer, chosen at compile time (the loop is
+  // unrolled by two): the compiler then sees that a tile load in flight does
+  // not alias the buffer being read and does not wait for it
+  __shared__ __attribute__((aligned(1024))) uint8_t Kb0[FBC * FD];
+  __shared__ __attribute__((aligned(1024))) uint8_t Kb1[FBC * FD];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vb0[FD * FBC];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vb1[FD * FBC];
 
   const int Sp = f.Sp;
   const int id = blockIdx.x;
@@ -395,9 +400,10 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8Buf f, uint16_t* __r
   };
   // iteration j issues K(j + 2) and V(j + 1) into the buffers the barrier of
   // iteration j - 1 freed; it reads K(j + 1) (scores of the next tile) and V(j)
-  auto issue = [&](int j) {
-    if (j + 2 < nkt) dma(Kh + (size_t)(j + 2) * FBC * FD, Kb[j & 1], of.kdma);
-    if (j + 1 >= 0 && j + 1 < nkt) dma(Vh + (size_t)(j + 1) * FBC, Vb[(j + 1) & 1], of.vdma);
+  auto issue = [&](int j, auto P) {  // P = j & 1
+    constexpr int par = decltype(P)::value;
+    if (j + 2 < nkt) dma(Kh + (size_t)(j + 2) * FBC * FD, par ? Kb1 : Kb0, of.kdma);
+    if (j + 1 >= 0 && j + 1 < nkt) dma(Vh + (size_t)(j + 1) * FBC, par ? Vb0 : Vb1, of.vdma);
   };
   auto scores = [&](const uint8_t* kb_, f32x16 (&s)[2]) {
 #pragma unroll
@@ -416,16 +422,21 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8Buf f, uint16_t* __r
   float m_run = kNegInf;  // running max in log2 units
   float l_part = 0.0f;    // this lane's partial row sum (unrounded P)
 
-  issue(-2);
-  issue(-1);
+  // the tile's K scale is loaded an iteration ahead: the wait for all loads
+  // that ends each iteration then covers it (a wait for it inside the tile
+  // would also wait for the tile loads issued after it)
+  float ks_cur = ksh[0];
+  issue(-2, std::integral_constant<int, 0>{});
+  issue(-1, std::integral_constant<int, 1>{});
   wait_vm_lds<0>();
   __syncthreads();
   f32x16 sa[2], sb[2];
-  scores(Kb[0], sa);
+  scores(Kb0, sa);
   wait_vm_lds<63>();
   barrier_keep_loads();
 
-  auto step = [&](auto maskc, int kt, float ks_t, f32x16(&scur)[2], f32x16(&snext)[2]) {
+  auto step = [&](auto maskc, auto P, int kt, float ks_t, f32x16(&scur)[2], f32x16(&snext)[2]) {
+    constexpr int par = decltype(P)::value;  // kt & 1
     constexpr bool MASK = decltype(maskc)::value;
     // distinct code at the top of each copy: keeps the compiler from hoisting
     // the two copies' common reads out of the masked / unmasked branch
@@ -435,7 +446,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8Buf f, uint16_t* __r
     // interleaved with this tile's softmax.  Back to back, each MFMA would
     // hold the wavefront until the previous one leaves the matrix pipe.
     __builtin_amdgcn_s_setprio(1);
-    scores(Kb[(kt + 1) & 1], snext);
+    scores(par ? Kb0 : Kb1, snext);
     const float mx = fp8_tile_max<MASK>(scur, kt * FBC, lim, hh);
     const float mxs = (mx == kNegInf) ? kNegInf : mx * ct;
     const float m_new = __builtin_fmaxf(m_run, mxs);
@@ -484,28 +495,29 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8Buf f, uint16_t* __r
 #pragma unroll
       for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
     }
-    const uint8_t* vb = Vb[kt & 1];
+    const uint8_t* vb = par ? Vb1 : Vb0;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
       oacc[db] = mfma_fp8(lds_frag32(vb + 32 * db * FBC + of.vfrag[0], vb + 32 * db * FBC + of.vfrag[1]), pf, oacc[db]);
   };
 
-  auto iteration = [&](int kt, f32x16(&scur)[2], f32x16(&snext)[2]) {
-    const float ks_t = ksh[kt];  // this tile's K scale, loaded ahead of the tile loads
-    issue(kt);
+  auto iteration = [&](int kt, auto P, f32x16(&scur)[2], f32x16(&snext)[2]) {
+    const float ks_t = ks_cur;
+    ks_cur = kt + 1 < nkt ? ksh[kt + 1] : 0.0f;  // used by the next iteration
+    issue(kt, P);
     __builtin_amdgcn_sched_barrier(0);
     if (kt < nkt_w) {
       if (kt < nfull)
-        step(std::false_type{}, kt, ks_t, scur, snext);
+        step(std::false_type{}, P, kt, ks_t, scur, snext);
       else
-        step(std::true_type{}, kt, ks_t, scur, snext);
+        step(std::true_type{}, P, kt, ks_t, scur, snext);
     }
     wait_vm_lds<0>();
     barrier_keep_loads();
   };
   for (int kt = 0; kt < nkt; kt += 2) {
-    iteration(kt, sa, sb);
-    if (kt + 1 < nkt) iteration(kt + 1, sb, sa);
+    iteration(kt, std::integral_constant<int, 0>{}, sa, sb);
+    if (kt + 1 < nkt) iteration(kt + 1, std::integral_constant<int, 1>{}, sb, sa);
   }
 
   // ---- epilogue: O = acc * vs / l, LSE = ln2 * (m + log2 l) ----------------

@@ -39,6 +39,8 @@
 // barrier per tile suffices.
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "attn_kernels.hpp"
 #include "device_common.hpp"
 #include "tile_layout.hpp"
@@ -257,8 +259,19 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
   constexpr int NBUF = Cfg::NBUF, DPW = Cfg::DMA_PER_WAVE;
   constexpr int TILE = Cfg::TILE_BYTES / 2;  // elements
 
-  __shared__ __attribute__((aligned(1024))) uint16_t Kb[NBUF][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vb[NBUF][TILE];
+  // One __shared__ array per buffer: with two buffers every buffer choice
+  // below is a compile-time constant (the loop is unrolled by two), and the
+  // compiler then sees that a tile load in flight cannot alias the buffer
+  // being read (with one array indexed at run time it waits for all loads
+  // before each read).
+  __shared__ __attribute__((aligned(1024))) uint16_t Kb0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t Kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vb0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vb1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Kb2[NBUF > 2 ? TILE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t Vb2[NBUF > 2 ? TILE : 8];
+  auto kbuf = [&](int i) -> uint16_t* { return i == 0 ? Kb0 : (i == 1 ? Kb1 : Kb2); };
+  auto vbuf = [&](int i) -> uint16_t* { return i == 0 ? Vb0 : (i == 1 ? Vb1 : Vb2); };
 
   // Heaviest causal query tiles first, all heads of one rank together; with
   // B*H a multiple of 8 every workgroup of one head lands on the same XCD.
@@ -339,14 +352,15 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
   // the buffers freed by the barrier of iteration j-1, and needs K(j + 1)
   // (scores of the next tile) and V(j).  The prologue issues what iterations
   // -NBUF..-1 would have.
-  auto issue = [&](int j) {  // loads of "iteration" j; returns the number of ops issued
+  // ki, vi: the buffers of K(j + NBUF) and V(j + NBUF - 1)
+  auto issue = [&](int j, int ki, int vi) {  // loads of "iteration" j; returns the number of ops issued
     int n = 0;
     if (j + NBUF < nkt) {
-      dma_tile<Cfg>(Kh, kb + (j + NBUF) * BC, Sk, Kb[(j + NBUF) % NBUF], wave, of.dma);
+      dma_tile<Cfg>(Kh, kb + (j + NBUF) * BC, Sk, kbuf(ki), wave, of.dma);
       n += DPW;
     }
     if (j + NBUF - 1 >= 0 && j + NBUF - 1 < nkt) {
-      dma_tile<Cfg>(Vh, kb + (j + NBUF - 1) * BC, Sk, Vb[(j + NBUF - 1) % NBUF], wave, of.dma);
+      dma_tile<Cfg>(Vh, kb + (j + NBUF - 1) * BC, Sk, vbuf(vi), wave, of.dma);
       n += DPW;
     }
     return n;
@@ -363,36 +377,43 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
   };
 
   int n_last = 0;
-  for (int j = -NBUF; j < 0; ++j) n_last = issue(j);
+  for (int j = -NBUF; j < 0; ++j) n_last = issue(j, (j + NBUF) % NBUF, (j + NBUF - 1 + NBUF) % NBUF);
   wait_loads(n_last);
   __syncthreads();
 
   // scores of the current and the next tile; the loop is unrolled by two so
   // that the two sets swap roles instead of being copied
   f32x16 sa[NKB], sb[NKB];
-  W::scores(Kb[0], of, qreg, sa);
-  // iteration 0 reloads Kb[0] (with K(NBUF)): every wave's reads of K(0)
+  W::scores(Kb0, of, qreg, sa);
+  // iteration 0 reloads buffer 0 (with K(NBUF)): every wave's reads of K(0)
   // must be complete first
   wait_vm_lds<63>();
   barrier_keep_loads();
 
-  auto iteration = [&](int kt, f32x16(&scur)[NKB], f32x16(&snext)[NKB]) {
-    n_last = issue(kt);
+  // P = kt & 1 (the loop is unrolled by two); with two buffers all indices
+  // follow from it at compile time
+  auto iteration = [&](int kt, auto P, f32x16(&scur)[NKB], f32x16(&snext)[NKB]) {
+    constexpr int par = decltype(P)::value;
+    const int kn = NBUF == 2 ? 1 - par : (kt + 1) % NBUF;  // K(kt + 1)
+    const int vc = NBUF == 2 ? par : kt % NBUF;            // V(kt)
+    const int ki = NBUF == 2 ? par : kt % NBUF;            // K(kt + NBUF)
+    const int vi = NBUF == 2 ? 1 - par : (kt + NBUF - 1) % NBUF;  // V(kt + NBUF - 1)
+    n_last = issue(kt, ki, vi);
     __builtin_amdgcn_sched_barrier(0);  // keep the load issue out of the compute schedule
     if (kt < nkt_w) {
       if (kt < nfull)
-        W::template step<false>(Kb[(kt + 1) % NBUF], Vb[kt % NBUF], of, qreg, scur, snext, oacc, m_run, l_part,
-                                kb + kt * BC, lim, hh, C, tau);
+        W::template step<false>(kbuf(kn), vbuf(vc), of, qreg, scur, snext, oacc, m_run, l_part, kb + kt * BC, lim,
+                                hh, C, tau);
       else
-        W::template step<true>(Kb[(kt + 1) % NBUF], Vb[kt % NBUF], of, qreg, scur, snext, oacc, m_run, l_part,
-                               kb + kt * BC, lim, hh, C, tau);
+        W::template step<true>(kbuf(kn), vbuf(vc), of, qreg, scur, snext, oacc, m_run, l_part, kb + kt * BC, lim,
+                               hh, C, tau);
     }
     wait_loads(n_last);
     barrier_keep_loads();
   };
   for (int kt = 0; kt < nkt; kt += 2) {
-    iteration(kt, sa, sb);
-    if (kt + 1 < nkt) iteration(kt + 1, sb, sa);
+    iteration(kt, std::integral_constant<int, 0>{}, sa, sb);
+    if (kt + 1 < nkt) iteration(kt + 1, std::integral_constant<int, 1>{}, sb, sa);
   }
 
 // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l) ----------------------
