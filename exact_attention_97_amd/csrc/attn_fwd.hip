@@ -1,8 +1,10 @@
 // attn_fwd.hip - forward pass of exact attention on gfx950.
 //
-// One workgroup of four wavefronts owns a tile of 128 query rows of one
-// (batch, head); each wavefront owns 32 of those rows and walks the key/value
-// sequence one tile of BC keys at a time:
+// One workgroup owns a tile of query rows of one (batch, head): eight
+// wavefronts and 256 rows at D = 128 (all eight share each K / V tile in
+// LDS), four and 128 at D = 64 and 256 and in the split-KV kernel.  Each
+// wavefront owns 32 of those rows and walks the key/value sequence one tile
+// of BC keys at a time:
 //
 //   S^T = K Q^T          bf16 MFMA, fp32 accumulate (scores, keys x queries)
 //   mask, row max        in-lane over the wavefront's half, one swap of halves
@@ -36,7 +38,8 @@
 // Pipeline: while the softmax of tile j runs on the VALU, the MFMA unit
 // computes the scores of tile j+1; then P_j V_j.  K tiles are loaded two
 // tiles ahead and V tiles one ahead, each into a double buffer, so one
-// barrier per tile suffices.
+// barrier per tile suffices.  One-query-row calls of the split-KV path
+// (decoding) run splitkv_decode_kernel instead, which has no matrix tiles.
 #include <stdlib.h>
 
 #include <type_traits>
