@@ -139,6 +139,21 @@ def gemm_reference(torch, dev, M=16384, N=16384, K=8192, reps=10):
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 
 
+def warm_up(torch, fn, min_ms=300.0):
+    """Run fn until at least min_ms of wall time has passed (three calls at
+    least).  The GPU clock drops while the host builds inputs and takes tens
+    of milliseconds to come back; a fixed count of short calls can end before
+    it has, and the first timed calls then run slow."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < 3 or (time.perf_counter() - t0) * 1e3 < min_ms:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def splitkv_measure(torch, attn, dev, reps=20):
     """Split-KV forward on its two workloads (outside the headline step).
 
@@ -157,9 +172,8 @@ def splitkv_measure(torch, attn, dev, reps=20):
         lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device=dev)
         ws = torch.empty(max(1, attn.fwd_splitkv_workspace_bytes(w.B, w.H, w.Sq, w.Sk, w.D, w.causal)),
                          dtype=torch.uint8, device=dev)
-        for _ in range(3):
-            attn.attn_fwd_splitkv(q, k, v, scale=w.scale, causal=w.causal, workspace=ws, out=o, lse=lse)
-        torch.cuda.synchronize()
+        warm_up(torch, lambda: attn.attn_fwd_splitkv(q, k, v, scale=w.scale, causal=w.causal, workspace=ws, out=o,
+                                                     lse=lse))
         attn.prof_reset()
         attn.prof_enable(True)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -210,9 +224,7 @@ def fp8_measure(torch, attn, dev, B, H, S, D, reps=20):
     lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
     out = {"workload": f"B={B} H={H} S={S} D={D}, Q and K with 1% x20 outliers, random-sign Hadamard transform"}
     for causal in (False, True):
-        for _ in range(3):
-            attn.attn_fwd_fp8_quantized(buf, B, H, S, D, causal=causal, out=o, lse=lse)
-        torch.cuda.synchronize()
+        warm_up(torch, lambda: attn.attn_fwd_fp8_quantized(buf, B, H, S, D, causal=causal, out=o, lse=lse))
         attn.prof_reset()
         attn.prof_enable(True)
         for _ in range(reps):
@@ -227,6 +239,7 @@ def fp8_measure(torch, attn, dev, B, H, S, D, reps=20):
             "ms": round(ms, 4), "tflops": round(tf, 1),
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / FP8_PEAK_TFLOPS, 4), "flops_per_launch": flops}}
+    warm_up(torch, lambda: attn.fp8_quantize(q, k, v, sg, buf=buf))
     attn.prof_reset()
     attn.prof_enable(True)
     for _ in range(reps):

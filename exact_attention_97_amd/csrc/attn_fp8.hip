@@ -37,7 +37,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int FD = 128;   // head dim
 constexpr int FBC = 64;   // keys per tile
-constexpr int FBR = 128;  // queries per workgroup (four wavefronts of 32)
+constexpr int FBR = 128;  // query padding of the buffer (rows per four-wavefront workgroup)
 constexpr float kE4M3Max = 448.0f;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
@@ -301,6 +301,9 @@ struct Fp8Wave {
   int vfrag[2];     // [half]: row c32 of V^T, chunks 2 hh + half
   uint32_t kdma[2], vdma[2];  // DMA source offsets (bytes) of this lane's chunks
 
+  // NCH = 16-byte chunks per lane of one 8 KiB tile (2 with four
+  // wavefronts, 1 with eight)
+  template <int NCH>
   __device__ __forceinline__ void init(int wave, int lane, int Sp) {
     const int hh = lane >> 5, c32 = lane & 31;
     const int kx = (c32 >> 1) & 7, vx = (c32 >> 2) & 3;
@@ -311,8 +314,8 @@ struct Fp8Wave {
 #pragma unroll
     for (int h = 0; h < 2; ++h) vfrag[h] = c32 * FBC + (((2 * hh + h) ^ vx) * 16);
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int P = 64 * (2 * wave + n) + lane;  // physical 16-byte chunk of the tile
+    for (int n = 0; n < NCH; ++n) {
+      const int P = 64 * (NCH * wave + n) + lane;  // physical 16-byte chunk of the tile
       const int krow = P >> 3, kc = (P & 7) ^ ((krow >> 1) & 7);
       kdma[n] = (uint32_t)(krow * FD + kc * 16);
       const int vrow = P >> 2, vc = (P & 3) ^ ((vrow >> 2) & 3);
@@ -338,9 +341,14 @@ __device__ __forceinline__ float fp8_tile_max(f32x16 (&s)[2], int k0, int lim, i
   return __builtin_fmaxf(mx, wave_swap_halves(mx));
 }
 
-__global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8Buf f, uint16_t* __restrict__ O, float* __restrict__ LSE,
-                                                         int BH, int S, int nqt, float C, uint32_t qsign, float tau,
-                                                         int causal) {
+// NW wavefronts (4 or 8) of 32 query rows each share every K / V tile.
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_fp8_kernel(Fp8Buf f, uint16_t* __restrict__ O,
+                                                                float* __restrict__ LSE, int BH, int S, int nqt,
+                                                                float C, uint32_t qsign, float tau, int causal) {
+  constexpr int BR = 32 * NW;         // query rows of the workgroup
+  constexpr int NCH = 512 / (64 * NW);  // 16-byte chunks per lane of a tile
+  static_assert(NCH * 64 * NW == 512, "a tile is 512 chunks of 16 bytes");
   // one __shared__ array per buffer, chosen at compile time (the loop is
   // unrolled by two): the compiler then sees that a tile load in flight does
   // not alias the buffer being read and does not wait for it
@@ -354,14 +362,17 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8Buf f, uint16_t* __r
   const int bh = id % BH;
   const int rank = id / BH;
   const int qt = causal ? (nqt - 1 - rank) : rank;  // heaviest causal tiles first
-  const int q0 = qt * FBR;
+  const int q0 = qt * BR;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int hh = lane >> 5;
   const int c32 = lane & 31;
   const int qw0 = q0 + 32 * wave;
-  const int qrow = qw0 + c32;  // < Sp always
+  const int qrow = qw0 + c32;
+  // rows past the padded length (eight wavefronts, Sp an odd multiple of
+  // 128) read the last padded row and store nothing
+  const int qread = min(qrow, Sp - 1);
   const uint8_t* Kh = f.k8 + (size_t)bh * Sp * FD;
   const uint8_t* Vh = f.v8t + (size_t)bh * FD * Sp;
   const float* ksh = f.ks + (size_t)bh * (Sp / FBC);
@@ -369,7 +380,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8Buf f, uint16_t* __r
   // Q^T operand: lane holds bytes 64 t + 32 hh .. + 31 of row qrow
   i32x8 qreg[2];
   {
-    const uint8_t* qp = f.q8 + ((size_t)bh * Sp + qrow) * FD;
+    const uint8_t* qp = f.q8 + ((size_t)bh * Sp + qread) * FD;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       u32x4 a = *reinterpret_cast<const u32x4*>(qp + 64 * t + 32 * hh);
@@ -379,9 +390,9 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8Buf f, uint16_t* __r
       qreg[t] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
     }
   }
-  const float cq = C * f.qs[(size_t)bh * Sp + qrow];  // scale * log2(e) * this row's Q scale
+  const float cq = C * f.qs[(size_t)bh * Sp + qread];  // scale * log2(e) * this row's Q scale
 
-  const int kend = causal ? min(S, q0 + FBR) : S;
+  const int kend = causal ? min(S, q0 + BR) : S;
   const int nkt = (kend + FBC - 1) / FBC;
   const int wend = causal ? min(kend, qw0 + 32) : kend;
   const int nkt_w = qw0 < S ? (wend + FBC - 1) / FBC : 0;
@@ -390,13 +401,14 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8Buf f, uint16_t* __r
   const int lim = causal ? min(qrow, S - 1) : (S - 1);
 
   Fp8Wave of;
-  of.init(wave, lane, Sp);
+  of.init<NCH>(wave, lane, Sp);
 
   auto dma = [&](const uint8_t* src, uint8_t* dst, const uint32_t (&off)[2]) {
 #pragma unroll
-    for (int n = 0; n < 2; ++n)
-      __builtin_amdgcn_global_load_lds(src + off[n], (__attribute__((address_space(3))) void*)(dst + 1024 * (2 * wave + n)),
-                                       16, 0, 0);
+    for (int n = 0; n < NCH; ++n)
+      __builtin_amdgcn_global_load_lds(src + off[n],
+                                       (__attribute__((address_space(3))) void*)(dst + 1024 * (NCH * wave + n)), 16,
+                                       0, 0);
   };
   // iteration j issues K(j + 2) and V(j + 1) into the buffers the barrier of
   // iteration j - 1 freed; it reads K(j + 1) (scores of the next tile) and V(j)
@@ -589,10 +601,16 @@ hipError_t launch_fp8_quantize(const void* Q, const void* K, const void* V, cons
 hipError_t launch_fwd_fp8(const Fp8Buf& f, void* O, float* LSE, int B, int H, int S, float C, uint32_t qsign,
                           float tau, int causal, hipStream_t st) {
   const int BH = B * H;
-  const int nqt = f.Sp / FBR;
+  // variant 1: eight wavefronts (256 query rows) per workgroup
+  const int nw = kernel_variant(VAR_FWD_FP8) == 1 ? 8 : 4;
+  const int nqt = (f.Sp + 32 * nw - 1) / (32 * nw);
   prof_begin(KID_FWD_FP8, st);
-  hipLaunchKernelGGL(fwd_fp8_kernel, dim3(nqt * BH), dim3(256), 0, st, f, (uint16_t*)O, LSE, BH, S, nqt, C, qsign,
-                     tau, causal);
+  if (nw == 8)
+    hipLaunchKernelGGL(fwd_fp8_kernel<8>, dim3(nqt * BH), dim3(512), 0, st, f, (uint16_t*)O, LSE, BH, S, nqt, C,
+                       qsign, tau, causal);
+  else
+    hipLaunchKernelGGL(fwd_fp8_kernel<4>, dim3(nqt * BH), dim3(256), 0, st, f, (uint16_t*)O, LSE, BH, S, nqt, C,
+                       qsign, tau, causal);
   prof_end(KID_FWD_FP8, st);
   return hipGetLastError();
 }

@@ -232,8 +232,9 @@ attn_status attn_exp2_eval(const float* x, float* y, long n, int mode, void* str
  * wavefronts per workgroup, load schedules), for subsequent calls in this
  * process.  kernel: "fwd" (D = 128 forward: 0 default, 1..4), "bwd_dkdv"
  * (D = 128 split-mode dK/dV: 0 default, 1..5), "bwd_dq" (D = 128 dQ: 0
- * default, 1..2); variant -1 returns to the choice of the environment
- * variables ATTN97_FWD_VARIANT / ATTN97_DKDV_VARIANT / ATTN97_DQ_VARIANT
+ * default, 1..2), "fwd_fp8" (FP8 forward: 0 default, 1); variant -1
+ * returns to the choice of the environment variables ATTN97_FWD_VARIANT /
+ * ATTN97_DKDV_VARIANT / ATTN97_DQ_VARIANT / ATTN97_FWD_FP8_VARIANT
  * (default 0).  Every variant computes the same result.  Not thread-safe.
  * Errors: ATTN_ERR_NULL, ATTN_ERR_UNSUPPORTED (unknown kernel name),
  * ATTN_ERR_VALUE (variant out of range).

@@ -237,7 +237,9 @@ def test_set_variant():
     assert lib.attn_set_variant(b"bwd_dq", 3) == VALUE
     assert lib.attn_set_variant(b"bwd_dkdv", 6) == VALUE
     assert lib.attn_set_variant(b"bwd_dkdv", -2) == VALUE
+    assert lib.attn_set_variant(b"fwd_fp8", 1) == OK
+    assert lib.attn_set_variant(b"fwd_fp8", 2) == VALUE
     assert lib.attn_set_variant(b"nope", 0) == UNSUP
     assert lib.attn_set_variant(None, 0) == NULL
-    for k in (b"fwd", b"bwd_dq", b"bwd_dkdv"):
+    for k in (b"fwd", b"bwd_dq", b"bwd_dkdv", b"fwd_fp8"):
         assert lib.attn_set_variant(k, -1) == OK
