@@ -113,6 +113,28 @@ def cpu_baseline(q, k, v, do, budget_s=15.0, max_heads=32):
     }
 
 
+def device_peak(torch):
+    """bf16 dense MFMA peak from the device's own attributes: compute units x
+    peak shader clock x 4096 flop per clock per CU (32x32x16 bf16 MFMA, 32
+    clocks, four SIMDs).  Read with hipDeviceGetAttribute from the HIP
+    runtime torch has loaded (same soname, so the same instance)."""
+    import ctypes
+
+    try:
+        hip = ctypes.CDLL("libamdhip64.so.7")
+        dev = torch.cuda.current_device()
+        clk, ncu = ctypes.c_int(0), ctypes.c_int(0)
+        # hipDeviceAttributeClockRate (kHz) = 5, hipDeviceAttributeMultiprocessorCount = 63
+        if hip.hipDeviceGetAttribute(ctypes.byref(clk), 5, dev) != 0:
+            return None
+        if hip.hipDeviceGetAttribute(ctypes.byref(ncu), 63, dev) != 0:
+            return None
+    except OSError:
+        return None
+    peak = ncu.value * clk.value * 1e3 * 4096 / 1e12
+    return {"compute_units": ncu.value, "clock_mhz": round(clk.value / 1e3, 1), "bf16_peak_tflops": round(peak, 1)}
+
+
 def gemm_reference(torch, dev, M=16384, N=16384, K=8192, reps=10):
     """Throughput of a large plain bf16 GEMM through torch.matmul (hipBLASLt) on the same GPU.
 
@@ -331,21 +353,28 @@ def main():
             kern[name] = {"launches": n, "avg_ms": ms / n}
 
     # ---- per-pass breakdown (separate, untimed for `value`) ----------------
+    # each pass timed per call with HIP events on the launch stream, 20 calls;
+    # TFLOP/s from the median, against the published and the device peak
+    dpeak = device_peak(torch)
     breakdown = {}
     for causal in (False, True):
         for which in ("fwd", "bwd"):
-            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = 10
-            ev0.record(stream)
-            for _ in range(reps):
+            reps = 20
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for e0, e1 in evs:
+                e0.record(stream)
                 run_pass(causal, which, False)
-            ev1.record(stream)
+                e1.record(stream)
             torch.cuda.synchronize()
-            ms = ev0.elapsed_time(ev1) / reps
+            times = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+            ms = 0.5 * (times[(reps - 1) // 2] + times[reps // 2])
             fl = fwd_flops(causal) if which == "fwd" else bwd_flops(causal)
             tf = fl / (ms * 1e-3) / 1e12
-            breakdown[f"{which}_{'causal' if causal else 'noncausal'}"] = {
-                "ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS, 4)}
+            entry = {"median_ms": round(ms, 4), "min_ms": round(times[0], 4), "tflops": round(tf, 1),
+                     "frac_of_peak": round(tf / PEAK_TFLOPS, 4)}
+            if dpeak:
+                entry["frac_of_device_peak"] = round(tf / dpeak["bf16_peak_tflops"], 4)
+            breakdown[f"{which}_{'causal' if causal else 'noncausal'}"] = entry
 
     # ---- roofline of the dominant kernel ------------------------------------
     # dominant = longest average non-causal launch among the MFMA kernels
@@ -389,6 +418,7 @@ def main():
         "breakdown": breakdown,
         "kernels_noncausal_avg_ms": {k2: round(v2["avg_ms"], 4) for k2, v2 in kern.items()},
         "roofline": roofline,
+        "device_peak": dpeak,
         "gemm_reference": gemm_reference(torch, dev),
         "splitkv": splitkv_measure(torch, attn, dev),
         "fp8": fp8_measure(torch, attn, dev, B, H, S, D),

@@ -8,6 +8,7 @@ and nothing else, so a counter run over it sees only these kernels plus
 input set-up.
 
     python3 -m exact_attention_97_amd.profile_driver --passes fwd,bwd --iters 2 --copy-mib 1024
+    python3 -m exact_attention_97_amd.profile_driver --passes fwd --exp-mode poly --tau 0 --iters 5
 """
 
 from __future__ import annotations
@@ -32,7 +33,10 @@ def main() -> None:
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--iters", type=int, default=2)
     ap.add_argument("--bwd-mode", default="split", choices=["split", "atomic"])
+    ap.add_argument("--exp-mode", default="native", choices=["native", "poly", "mixed"], help="forward exp2")
+    ap.add_argument("--tau", type=float, default=8.0, help="forward rescale threshold (log2 units)")
     ap.add_argument("--copy-mib", type=int, default=0, help="MiB of the calibration copy (0 = none)")
+    ap.add_argument("--outliers", action="store_true", help="1%% of Q and K entries x20 (the benchmark's inputs)")
     a = ap.parse_args()
     if not torch.cuda.is_available():
         raise SystemExit("profile_driver needs a GPU")
@@ -47,7 +51,8 @@ def main() -> None:
         print(f"copy {a.copy_mib} MiB done", flush=True)
         del x, y
 
-    q, k, v, do = (t.to(dev) for t in make_qkvdo(a.B, a.H, a.S, a.D, a.seed))
+    extra = dict(outlier_frac=0.01, outlier_scale=20.0) if a.outliers else {}
+    q, k, v, do = (t.to(dev) for t in make_qkvdo(a.B, a.H, a.S, a.D, a.seed, **extra))
     scale = 1.0 / math.sqrt(a.D)
     causal = bool(a.causal)
     o, lse = L.attn_fwd(q, k, v, scale=scale, causal=causal)
@@ -56,7 +61,8 @@ def main() -> None:
     for p in passes:
         if p == "fwd":
             for _ in range(a.iters):
-                L.attn_fwd(q, k, v, scale=scale, causal=causal, out=o, lse=lse)
+                L.attn_fwd(q, k, v, scale=scale, causal=causal, exp_mode=a.exp_mode, rescale_tau=a.tau, out=o,
+                           lse=lse)
         elif p == "fp8":
             from .inputs import hadamard_signs
 
