@@ -269,7 +269,7 @@ attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O,
   attn_opts o;
   st = read_opts(opts, &o);
   if (st != ATTN_OK) return st;
-  if (!attn97::bwd_supported(D)) return ATTN_ERR_UNSUPPORTED;
+  if (!attn97::bwd_supported(D, o.bwd_mode == ATTN_BWD_ATOMIC)) return ATTN_ERR_UNSUPPORTED;
   const size_t need = attn_bwd_workspace_bytes(B, H, S, D, causal, &o);
   if (workspace == nullptr || workspace_bytes < need || misaligned(workspace, 256))
     return ATTN_ERR_WORKSPACE;

@@ -125,13 +125,15 @@ struct BwdOffsets {
   uint32_t dmaq[Cfg::DMA_Q];
   uint32_t dmak[Cfg::DMA_K];
 
-  __device__ __forceinline__ void init(int wave, int lane) {
+  // d0: first column of the dK / dV block this workgroup forms (the
+  // transpose-read offsets start there; 0 unless the columns are split).
+  __device__ __forceinline__ void init(int wave, int lane, int d0 = 0) {
     const int hh = lane >> 5, c32 = lane & 31, i = lane & 15, g16 = lane >> 4;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) arow[ks] = swz_chunk<D>(c32, 2 * ks + hh) * 8;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const int d = 32 * db + 16 * (g16 & 1) + 4 * (i & 3);
+      const int d = d0 + 32 * db + 16 * (g16 & 1) + 4 * (i & 3);
 #pragma unroll
       for (int r2 = 0; r2 < 2; ++r2) {
         trq[db][r2] = swz_chunk<D>(8 * r2 + 4 * (g16 >> 1) + (i >> 2), d >> 3) * 8 + (d & 7);
@@ -185,12 +187,15 @@ __device__ __forceinline__ void dma_rows(const uint16_t* __restrict__ src, int r
 // the diagonal / ragged mask after the exponentials; one code path serves
 // every tile, so the operand reads stay inside the step's read-ahead
 // schedule.
-template <int D, class Cfg, bool CAUSAL, bool WRITE_DS, bool VLDS>
+// NDO: 32-wide column blocks of dK / dV this wavefront accumulates (D / 32,
+// or fewer when the workgroups split the columns; the offsets then start at
+// the block's first column).
+template <int D, class Cfg, bool CAUSAL, bool WRITE_DS, bool VLDS, int NDO>
 __device__ __forceinline__ void bwd_tile(BwdSmem<Cfg, WRITE_DS, VLDS>& sm, int buf, const BwdOffsets<D, Cfg>& of,
                                          const bf16x8 (&kreg)[D / 16], const bf16x8 (&vreg)[VLDS ? 1 : D / 16],
-                                         const uint16_t* Vw, f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], int q0,
+                                         const uint16_t* Vw, f32x16 (&dk)[NDO], f32x16 (&dv)[NDO], int q0,
                                          int key, int S, float C, int c32, int hh, int dsw, bool need_mask) {
-  constexpr int NQB = Cfg::NQB, NKS = Cfg::NKS, NDB = Cfg::NDB, SRS = Cfg::SRS, CPR = Cfg::CPR;
+  constexpr int NQB = Cfg::NQB, NKS = Cfg::NKS, NDB = NDO, SRS = Cfg::SRS, CPR = Cfg::CPR;
   const uint16_t* Qb = sm.Qs[buf];
   const uint16_t* dOb = sm.dOs[buf];
   const bool odd = c32 & 1;
@@ -454,7 +459,11 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* Qb, const uint16_t* dO
 // kernel (attn_bwd_dq.hip) forms dQ.  VLDS (split mode only) reads the V
 // operand from an LDS tile instead of registers; OCC is the target number of
 // workgroups per compute unit.
-template <int D, int BQ_, bool CAUSAL, bool WITH_DQ, bool VLDS, int OCC>
+// DSPLIT (split mode only): the dK / dV columns are divided among DSPLIT
+// workgroups per key tile; each recomputes P and dS over the full head dim
+// and accumulates D / DSPLIT columns (D = 256: the full-width accumulators
+// do not fit the register file next to the K / V operands).
+template <int D, int BQ_, bool CAUSAL, bool WITH_DQ, bool VLDS, int OCC, int DSPLIT = 1>
 __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ nlse2, const float* __restrict__ delta,
@@ -465,13 +474,19 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
   constexpr int BK = Cfg::BK, BQ = Cfg::BQ, NKS = Cfg::NKS, NDB = Cfg::NDB, SRS = Cfg::SRS, NDQ = Cfg::NDQ,
                 CPR = Cfg::CPR, DMA_Q = Cfg::DMA_Q, DMA_K = Cfg::DMA_K;
   static_assert(!WITH_DQ || (NDQ >= 1 && Cfg::NQB * NDB == NDQ * Cfg::NW), "dQ blocks split evenly");
+  static_assert(DSPLIT == 1 || (!WITH_DQ && NDB % DSPLIT == 0), "column split: split mode, whole blocks");
+  constexpr int NDO = NDB / DSPLIT;  // 32-wide dK / dV column blocks of this workgroup
 
   __shared__ __attribute__((aligned(1024))) BwdSmem<Cfg, WITH_DQ, VLDS> sm;
 
+  // with B*H a multiple of 8 all workgroups of one head (both column parts)
+  // land on one XCD
   const int id = blockIdx.x;
   const int bh = id % BH;
-  const int ktile = id / BH;  // causal: lowest keys (most work) first
+  const int part = (id / BH) % DSPLIT;
+  const int ktile = id / BH / DSPLIT;  // causal: lowest keys (most work) first
   const int k0 = ktile * BK;
+  const int d0 = part * (D / DSPLIT);  // first dK / dV column of this workgroup
   const size_t base = (size_t)bh * (size_t)S * D;
   const uint16_t* Qh = Q + base;
   const uint16_t* Kh = K + base;
@@ -490,7 +505,7 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
   const int key = kw0 + c32;       // this lane's key (MFMA column)
 
   BwdOffsets<D, Cfg> of;
-  of.init(wave, lane);
+  of.init(wave, lane, d0);
 
   // per-tile loads: Q and dO tiles by all waves, -LSE log2e / Delta (64
   // floats each, 4 bytes per lane, at least BQ of them used) by waves 0 / 1
@@ -527,9 +542,9 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
   const uint16_t* Vw = nullptr;  // this wave's 32 rows of the V tile
   if constexpr (VLDS) Vw = sm.Vs + 32 * wave * D;
 
-  f32x16 dk[NDB], dv[NDB];
+  f32x16 dk[NDO], dv[NDO];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
+  for (int db = 0; db < NDO; ++db) {
     dk[db] = f32x16{};
     dv[db] = f32x16{};
   }
@@ -550,8 +565,8 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
     const bool active = !CAUSAL || (q0 + BQ - 1 >= kw0);  // wave-uniform
     if (active) {
       const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > S) || (q0 + BQ > S);
-      bwd_tile<D, Cfg, CAUSAL, WITH_DQ, VLDS>(sm, buf, of, kreg, vreg, Vw, dk, dv, q0, key, S, C, c32, hh, dsw,
-                                              need_mask);
+      bwd_tile<D, Cfg, CAUSAL, WITH_DQ, VLDS, NDO>(sm, buf, of, kreg, vreg, Vw, dk, dv, q0, key, S, C, c32, hh, dsw,
+                                                   need_mask);
     } else {
       if constexpr (WITH_DQ) {
 #pragma unroll
@@ -602,8 +617,8 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
 
   // ---- epilogue: dK = scale * acc, dV = acc (bf16) -------------------------
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const int d = 32 * db + c32;
+  for (int db = 0; db < NDO; ++db) {
+    const int d = d0 + 32 * db + c32;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kk = kw0 + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -868,15 +883,19 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict
   }
 }
 
-bool bwd_supported(int D) { return D == 64 || D == 128; }
+// The atomic mode keeps full-width dK, dV and the dQ tile's K operands in
+// one workgroup, which does not fit at D = 256; the split mode divides the
+// dK / dV columns there.
+bool bwd_supported(int D, bool atomic) { return D == 64 || D == 128 || (D == 256 && !atomic); }
 
-template <int D, int BQ, bool CAUSAL, bool WITH_DQ, bool VLDS, int OCC>
+template <int D, int BQ, bool CAUSAL, bool WITH_DQ, bool VLDS, int OCC, int DSPLIT = 1>
 static hipError_t launch_main_t(const BwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   const int nkt = (a.S + BwdCfg<D, BQ>::BK - 1) / BwdCfg<D, BQ>::BK;
   const int kid = WITH_DQ ? KID_BWD_MAIN : KID_BWD_DKDV;
   prof_begin(kid, st);
-  hipLaunchKernelGGL((bwd_main_kernel<D, BQ, CAUSAL, WITH_DQ, VLDS, OCC>), dim3(nkt * BH), dim3(256), 0, st,
+  hipLaunchKernelGGL((bwd_main_kernel<D, BQ, CAUSAL, WITH_DQ, VLDS, OCC, DSPLIT>), dim3(nkt * BH * DSPLIT), dim3(256),
+                     0, st,
                      (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                      (const uint16_t*)a.dO, a.nlse2, a.delta, a.dq32, (uint16_t*)a.dK,
                      (uint16_t*)a.dV, BH, a.S, a.scale, a.scale * kLog2e);
@@ -912,8 +931,12 @@ static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
       default: break;
     }
     return launch_dkdv_pipe_t<CAUSAL>(a, st);
+  } else if constexpr (D == 256) {
+    // 32-query tiles, V tile in LDS, each workgroup forms 128 of the 256 columns
+    return launch_main_t<D, 32, CAUSAL, false, true, 1, 2>(a, st);
+  } else {
+    return launch_main_t<D, 32, CAUSAL, false, false, 2>(a, st);
   }
-  return launch_main_t<D, 32, CAUSAL, false, false, 2>(a, st);
 }
 
 template <bool WITH_DQ>
@@ -932,6 +955,8 @@ static hipError_t launch_main(const BwdArgs& a, hipStream_t st) {
       case 129: return launch_dkdv_t<64, true>(a, st);
       case 256: return launch_dkdv_t<128, false>(a, st);
       case 257: return launch_dkdv_t<128, true>(a, st);
+      case 512: return launch_dkdv_t<256, false>(a, st);
+      case 513: return launch_dkdv_t<256, true>(a, st);
       default: return hipErrorInvalidValue;
     }
   }
@@ -941,6 +966,7 @@ static hipError_t launch_pre(const BwdArgs& a, hipStream_t st) {
   switch (a.D) {
     case 64: return launch_pre_t<64>(a, st);
     case 128: return launch_pre_t<128>(a, st);
+    case 256: return launch_pre_t<256>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -331,6 +331,7 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
         case 2: return launch_dq_t<FwdCfg<128, 64, 8, 2>, 1, true>(a, st);  // eight wavefronts per workgroup
         default: return launch_dq_t<FwdCfg<128, 64, 4, 2>, 2, true>(a, st);
       }
+    case 256: return launch_dq_t<FwdCfg<256, 32, 4, 2>, 1>(a, st);  // 32-key tiles, one workgroup per CU
     default: return hipErrorInvalidValue;
   }
 }

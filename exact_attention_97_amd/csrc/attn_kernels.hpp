@@ -113,6 +113,6 @@ hipError_t launch_exp2_eval(const float* x, float* y, long n, int mode, hipStrea
 hipError_t launch_bwd_atomic(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_split(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st);
-bool bwd_supported(int D);
+bool bwd_supported(int D, bool atomic);
 
 }  // namespace attn97

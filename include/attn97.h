@@ -67,7 +67,8 @@ typedef enum {
  * the backward pass as an overhead at long sequence lengths (page
  * "FlashAttention-3 и FlashAttention-4", section "Режим 2-CTA MMA"). */
 typedef enum {
-    ATTN_BWD_ATOMIC = 0, /* one kernel per key tile; dQ summed with fp32 atomics into the workspace */
+    ATTN_BWD_ATOMIC = 0, /* one kernel per key tile; dQ summed with fp32 atomics into the workspace
+                            (D = 64 and 128 only; D = 256 returns ATTN_ERR_UNSUPPORTED)            */
     ATTN_BWD_SPLIT = 1   /* a dK/dV kernel plus a separate dQ kernel; no atomics, deterministic    */
 } attn_bwd_mode;
 
@@ -118,6 +119,9 @@ size_t attn_bwd_workspace_bytes(int B, int H, int S, int D, int causal, const at
  *        attn_bwd_workspace_bytes(...) bytes, 256-byte aligned; its contents
  *        on entry do not matter and are overwritten.  Two calls in flight at
  *        once must not share a workspace.
+ *   D = 256 runs in ATTN_BWD_SPLIT mode only (two workgroups per key tile,
+ *   each forming half of the dK / dV columns); ATTN_BWD_ATOMIC returns
+ *   ATTN_ERR_UNSUPPORTED there.
  */
 attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                      const float* LSE, void* dQ, void* dK, void* dV,

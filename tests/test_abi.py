@@ -111,6 +111,12 @@ def test_bwd_bad_options():
     assert bwd(opts=L.make_opts(bwd_mode=2)) == UNSUP
 
 
+def test_bwd_d256_modes():
+    # D = 256 runs in the split mode only; validation reaches the workspace check
+    assert bwd(D=256, opts=L.make_opts(bwd_mode="atomic")) == UNSUP
+    assert bwd(D=256, wsb=16, opts=L.make_opts(bwd_mode="split")) == WS
+
+
 def test_workspace_bytes():
     lib = L.load()
     o = L.make_opts(bwd_mode="atomic")

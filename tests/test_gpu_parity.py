@@ -116,10 +116,13 @@ def test_fwd_constant_v():
         _assert_close("O (constant V)", _np(o), np.full(o.shape, 0.75))
 
 
-@pytest.mark.parametrize("D", (64, 128))
+# the atomic mode supports D = 64 and 128; the split mode also D = 256
+BWD_D_MODES = ((64, "atomic"), (64, "split"), (128, "atomic"), (128, "split"), (256, "split"))
+
+
+@pytest.mark.parametrize("D,bwd_mode", BWD_D_MODES)
 @pytest.mark.parametrize("S", SMALL_S)
 @pytest.mark.parametrize("causal", (False, True))
-@pytest.mark.parametrize("bwd_mode", ("atomic", "split"))
 def test_bwd_small(D, S, causal, bwd_mode):
     print(f"[bwd small] D={D} S={S} causal={causal} mode={bwd_mode}", flush=True)
     q, k, v, do = make_qkvdo(1, 2, S, D, seed=200 + S + D)
@@ -166,11 +169,19 @@ def test_bwd_split_full_size():
         _check_bwd_heads(w, q, k, v, do, dq, dk, dv, causal, [(1, 9)])
 
 
-def test_bwd_d256_reported_unsupported():
-    q, k, v, do = _gpu(*make_qkvdo(1, 1, 64, 256, seed=1))
-    o, lse = L.attn_fwd(q, k, v)
+def test_bwd_d256_split_deterministic_atomic_unsupported():
+    """D = 256: the split pass (dK / dV columns in two halves, one workgroup
+    each) is bitwise repeatable; the atomic pass reports the head dim as
+    unsupported."""
+    q, k, v, do = _gpu(*make_qkvdo(1, 2, 333, 256, seed=1))
+    for causal in (False, True):
+        o, lse = L.attn_fwd(q, k, v, causal=causal)
+        a = L.attn_bwd(q, k, v, o, do, lse, causal=causal, bwd_mode="split")
+        b = L.attn_bwd(q, k, v, o, do, lse, causal=causal, bwd_mode="split")
+        for x, y, nm in zip(a, b, ("dQ", "dK", "dV")):
+            assert bool((x == y).all()), f"D=256 split {nm} not bitwise repeatable"
     with pytest.raises(L.AttnError) as e:
-        L.attn_bwd(q, k, v, o, do, lse)
+        L.attn_bwd(q, k, v, o, do, lse, bwd_mode="atomic")
     assert e.value.code == 3
 
 
@@ -232,7 +243,7 @@ def test_workload_full_size(name):
         o, lse = L.attn_fwd(qg, kg, vg, scale=w.scale, causal=causal)
         torch.cuda.synchronize()
         _check_fwd_rows(w, q, k, v, o, lse, causal)
-        if "bwd" in w.passes and w.D != 256:
+        if "bwd" in w.passes:
             dq, dk, dv = L.attn_bwd(qg, kg, vg, o, dog, lse, scale=w.scale, causal=causal)
             torch.cuda.synchronize()
             heads = [(0, 0)] if w.S > 8192 else [(0, 0), (w.B - 1, w.H - 1)]
