@@ -225,6 +225,52 @@ def splitkv_measure(torch, attn, dev, reps=20):
     return out
 
 
+def workloads_measure(torch, attn, dev, names=("fwd2k", "bwd4k", "ctx32k", "d64", "d256"), reps=10):
+    """The other named workloads (outside the headline step): the forward
+    pass and, where the workload has one, the backward pass, per causal
+    setting, each timed per call with HIP events on the launch stream (median
+    of `reps` calls after a warm-up).  TFLOP/s use the same algorithmic flops
+    as the headline (4 B H S^2 D forward, half causal; backward 2.5x)."""
+    from exact_attention_97_amd.inputs import WORKLOADS, make_workload
+
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name in names:
+        w = WORKLOADS[name]
+        q, k, v, do = (t.to(dev) for t in make_workload(w))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        ws = torch.empty(attn.bwd_workspace_bytes(w.B, w.H, w.S, w.D), dtype=torch.uint8, device=dev)
+        r = {"B": w.B, "H": w.H, "S": w.S, "D": w.D}
+        for causal in w.causal:
+            calls = {"fwd": lambda c=causal: attn.attn_fwd(q, k, v, scale=w.scale, causal=c, out=o, lse=lse)}
+            if "bwd" in w.passes:
+                calls["bwd"] = lambda c=causal: attn.attn_bwd(q, k, v, o, do, lse, scale=w.scale, causal=c,
+                                                              workspace=ws, dq=grads[0], dk=grads[1], dv=grads[2])
+            for which, fn in calls.items():
+                if which == "bwd":
+                    calls["fwd"]()  # O and LSE of this causal setting
+                warm_up(torch, fn, min_ms=200.0)
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(reps)]
+                for e0, e1 in evs:
+                    e0.record(stream)
+                    fn()
+                    e1.record(stream)
+                torch.cuda.synchronize()
+                times = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+                ms = 0.5 * (times[(reps - 1) // 2] + times[reps // 2])
+                fl = 4.0 * w.B * w.H * w.S * w.S * w.D * (0.5 if causal else 1.0) * (2.5 if which == "bwd" else 1.0)
+                tf = fl / (ms * 1e-3) / 1e12
+                r[f"{which}_{'causal' if causal else 'noncausal'}"] = {
+                    "median_ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS, 4)}
+        out[name] = r
+        del q, k, v, do, o, lse, grads, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, published
 
 
@@ -422,6 +468,7 @@ def main():
         "gemm_reference": gemm_reference(torch, dev),
         "splitkv": splitkv_measure(torch, attn, dev),
         "fp8": fp8_measure(torch, attn, dev, B, H, S, D),
+        "workloads": workloads_measure(torch, attn, dev),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(q, k, v, do)
