@@ -254,17 +254,26 @@ def workloads_measure(torch, attn, dev, names=("fwd2k", "bwd4k", "ctx32k", "d64"
                 warm_up(torch, fn, min_ms=200.0)
                 evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                        for _ in range(reps)]
+                attn.prof_reset()
+                attn.prof_enable(True)
                 for e0, e1 in evs:
                     e0.record(stream)
                     fn()
                     e1.record(stream)
                 torch.cuda.synchronize()
+                attn.prof_enable(False)
                 times = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
                 ms = 0.5 * (times[(reps - 1) // 2] + times[reps // 2])
                 fl = 4.0 * w.B * w.H * w.S * w.S * w.D * (0.5 if causal else 1.0) * (2.5 if which == "bwd" else 1.0)
                 tf = fl / (ms * 1e-3) / 1e12
+                kavg = {}
+                for kn in (("fwd",) if which == "fwd" else ("bwd_pre", "bwd_dkdv", "bwd_dq")):
+                    n, kms = attn.prof_collect(kn)
+                    if n:
+                        kavg[kn] = round(kms / n, 4)
                 r[f"{which}_{'causal' if causal else 'noncausal'}"] = {
-                    "median_ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS, 4)}
+                    "median_ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS, 4),
+                    "kernel_avg_ms": kavg}
         out[name] = r
         del q, k, v, do, o, lse, grads, ws
         torch.cuda.empty_cache()
