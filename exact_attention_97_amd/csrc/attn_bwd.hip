@@ -156,7 +156,7 @@ struct BwdOffsets {
 };
 
 // Load rows r0.. of a [S, D] bf16 matrix into a swizzled LDS tile with
-// global_load_lds; rows past S are clamped to S-1 (finite data, masked
+// buffer loads with the LDS bit (lds_dma); rows past S are clamped to S-1 (finite data, masked
 // later).  `loff` are this lane's logical element offsets inside the tile;
 // dma_row_part issues this wave's n-th 1 KiB piece only.
 template <int D, int NPW>
@@ -169,8 +169,7 @@ __device__ __forceinline__ void dma_row_part(const uint16_t* __restrict__ src, i
     const uint32_t last = (uint32_t)(S - 1 - r0);
     off = (row > last ? last : row) * D + off % D;
   }
-  __builtin_amdgcn_global_load_lds(tile + off, (__attribute__((address_space(3))) void*)(dst + 512 * (wave * NPW + n)),
-                                   16, 0, 0);
+  lds_dma<16>(tile, (uint32_t)(S - r0) * (uint32_t)(D * 2), off * 2, dst + 512 * (wave * NPW + n));
 }
 
 template <int D, int NPW>
@@ -514,9 +513,9 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
     dma_rows<D, DMA_Q>(Qh, q0, BQ, S, sm.Qs[buf], wave, of.dmaq);
     dma_rows<D, DMA_Q>(dOh, q0, BQ, S, sm.dOs[buf], wave, of.dmaq);
     if (wave < 2) {
-      const float* src = (wave == 0 ? LSEh : dlth) + min(q0 + lane, S - 1);
+      const float* src = wave == 0 ? LSEh : dlth;
       float* dst = (wave == 0) ? sm.lse[buf] : sm.dlt[buf];
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+      lds_dma<4>(src, (uint32_t)S * 4u, (uint32_t)min(q0 + lane, S - 1) * 4u, dst);
     }
   };
 
@@ -701,9 +700,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     } else if (p < 2 * DMA_Q) {
       dma_row_part<D, DMA_Q>(dOh, q0, BQ, S, dd, wave, of.dmaq, p - DMA_Q);
     } else if (p == 2 * DMA_Q && wave < 2) {
-      const float* src = (wave == 0 ? NLh : DLh) + min(q0 + lane, S - 1);
+      const float* src = wave == 0 ? NLh : DLh;
       float* dst = (wave == 0) ? (set ? nl1 : nl0) : (set ? dl1 : dl0);
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+      lds_dma<4>(src, (uint32_t)S * 4u, (uint32_t)min(q0 + lane, S - 1) * 4u, dst);
     }
   };
 

@@ -290,7 +290,7 @@ __global__ __launch_bounds__(256) void fp8_v_quant_kernel(const uint16_t* __rest
 // ---------------------------------------------------------------------------
 // Forward.  One workgroup of four wavefronts per 128 queries of one head;
 // 64-key tiles of K (64 rows x 128 B) and V^T (128 rows x 64 B) stream
-// through two LDS buffers each with global_load_lds.  16-byte chunks are
+// through two LDS buffers each with LDS-direct buffer loads.  16-byte chunks are
 // XOR-swizzled (K: chunk ^ ((key >> 1) & 7); V^T: chunk ^ ((d >> 2) & 3)) so
 // that each 16-lane group of a 128-bit operand read hits 16 distinct bank
 // groups.
@@ -403,19 +403,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_fp8_kernel(Fp8Buf f, uint
   Fp8Wave of;
   of.init<NCH>(wave, lane, Sp);
 
-  auto dma = [&](const uint8_t* src, uint8_t* dst, const uint32_t (&off)[2]) {
+  // extent: bytes of the head's array from the tile start on
+  auto dma = [&](const uint8_t* src, uint32_t extent, uint8_t* dst, const uint32_t (&off)[2]) {
 #pragma unroll
-    for (int n = 0; n < NCH; ++n)
-      __builtin_amdgcn_global_load_lds(src + off[n],
-                                       (__attribute__((address_space(3))) void*)(dst + 1024 * (NCH * wave + n)), 16,
-                                       0, 0);
+    for (int n = 0; n < NCH; ++n) lds_dma<16>(src, extent, off[n], dst + 1024 * (NCH * wave + n));
   };
   // iteration j issues K(j + 2) and V(j + 1) into the buffers the barrier of
   // iteration j - 1 freed; it reads K(j + 1) (scores of the next tile) and V(j)
+  const uint32_t head_bytes = (uint32_t)Sp * FD;
   auto issue = [&](int j, auto P) {  // P = j & 1
     constexpr int par = decltype(P)::value;
-    if (j + 2 < nkt) dma(Kh + (size_t)(j + 2) * FBC * FD, par ? Kb1 : Kb0, of.kdma);
-    if (j + 1 >= 0 && j + 1 < nkt) dma(Vh + (size_t)(j + 1) * FBC, par ? Vb0 : Vb1, of.vdma);
+    if (j + 2 < nkt)
+      dma(Kh + (size_t)(j + 2) * FBC * FD, head_bytes - (uint32_t)((j + 2) * FBC * FD), par ? Kb1 : Kb0, of.kdma);
+    if (j + 1 >= 0 && j + 1 < nkt)
+      dma(Vh + (size_t)(j + 1) * FBC, head_bytes - (uint32_t)((j + 1) * FBC), par ? Vb0 : Vb1, of.vdma);
   };
   auto scores = [&](const uint8_t* kb_, f32x16 (&s)[2]) {
 #pragma unroll

@@ -27,7 +27,7 @@
 //   scores of one query row sit in one lane pair (l, l+32): the row max and
 //   row sum are in-lane and the rescale of the output accumulator is a
 //   per-lane scalar.
-// * K and V tiles go from HBM straight into LDS with global_load_lds (16
+// * K and V tiles go from HBM straight into LDS with LDS-direct buffer loads (16
 //   bytes per lane, no register staging), row-major with an XOR swizzle of
 //   the 16-byte chunks chosen so that both the K operand reads
 //   (ds_read_b128, 16 rows at one chunk) and the V operand reads

@@ -1,5 +1,5 @@
 // kv_stream.hpp - streaming K/V (or any [S, D] bf16 matrix) tiles through
-// swizzled LDS buffers with global_load_lds, and the per-lane LDS offsets of
+// swizzled LDS buffers with LDS-direct buffer loads, and the per-lane LDS offsets of
 // the MFMA operands read from those tiles.  Used by the forward kernel and
 // by the dQ kernel of the split backward pass, which walk the key sequence
 // the same way.
@@ -55,8 +55,7 @@ __device__ __forceinline__ void dma_tile_part(const uint16_t* __restrict__ src, 
     const uint32_t last = (uint32_t)(S - 1 - k0);
     off = (row > last ? last : row) * D + off % D;
   }
-  __builtin_amdgcn_global_load_lds(tile + off, (__attribute__((address_space(3))) void*)(dst + 512 * (wave * NPW + n)),
-                                   16, 0, 0);
+  lds_dma<16>(tile, (uint32_t)(S - k0) * (uint32_t)(D * 2), off * 2, dst + 512 * (wave * NPW + n));
 }
 
 template <class Cfg>

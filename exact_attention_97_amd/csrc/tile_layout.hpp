@@ -1,5 +1,5 @@
 // tile_layout.hpp - swizzled row-major LDS tiles shared by the attention
-// kernels: 16-byte chunk placement for tiles filled by global_load_lds and
+// kernels: 16-byte chunk placement for tiles filled by LDS-direct loads and
 // read with ds_read_b128 (16 rows at one chunk) and ds_read_b64_tr_b16
 // (4 rows x 32 bytes), plus the wait helper for those loads.
 #pragma once
@@ -42,6 +42,37 @@ __device__ __forceinline__ void unswz_chunk(int P, int& row, int& c) {
     const int f = ((row & 3) << 2) | ((row >> 2) & 3);
     c = (P % (D / 8)) ^ f;
   }
+}
+
+// Word 3 of a raw buffer resource (stride 0, 32-bit data format, no
+// thread-id swizzle), as used for the gfx9-family buffer instructions.
+constexpr int kBufRsrcWord3 = 0x00020000;
+
+// Copy BYTES (16 or 4) per lane from global memory straight into LDS: lane l
+// reads base + voff (bytes) and writes lds + BYTES * l (lds is wave-uniform).
+// It is a buffer load with the LDS bit over the resource [base, base +
+// extent), not the FLAT-encoded global_load_lds.  With a FLAT LDS load in
+// flight the compiler has to assume it may complete out of order on the LDS
+// counter and makes every later LDS read wait for all outstanding ones
+// (lgkmcnt(0)); buffer loads count on the vector-memory counter only, so the
+// MFMA operand reads keep exact partial waits and stay ahead of the MFMAs.
+// Offsets at or past `extent` read zero.
+// base and extent must be the same in every lane of the wavefront; they are
+// read from the first active lane (a resource the compiler cannot prove
+// uniform would otherwise become a loop over the distinct values).
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(const void* base, uint32_t extent, uint32_t voff, void* lds) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  const int ue = __builtin_amdgcn_readfirstlane((int)extent);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, ue, kBufRsrcWord3);
+  static_assert(BYTES == 16 || BYTES == 4, "16 or 4 bytes per lane");
+  if constexpr (BYTES == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
 }
 
 // s_waitcnt with vmcnt <= N, lgkmcnt = 0, expcnt unconstrained (gfx9 encoding).
