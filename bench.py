@@ -343,6 +343,9 @@ def main():
     ap.add_argument("--tau", type=float, default=8.0)
     ap.add_argument("--bwd-mode", default="split", choices=["split", "atomic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the side measurements (GEMM reference, split-KV, FP8, other workloads), "
+                         "e.g. for a kernel trace of the headline step alone")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -474,11 +477,12 @@ def main():
         "kernels_noncausal_avg_ms": {k2: round(v2["avg_ms"], 4) for k2, v2 in kern.items()},
         "roofline": roofline,
         "device_peak": dpeak,
-        "gemm_reference": gemm_reference(torch, dev),
-        "splitkv": splitkv_measure(torch, attn, dev),
-        "fp8": fp8_measure(torch, attn, dev, B, H, S, D),
-        "workloads": workloads_measure(torch, attn, dev),
     }
+    if not args.headline_only:
+        result["gemm_reference"] = gemm_reference(torch, dev)
+        result["splitkv"] = splitkv_measure(torch, attn, dev)
+        result["fp8"] = fp8_measure(torch, attn, dev, B, H, S, D)
+        result["workloads"] = workloads_measure(torch, attn, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(q, k, v, do)
     print(json.dumps(result), flush=True)
