@@ -110,7 +110,14 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* p0, const uint16_t*
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Per-lane LDS offsets (elements) fixed over the whole kernel.
+// p advanced by `bytes` (the per-lane offsets below are byte offsets, so an
+// LDS address is the offset plus the tile's base as the instruction's
+// immediate, with no shift per use).
+__device__ __forceinline__ const uint16_t* at_bytes(const uint16_t* p, uint32_t bytes) {
+  return reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(p) + bytes);
+}
+
+// Per-lane LDS and DMA offsets (bytes) fixed over the whole kernel.
 template <int D, class Cfg>
 struct BwdOffsets {
   static constexpr int NKS = Cfg::NKS, NDB = Cfg::NDB;
@@ -130,46 +137,47 @@ struct BwdOffsets {
   __device__ __forceinline__ void init(int wave, int lane, int d0 = 0) {
     const int hh = lane >> 5, c32 = lane & 31, i = lane & 15, g16 = lane >> 4;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) arow[ks] = swz_chunk<D>(c32, 2 * ks + hh) * 8;
+    for (int ks = 0; ks < NKS; ++ks) arow[ks] = swz_chunk<D>(c32, 2 * ks + hh) * 16;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const int d = d0 + 32 * db + 16 * (g16 & 1) + 4 * (i & 3);
 #pragma unroll
       for (int r2 = 0; r2 < 2; ++r2) {
-        trq[db][r2] = swz_chunk<D>(8 * r2 + 4 * (g16 >> 1) + (i >> 2), d >> 3) * 8 + (d & 7);
-        trk[db][r2] = swz_chunk<D>(8 * (g16 >> 1) + 4 * r2 + (i >> 2), d >> 3) * 8 + (d & 7);
+        trq[db][r2] = (swz_chunk<D>(8 * r2 + 4 * (g16 >> 1) + (i >> 2), d >> 3) * 8 + (d & 7)) * 2;
+        trk[db][r2] = (swz_chunk<D>(8 * (g16 >> 1) + 4 * r2 + (i >> 2), d >> 3) * 8 + (d & 7)) * 2;
       }
     }
 #pragma unroll
     for (int n = 0; n < Cfg::DMA_Q; ++n) {
       int row, c;
       unswz_chunk<D>(64 * (wave * Cfg::DMA_Q + n) + lane, row, c);
-      dmaq[n] = (uint32_t)(row * D + 8 * c);
+      dmaq[n] = (uint32_t)(row * D + 8 * c) * 2;
     }
 #pragma unroll
     for (int n = 0; n < Cfg::DMA_K; ++n) {
       int row, c;
       unswz_chunk<D>(64 * (wave * Cfg::DMA_K + n) + lane, row, c);
-      dmak[n] = (uint32_t)(row * D + 8 * c);
+      dmak[n] = (uint32_t)(row * D + 8 * c) * 2;
     }
   }
 };
 
 // Load rows r0.. of a [S, D] bf16 matrix into a swizzled LDS tile with
-// buffer loads with the LDS bit (lds_dma); rows past S are clamped to S-1 (finite data, masked
-// later).  `loff` are this lane's logical element offsets inside the tile;
-// dma_row_part issues this wave's n-th 1 KiB piece only.
-template <int D, int NPW>
+// buffer loads with the LDS bit (lds_dma); rows past S are clamped to S-1
+// (finite data, masked later).  `loff` are this lane's logical byte offsets
+// inside the tile; dma_row_part issues this wave's n-th 1 KiB piece only.
+// CLAMP = false: the caller guarantees r0 + rows <= S (no clamp code).
+template <int D, int NPW, bool CLAMP = true>
 __device__ __forceinline__ void dma_row_part(const uint16_t* __restrict__ src, int r0, int rows, int S, uint16_t* dst,
                                              int wave, const uint32_t (&loff)[NPW], int n) {
   const uint16_t* tile = src + (size_t)r0 * D;
-  uint32_t off = loff[n];
-  if (r0 + rows > S) {
-    const uint32_t row = off / D;
+  uint32_t off = loff[n];  // bytes
+  if (CLAMP && r0 + rows > S) {
+    const uint32_t row = off / (2 * D);
     const uint32_t last = (uint32_t)(S - 1 - r0);
-    off = (row > last ? last : row) * D + off % D;
+    off = (row > last ? last : row) * (2 * D) + off % (2 * D);
   }
-  lds_dma<16>(tile, (uint32_t)(S - r0) * (uint32_t)(D * 2), off * 2, dst + 512 * (wave * NPW + n));
+  lds_dma<16>(tile, (uint32_t)(S - r0) * (uint32_t)(D * 2), off, dst + 512 * (wave * NPW + n));
 }
 
 template <int D, int NPW>
@@ -210,11 +218,11 @@ __device__ __forceinline__ void bwd_tile(BwdSmem<Cfg, WRITE_DS, VLDS>& sm, int b
     f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      sacc = mfma32(lds_frag(Qb + of.arow[ks] + 32 * qb * CPR * 8), kreg[ks], sacc);
+      sacc = mfma32(lds_frag(at_bytes(Qb, of.arow[ks]) + 32 * qb * CPR * 8), kreg[ks], sacc);
       if constexpr (VLDS)
-        dpacc = mfma32(lds_frag(dOb + of.arow[ks] + 32 * qb * CPR * 8), lds_frag(Vw + of.arow[ks]), dpacc);
+        dpacc = mfma32(lds_frag(at_bytes(dOb, of.arow[ks]) + 32 * qb * CPR * 8), lds_frag(at_bytes(Vw, of.arow[ks])), dpacc);
       else
-        dpacc = mfma32(lds_frag(dOb + of.arow[ks] + 32 * qb * CPR * 8), vreg[ks], dpacc);
+        dpacc = mfma32(lds_frag(at_bytes(dOb, of.arow[ks]) + 32 * qb * CPR * 8), vreg[ks], dpacc);
     }
     // two reduction steps of operands read ahead of the MFMAs (Q, dO and,
     // with VLDS, V fragments: 2 or 3 LDS reads per step of two MFMAs)
@@ -281,8 +289,8 @@ __device__ __forceinline__ void bwd_tile(BwdSmem<Cfg, WRITE_DS, VLDS>& sm, int b
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const int o = 16 * t * CPR * 8;
-      dv[db] = mfma32(pb[t], tr_operand(dOb + of.trq[db][0] + o, dOb + of.trq[db][1] + o), dv[db]);
-      dk[db] = mfma32(dsb[t], tr_operand(Qb + of.trq[db][0] + o, Qb + of.trq[db][1] + o), dk[db]);
+      dv[db] = mfma32(pb[t], tr_operand(at_bytes(dOb, of.trq[db][0]) + o, at_bytes(dOb, of.trq[db][1]) + o), dv[db]);
+      dk[db] = mfma32(dsb[t], tr_operand(at_bytes(Qb, of.trq[db][0]) + o, at_bytes(Qb, of.trq[db][1]) + o), dk[db]);
     }
   }
   __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
@@ -341,15 +349,15 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* Qb, const uint16_t* dO
     mlo = CAUSAL ? key - mt : 0;
     mhi = key < S ? S - mt : -1;
   }
-  auto qfrag = [&](int qb, int ks) { return lds_frag(Qb + of.arow[ks] + 32 * qb * CPR * 8); };
-  auto dofrag = [&](int qb, int ks) { return lds_frag(dOb + of.arow[ks] + 32 * qb * CPR * 8); };
+  auto qfrag = [&](int qb, int ks) { return lds_frag(at_bytes(Qb, of.arow[ks]) + 32 * qb * CPR * 8); };
+  auto dofrag = [&](int qb, int ks) { return lds_frag(at_bytes(dOb, of.arow[ks]) + 32 * qb * CPR * 8); };
   auto trdo = [&](int t, int db) {
     const int o = 16 * t * CPR * 8;
-    return tr_operand(dOb + of.trq[db][0] + o, dOb + of.trq[db][1] + o);
+    return tr_operand(at_bytes(dOb, of.trq[db][0]) + o, at_bytes(dOb, of.trq[db][1]) + o);
   };
   auto trq = [&](int t, int db) {
     const int o = 16 * t * CPR * 8;
-    return tr_operand(Qb + of.trq[db][0] + o, Qb + of.trq[db][1] + o);
+    return tr_operand(at_bytes(Qb, of.trq[db][0]) + o, at_bytes(Qb, of.trq[db][1]) + o);
   };
 
   f32x16 s0 = f32x16{}, dp0 = f32x16{}, s1 = f32x16{}, dp1 = f32x16{};
@@ -590,9 +598,9 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
       for (int t = 0; t < BK / 16; t += 2) {
         const int o0 = 16 * t * CPR * 8, o1 = 16 * (t + 1) * CPR * 8;
         acc0 = mfma32(lds_frag(&sm.dSs[(32 * qb + c32) * SRS + 16 * t + 8 * hh]),
-                      tr_operand(sm.Ks + of.trk[db][0] + o0, sm.Ks + of.trk[db][1] + o0), acc0);
+                      tr_operand(at_bytes(sm.Ks, of.trk[db][0]) + o0, at_bytes(sm.Ks, of.trk[db][1]) + o0), acc0);
         acc1 = mfma32(lds_frag(&sm.dSs[(32 * qb + c32) * SRS + 16 * t + 16 + 8 * hh]),
-                      tr_operand(sm.Ks + of.trk[db][0] + o1, sm.Ks + of.trk[db][1] + o1), acc1);
+                      tr_operand(at_bytes(sm.Ks, of.trk[db][0]) + o1, at_bytes(sm.Ks, of.trk[db][1]) + o1), acc1);
       }
       const uint32_t off0 = (uint32_t)(q0 + 32 * qb + 4 * hh) * D + 32 * db + c32;
       if (q0 + BQ <= S) {
@@ -679,7 +687,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const float* DLh = delta + (size_t)bh * S;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // Wavefront index.  Read from the first lane (uniform by construction) it
+  // makes the LDS-DMA destinations scalar values, which saves about 20
+  // readfirstlanes per pair of tiles; the causal kernels keep the plain form,
+  // with which their register allocation stays below the spill point.
+  const int wave = CAUSAL ? (tid >> 6) : __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int hh = lane >> 5;
   const int c32 = lane & 31;
@@ -696,13 +708,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     uint16_t* dd = set ? dOs1 : dOs0;
     const int q0 = qt * BQ;
     if (p < DMA_Q) {
-      dma_row_part<D, DMA_Q>(Qh, q0, BQ, S, qd, wave, of.dmaq, p);
+      dma_row_part<D, DMA_Q, RAGGED>(Qh, q0, BQ, S, qd, wave, of.dmaq, p);
     } else if (p < 2 * DMA_Q) {
-      dma_row_part<D, DMA_Q>(dOh, q0, BQ, S, dd, wave, of.dmaq, p - DMA_Q);
+      dma_row_part<D, DMA_Q, RAGGED>(dOh, q0, BQ, S, dd, wave, of.dmaq, p - DMA_Q);
     } else if (p == 2 * DMA_Q && wave < 2) {
       const float* src = wave == 0 ? NLh : DLh;
       float* dst = (wave == 0) ? (set ? nl1 : nl0) : (set ? dl1 : dl0);
-      lds_dma<4>(src, (uint32_t)S * 4u, (uint32_t)min(q0 + lane, S - 1) * 4u, dst);
+      // without RAGGED, S is a multiple of 128 and q0 + 63 < S
+      lds_dma<4>(src, (uint32_t)S * 4u, (uint32_t)(RAGGED ? min(q0 + lane, S - 1) : q0 + lane) * 4u, dst);
     }
   };
 
