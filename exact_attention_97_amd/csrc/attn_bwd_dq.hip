@@ -216,8 +216,14 @@ __global__ __launch_bounds__(64 * Cfg::NW, OCC) void bwd_dq_kernel(
   constexpr int D = Cfg::D, BC = Cfg::BC, BR = Cfg::BR, NKS = Cfg::NKS, NDB = Cfg::NDB;
   constexpr int TILE = Cfg::TILE_BYTES / 2;
 
-  __shared__ __attribute__((aligned(1024))) uint16_t Kb[2][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vb[2][TILE];
+  // one __shared__ array per buffer; the loop below is unrolled by two, so
+  // every buffer a tile reads or loads into is a compile-time constant (LDS
+  // addresses become instruction immediates, and the compiler can see that
+  // the next tile's loads do not alias this tile's reads)
+  __shared__ __attribute__((aligned(1024))) uint16_t Kb0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t Kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vb0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vb1[TILE];
 
   // heaviest causal query tiles first; one head's tiles on one XCD when B*H % 8 == 0
   const int id = blockIdx.x;
@@ -266,26 +272,41 @@ __global__ __launch_bounds__(64 * Cfg::NW, OCC) void bwd_dq_kernel(
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16{};
 
-  dma_tile<Cfg>(Kh, 0, S, Kb[0], wave, of.dma);
-  dma_tile<Cfg>(Vh, 0, S, Vb[0], wave, of.dma);
+  dma_tile<Cfg>(Kh, 0, S, Kb0, wave, of.dma);
+  dma_tile<Cfg>(Vh, 0, S, Vb0, wave, of.dma);
   wait_vm_lds<0>();
   barrier_keep_loads();
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nkt) {  // the other buffer was last read in the previous iteration
-      dma_tile<Cfg>(Kh, (kt + 1) * BC, S, Kb[buf ^ 1], wave, of.dma);
-      dma_tile<Cfg>(Vh, (kt + 1) * BC, S, Vb[buf ^ 1], wave, of.dma);
+  // P = kt & 1: tile kt sits in buffer P, tile kt + 1 goes to the other one
+  // (last read in the previous iteration)
+  auto iteration = [&](int kt, auto P) {
+    constexpr int par = decltype(P)::value;
+    const uint16_t* kc = par ? Kb1 : Kb0;
+    const uint16_t* vc = par ? Vb1 : Vb0;
+    if (kt + 1 < nkt) {
+      dma_tile<Cfg>(Kh, (kt + 1) * BC, S, par ? Kb0 : Kb1, wave, of.dma);
+      dma_tile<Cfg>(Vh, (kt + 1) * BC, S, par ? Vb0 : Vb1, wave, of.dma);
     }
     __builtin_amdgcn_sched_barrier(0);
+    // The offsets pass through an empty asm at each tile: the compiler then
+    // cannot precompute both buffers' addresses and hold them over the loop
+    // (it adds the constant buffer base as the instruction's immediate).
+#pragma unroll
+    for (int ks = 0; ks < Cfg::NKS; ++ks) asm volatile("" : "+v"(of.kfrag[ks]));
+#pragma unroll
+    for (int db = 0; db < Cfg::NDB; ++db) asm volatile("" : "+v"(of.vfrag[db][0]), "+v"(of.vfrag[db][1]));
     if (kt < nkt_w) {
       if (kt < nfull)
-        W::template step<false>(Kb[buf], Vb[buf], of, qreg, doreg, dqacc, C, nlse2, dlt, kt * BC, lim, hh);
+        W::template step<false>(kc, vc, of, qreg, doreg, dqacc, C, nlse2, dlt, kt * BC, lim, hh);
       else
-        W::template step<true>(Kb[buf], Vb[buf], of, qreg, doreg, dqacc, C, nlse2, dlt, kt * BC, lim, hh);
+        W::template step<true>(kc, vc, of, qreg, doreg, dqacc, C, nlse2, dlt, kt * BC, lim, hh);
     }
     wait_vm_lds<0>();
     barrier_keep_loads();
+  };
+  for (int kt = 0; kt < nkt; kt += 2) {
+    iteration(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < nkt) iteration(kt + 1, std::integral_constant<int, 1>{});
   }
 
   // dQ = scale * acc: lane holds column qrow, rows d = 32 db + 8 g + 4 h + 0..3
