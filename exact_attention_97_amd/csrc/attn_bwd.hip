@@ -180,11 +180,11 @@ __device__ __forceinline__ void dma_row_part(const uint16_t* __restrict__ src, i
   lds_dma<16>(tile, (uint32_t)(S - r0) * (uint32_t)(D * 2), off, dst + 512 * (wave * NPW + n));
 }
 
-template <int D, int NPW>
+template <int D, int NPW, bool CLAMP = true>
 __device__ __forceinline__ void dma_rows(const uint16_t* __restrict__ src, int r0, int rows, int S, uint16_t* dst,
                                          int wave, const uint32_t (&loff)[NPW]) {
 #pragma unroll
-  for (int n = 0; n < NPW; ++n) dma_row_part<D, NPW>(src, r0, rows, S, dst, wave, loff, n);
+  for (int n = 0; n < NPW; ++n) dma_row_part<D, NPW, CLAMP>(src, r0, rows, S, dst, wave, loff, n);
 }
 
 // One query tile against one wavefront's 32 keys: S = Q K^T and dP = dO V^T,
@@ -470,7 +470,9 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* Qb, const uint16_t* dO
 // workgroups per key tile; each recomputes P and dS over the full head dim
 // and accumulates D / DSPLIT columns (D = 256: the full-width accumulators
 // do not fit the register file next to the K / V operands).
-template <int D, int BQ_, bool CAUSAL, bool WITH_DQ, bool VLDS, int OCC, int DSPLIT = 1>
+// RAGGED = false (split mode, S a multiple of BQ): no query tile is partial,
+// so the tile loads carry no clamp arithmetic.
+template <int D, int BQ_, bool CAUSAL, bool WITH_DQ, bool VLDS, int OCC, int DSPLIT = 1, bool RAGGED = true>
 __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ nlse2, const float* __restrict__ delta,
@@ -518,8 +520,8 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
   // floats each, 4 bytes per lane, at least BQ of them used) by waves 0 / 1
   auto issue = [&](int qt, int buf) {
     const int q0 = qt * BQ;
-    dma_rows<D, DMA_Q>(Qh, q0, BQ, S, sm.Qs[buf], wave, of.dmaq);
-    dma_rows<D, DMA_Q>(dOh, q0, BQ, S, sm.dOs[buf], wave, of.dmaq);
+    dma_rows<D, DMA_Q, RAGGED>(Qh, q0, BQ, S, sm.Qs[buf], wave, of.dmaq);
+    dma_rows<D, DMA_Q, RAGGED>(dOh, q0, BQ, S, sm.dOs[buf], wave, of.dmaq);
     if (wave < 2) {
       const float* src = wave == 0 ? LSEh : dlth;
       float* dst = (wave == 0) ? sm.lse[buf] : sm.dlt[buf];
@@ -544,6 +546,18 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
       const uint32_t off = (uint32_t)keyc * D + 16 * ks + 8 * hh;
       kreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(Kh + off));
       if constexpr (!VLDS) vreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(Vh + off));
+    }
+    // At D = 256 the kernel needs more than the 256 arch VGPRs.  K is read
+    // only as an MFMA operand, which gfx950 takes from AGPRs, so its 64
+    // registers are placed there once; otherwise the allocator moves values
+    // between VGPRs and AGPRs on every tile.
+    if constexpr (D == 256) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        u32x4 kk = __builtin_bit_cast(u32x4, kreg[ks]);
+        asm volatile("" : "+a"(kk));
+        kreg[ks] = __builtin_bit_cast(bf16x8, kk);
+      }
     }
   }
   const uint16_t* Vw = nullptr;  // this wave's 32 rows of the V tile
@@ -900,13 +914,14 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict
 // dK / dV columns there.
 bool bwd_supported(int D, bool atomic) { return D == 64 || D == 128 || (D == 256 && !atomic); }
 
-template <int D, int BQ, bool CAUSAL, bool WITH_DQ, bool VLDS, int OCC, int DSPLIT = 1>
+template <int D, int BQ, bool CAUSAL, bool WITH_DQ, bool VLDS, int OCC, int DSPLIT = 1, bool RAGGED = true>
 static hipError_t launch_main_t(const BwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   const int nkt = (a.S + BwdCfg<D, BQ>::BK - 1) / BwdCfg<D, BQ>::BK;
   const int kid = WITH_DQ ? KID_BWD_MAIN : KID_BWD_DKDV;
   prof_begin(kid, st);
-  hipLaunchKernelGGL((bwd_main_kernel<D, BQ, CAUSAL, WITH_DQ, VLDS, OCC, DSPLIT>), dim3(nkt * BH * DSPLIT), dim3(256),
+  hipLaunchKernelGGL((bwd_main_kernel<D, BQ, CAUSAL, WITH_DQ, VLDS, OCC, DSPLIT, RAGGED>), dim3(nkt * BH * DSPLIT),
+                     dim3(256),
                      0, st,
                      (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                      (const uint16_t*)a.dO, a.nlse2, a.delta, a.dq32, (uint16_t*)a.dK,
@@ -945,8 +960,10 @@ static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
     return launch_dkdv_pipe_t<CAUSAL>(a, st);
   } else if constexpr (D == 256) {
     // 32-query tiles, V tile in LDS, each workgroup forms 128 of the 256 columns
-    return launch_main_t<D, 32, CAUSAL, false, true, 1, 2>(a, st);
+    return (a.S % 32 == 0) ? launch_main_t<D, 32, CAUSAL, false, true, 1, 2, false>(a, st)
+                           : launch_main_t<D, 32, CAUSAL, false, true, 1, 2, true>(a, st);
   } else {
+    // (the clamp-free variant measured no faster here: non-causal -0.5 %, causal +2 %)
     return launch_main_t<D, 32, CAUSAL, false, false, 2>(a, st);
   }
 }
