@@ -254,6 +254,19 @@ __global__ __launch_bounds__(64 * Cfg::NW, OCC) void bwd_dq_kernel(
       qreg[ks] = as_bf16x8(qs[2 * ks + hh]);
       doreg[ks] = as_bf16x8(ds[2 * ks + hh]);
     }
+    // At D = 256 the kernel needs more than the 256 arch VGPRs.  Q and dO are
+    // read only as MFMA operands, which gfx950 takes from AGPRs, so their 128
+    // registers are placed there once; otherwise the allocator moves values
+    // between VGPRs and AGPRs on every tile.
+    if constexpr (D == 256) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        u32x4 a = __builtin_bit_cast(u32x4, qreg[ks]), b = __builtin_bit_cast(u32x4, doreg[ks]);
+        asm volatile("" : "+a"(a), "+a"(b));
+        qreg[ks] = __builtin_bit_cast(bf16x8, a);
+        doreg[ks] = __builtin_bit_cast(bf16x8, b);
+      }
+    }
   }
   const float nlse2 = nlse2v[(size_t)bh * S + qc];  // -LSE log2(e)
   const float dlt = delta[(size_t)bh * S + qc];

@@ -311,6 +311,10 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
     for (int ks = 0; ks < NKS; ++ks) {
       u32x4 v = src[2 * ks + hh];
       v ^= qsign;
+      // At D = 256 the kernel needs more than the 256 arch VGPRs; Q is read
+      // only as an MFMA operand, which gfx950 takes from AGPRs, so it is
+      // placed there once instead of being moved on every tile.
+      if constexpr (D == 256) asm volatile("" : "+a"(v));
       qreg[ks] = as_bf16x8(v);
     }
   }
