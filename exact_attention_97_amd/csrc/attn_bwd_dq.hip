@@ -358,7 +358,7 @@ static int dq_variant() { return kernel_variant(VAR_DQ); }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
   switch (a.D) {
-    case 64: return launch_dq_t<FwdCfg<64, 64, 4, 2>, 1>(a, st);
+    case 64: return launch_dq_t<FwdCfg<64, 64, 4, 2>, 2>(a, st);  // two workgroups (eight wavefronts) per CU
     case 128:
       switch (dq_variant()) {
         case 1: return launch_dq_t<FwdCfg<128, 32, 4, 2>, 2>(a, st);        // 32-key tiles, one block per step
