@@ -706,6 +706,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   // readfirstlanes per pair of tiles; the causal kernels keep the plain form,
   // with which their register allocation stays below the spill point.
   const int wave = CAUSAL ? (tid >> 6) : __builtin_amdgcn_readfirstlane(tid >> 6);
+  // the index read from the first lane in every kernel, for the LDS-DMA
+  // destinations (which must be uniform) only
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int hh = lane >> 5;
   const int c32 = lane & 31;
@@ -722,9 +725,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     uint16_t* dd = set ? dOs1 : dOs0;
     const int q0 = qt * BQ;
     if (p < DMA_Q) {
-      dma_row_part<D, DMA_Q, RAGGED>(Qh, q0, BQ, S, qd, wave, of.dmaq, p);
+      dma_row_part<D, DMA_Q, RAGGED>(Qh, q0, BQ, S, qd, wave_u, of.dmaq, p);
     } else if (p < 2 * DMA_Q) {
-      dma_row_part<D, DMA_Q, RAGGED>(dOh, q0, BQ, S, dd, wave, of.dmaq, p - DMA_Q);
+      dma_row_part<D, DMA_Q, RAGGED>(dOh, q0, BQ, S, dd, wave_u, of.dmaq, p - DMA_Q);
     } else if (p == 2 * DMA_Q && wave < 2) {
       const float* src = wave == 0 ? NLh : DLh;
       float* dst = (wave == 0) ? (set ? nl1 : nl0) : (set ? dl1 : dl0);

@@ -237,6 +237,10 @@ __global__ __launch_bounds__(64 * Cfg::NW, OCC) void bwd_dq_kernel(
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
+  // the same index read from the first lane, for the LDS-DMA destinations
+  // only (they must be uniform: with it they are scalar arithmetic, without
+  // it every tile load pays a readfirstlane)
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int lane = tid & 63;
   const int hh = lane >> 5;
   const int c32 = lane & 31;
@@ -285,8 +289,8 @@ __global__ __launch_bounds__(64 * Cfg::NW, OCC) void bwd_dq_kernel(
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16{};
 
-  dma_tile<Cfg>(Kh, 0, S, Kb0, wave, of.dma);
-  dma_tile<Cfg>(Vh, 0, S, Vb0, wave, of.dma);
+  dma_tile<Cfg>(Kh, 0, S, Kb0, wave_u, of.dma);
+  dma_tile<Cfg>(Vh, 0, S, Vb0, wave_u, of.dma);
   wait_vm_lds<0>();
   barrier_keep_loads();
 
@@ -297,8 +301,8 @@ __global__ __launch_bounds__(64 * Cfg::NW, OCC) void bwd_dq_kernel(
     const uint16_t* kc = par ? Kb1 : Kb0;
     const uint16_t* vc = par ? Vb1 : Vb0;
     if (kt + 1 < nkt) {
-      dma_tile<Cfg>(Kh, (kt + 1) * BC, S, par ? Kb0 : Kb1, wave, of.dma);
-      dma_tile<Cfg>(Vh, (kt + 1) * BC, S, par ? Vb0 : Vb1, wave, of.dma);
+      dma_tile<Cfg>(Kh, (kt + 1) * BC, S, par ? Kb0 : Kb1, wave_u, of.dma);
+      dma_tile<Cfg>(Vh, (kt + 1) * BC, S, par ? Vb0 : Vb1, wave_u, of.dma);
     }
     __builtin_amdgcn_sched_barrier(0);
     // The offsets pass through an empty asm at each tile: the compiler then

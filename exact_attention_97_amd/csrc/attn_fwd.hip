@@ -297,6 +297,10 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
+  // the same index read from the first lane, for the LDS-DMA destinations
+  // only (they must be uniform: with it they are scalar arithmetic, without
+  // it every tile load pays a readfirstlane)
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int lane = tid & 63;
   const int hh = lane >> 5;
   const int c32 = lane & 31;
@@ -365,11 +369,11 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
   auto issue = [&](int j, int ki, int vi) {  // loads of "iteration" j; returns the number of ops issued
     int n = 0;
     if (j + NBUF < nkt) {
-      dma_tile<Cfg>(Kh, kb + (j + NBUF) * BC, Sk, kbuf(ki), wave, of.dma);
+      dma_tile<Cfg>(Kh, kb + (j + NBUF) * BC, Sk, kbuf(ki), wave_u, of.dma);
       n += DPW;
     }
     if (j + NBUF - 1 >= 0 && j + NBUF - 1 < nkt) {
-      dma_tile<Cfg>(Vh, kb + (j + NBUF - 1) * BC, Sk, vbuf(vi), wave, of.dma);
+      dma_tile<Cfg>(Vh, kb + (j + NBUF - 1) * BC, Sk, vbuf(vi), wave_u, of.dma);
       n += DPW;
     }
     return n;
