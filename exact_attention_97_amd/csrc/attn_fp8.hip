@@ -365,6 +365,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_fp8_kernel(Fp8Buf f, uint
   const int q0 = qt * BR;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
+  // the same index read from the first lane, for the LDS-DMA destinations only
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int lane = tid & 63;
   const int hh = lane >> 5;
   const int c32 = lane & 31;
@@ -406,7 +408,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_fp8_kernel(Fp8Buf f, uint
   // extent: bytes of the head's array from the tile start on
   auto dma = [&](const uint8_t* src, uint32_t extent, uint8_t* dst, const uint32_t (&off)[2]) {
 #pragma unroll
-    for (int n = 0; n < NCH; ++n) lds_dma<16>(src, extent, off[n], dst + 1024 * (NCH * wave + n));
+    for (int n = 0; n < NCH; ++n) lds_dma<16>(src, extent, off[n], dst + 1024 * (NCH * wave_u + n));
   };
   // iteration j issues K(j + 2) and V(j + 1) into the buffers the barrier of
   // iteration j - 1 freed; it reads K(j + 1) (scores of the next tile) and V(j)
