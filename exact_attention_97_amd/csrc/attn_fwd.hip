@@ -674,10 +674,17 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
         case 2: return launch_fwd_e<FwdCfg<128, 32, 4, 3>>(a, st);
         case 3: return launch_fwd_e<FwdDefault<128>::type>(a, st);  // four wavefronts (the split-KV tile)
         case 4: return launch_fwd_e<FwdCfg<128, 64, 4, 3>>(a, st);
-        // default: the cooperative tile, eight wavefronts (256 queries) per
-        // workgroup sharing each K / V tile (0-2 % faster than four at the
-        // headline shape; split-KV keeps four, which suits few query rows)
-        default: return launch_fwd_e<FwdCfg<128, 64, 8, 2>>(a, st);
+        case 5: return launch_fwd_e<FwdCfg<128, 64, 8, 2>>(a, st);  // eight wavefronts at any length
+        // default: from 8192 queries on the cooperative tile, eight
+        // wavefronts (256 queries) per workgroup sharing each K / V tile
+        // (1-2 % faster than four at B=2, H=16, S=8192 with the outlier
+        // inputs); shorter sequences have few 256-query tiles per head and
+        // balance better with four wavefronts (measured 4-6 % faster at
+        // S = 2048, 0.5-2 % at 4096).  Split-KV keeps four, which suits few
+        // query rows.
+        default:
+          return a.S <= 4096 ? launch_fwd_e<FwdDefault<128>::type>(a, st)
+                             : launch_fwd_e<FwdCfg<128, 64, 8, 2>>(a, st);
       }
     case 256: return launch_fwd_e<FwdDefault<256>::type>(a, st);
     default: return hipErrorInvalidValue;

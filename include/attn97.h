@@ -234,7 +234,7 @@ attn_status attn_exp2_eval(const float* x, float* y, long n, int mode, void* str
 /*
  * Diagnostic: select a kernel variant kept for measurement (tile shapes,
  * wavefronts per workgroup, load schedules), for subsequent calls in this
- * process.  kernel: "fwd" (D = 128 forward: 0 default, 1..4), "bwd_dkdv"
+ * process.  kernel: "fwd" (D = 128 forward: 0 default, 1..5), "bwd_dkdv"
  * (D = 128 split-mode dK/dV: 0 default, 1..5), "bwd_dq" (D = 128 dQ: 0
  * default, 1..2), "fwd_fp8" (FP8 forward: 0 default, 1); variant -1
  * returns to the choice of the environment variables ATTN97_FWD_VARIANT /

@@ -397,11 +397,12 @@ def test_splitkv_workload_full_size(name):
 
 # ----------------------------------------------------------------------------
 # kernel variants kept for measurement (tile shapes, wavefronts per workgroup,
-# load schedules; fwd 1 / 3 and dQ 2 are the eight-wavefront cooperative
-# tiles): each against the float64 oracle, ragged length, both causal settings
+# load schedules; fwd 1 / 5 and dQ 2 are the eight-wavefront cooperative
+# tiles, fwd 3 the four-wavefront tile the default takes up to S = 4096):
+# each against the float64 oracle, ragged length, both causal settings
 # ----------------------------------------------------------------------------
 
-VARIANTS = [("fwd", v) for v in range(1, 5)] + [("bwd_dkdv", v) for v in range(1, 6)] + \
+VARIANTS = [("fwd", v) for v in range(1, 6)] + [("bwd_dkdv", v) for v in range(1, 6)] + \
            [("bwd_dq", v) for v in range(1, 3)]
 
 
