@@ -397,8 +397,9 @@ def test_splitkv_workload_full_size(name):
 
 # ----------------------------------------------------------------------------
 # kernel variants kept for measurement (tile shapes, wavefronts per workgroup,
-# load schedules; fwd 1 / 5 and dQ 2 are the eight-wavefront cooperative
-# tiles, fwd 3 the four-wavefront tile the default takes up to S = 4096):
+# load schedules; fwd 1 / 5 are the eight-wavefront cooperative tiles, fwd 3
+# the four-wavefront tile the default takes up to S = 4096, dQ 2 the
+# four-wavefront dQ tile):
 # each against the float64 oracle, ragged length, both causal settings
 # ----------------------------------------------------------------------------
 
