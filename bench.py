@@ -2,13 +2,19 @@
 
 One step is one pass of the whole path over one batch of synthetic input:
 forward (O, LSE) and backward (dQ, dK, dV), non-causal and causal, at
-B=2, H=16, S=8192, D=128 in bf16 (Q and K N(0,1) with 1% of entries x20,
-V and dO N(0,1), seed 2).  The inputs are resident in HBM before timing.
+B=2, H=16, S=8192, D=128 in bf16.  The forward leg runs on the outlier
+workload (Q and K N(0,1) with 1% of entries x20, V N(0,1), seed 2), the
+backward leg on the iid workload of the same shape (Q, K, V, dO N(0,1),
+seed 7; its O and LSE come from one forward call before timing).  The inputs
+are resident in HBM before timing.
 
 Printed: one JSON line with the whole-step attention TFLOPs/s, a per-pass
 breakdown (fraction of the 2.5 PFLOP/s dense bf16 MFMA peak), the roofline
-of the dominant kernel timed with HIP events on its own launch stream, and
-the CPU oracle timed on a bounded sample on the host cores.
+of the dominant kernel, and the CPU oracle timed on a bounded sample on the
+host cores.  The K timed steps run with the library's timing hooks off; the
+dominant kernel's launch time comes from a second run of K steps right
+after, identical except that the hooks record HIP events on the launch
+stream around every non-causal launch.
 
 Attention flops (algorithmic, not executed): forward 4*B*H*S^2*D, causal
 half of that; backward 2.5x forward (five S x S x D products).  For the
@@ -35,7 +41,8 @@ sys.path.insert(0, ROOT)
 METRIC = "attention TFLOPs/s fwd & bwd, bf16 D=128 S=8192 (causal/non), % of MFMA peak"
 PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 B, H, S, D = 2, 16, 8192, 128
-SEED = 2
+SEED = 2       # forward leg: the outlier workload
+SEED_BWD = 7   # backward leg: iid N(0,1) inputs
 # counter summaries (HBM bytes per launch) of the kernels the roofline may name
 TRAFFIC_FILES = {
     "bwd_dkdv": os.path.join(ROOT, "profiles", "bwd_dkdv_d128_s8192_traffic.md"),
@@ -107,7 +114,7 @@ def cpu_baseline(q, k, v, do, budget_s=15.0, max_heads=32):
         "unit": "TFLOPs/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{heads} whole head(s) of the B=2,H=16,S=8192,D=128 workload, forward + backward, "
+        "sample": f"{heads} whole head(s) of the B=2,H=16,S=8192,D=128 iid workload (seed 7), forward + backward, "
                   f"non-causal, float32 torch CPU oracle, {t_total:.1f} s; flops counted as 14*S^2*D per head",
         "os_cpu_count": os.cpu_count(),
     }
@@ -340,6 +347,8 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--exp-mode", default="native", choices=["native", "poly", "mixed"])
+    ap.add_argument("--poly-fraction", type=float, default=0.5,
+                    help="mixed mode: share of the exponentials on the polynomial (nearest quarter)")
     ap.add_argument("--tau", type=float, default=8.0)
     ap.add_argument("--bwd-mode", default="split", choices=["split", "atomic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -363,22 +372,27 @@ def main():
         sys.exit(1)
     attn.load()
     dev = torch.device("cuda:0")
-    q, k, v, do = make_qkvdo(B, H, S, D, SEED, outlier_frac=0.01, outlier_scale=20.0)
-    qg, kg, vg, dog = (t.to(dev) for t in (q, k, v, do))
+    q, k, v, _ = make_qkvdo(B, H, S, D, SEED, outlier_frac=0.01, outlier_scale=20.0)
+    qg, kg, vg = (t.to(dev) for t in (q, k, v))
+    qb, kb, vb, dob = make_qkvdo(B, H, S, D, SEED_BWD)
+    qbg, kbg, vbg, dobg = (t.to(dev) for t in (qb, kb, vb, dob))
     scale = 1.0 / math.sqrt(D)
     outs = {c: (torch.empty_like(qg), torch.empty((B, H, S), dtype=torch.float32, device=dev)) for c in (False, True)}
-    grads = (torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(vg))
+    # O and LSE of the backward leg's inputs, once, outside the timed region
+    outs_b = {c: attn.attn_fwd(qbg, kbg, vbg, scale=scale, causal=c) for c in (False, True)}
+    grads = (torch.empty_like(qbg), torch.empty_like(kbg), torch.empty_like(vbg))
     ws = torch.empty(attn.bwd_workspace_bytes(B, H, S, D, bwd_mode=args.bwd_mode), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def run_pass(causal, which, prof_on):
         attn.prof_enable(prof_on)
-        o, lse = outs[causal]
         if which == "fwd":
+            o, lse = outs[causal]
             attn.attn_fwd(qg, kg, vg, scale=scale, causal=causal, exp_mode=args.exp_mode,
-                          rescale_tau=args.tau, out=o, lse=lse)
+                          rescale_tau=args.tau, poly_fraction=args.poly_fraction, out=o, lse=lse)
         else:
-            attn.attn_bwd(qg, kg, vg, o, dog, lse, scale=scale, causal=causal, bwd_mode=args.bwd_mode,
+            o, lse = outs_b[causal]
+            attn.attn_bwd(qbg, kbg, vbg, o, dobg, lse, scale=scale, causal=causal, bwd_mode=args.bwd_mode,
                           workspace=ws, dq=grads[0], dk=grads[1], dv=grads[2])
         attn.prof_enable(False)
 
@@ -391,19 +405,26 @@ def main():
         step(False)
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly `steps` steps -------------------------------
-    attn.prof_reset()
+    # ---- timed region: exactly `steps` steps, timing hooks off -------------
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(True)
+        step(False)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
     step_flops = sum(fwd_flops(c) + bwd_flops(c) for c in (False, True))
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
-    # per-kernel averages of the non-causal launches inside the timed region
+    # ---- the same `steps` steps again with the timing hooks on: per-kernel
+    # averages of the non-causal launches (HIP events on the launch stream)
+    attn.prof_reset()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    ms_per_step_hooked = (time.perf_counter() - t1) * 1e3 / args.steps
     kern = {}
     for name in ("fwd", "bwd_pre", "bwd_main", "dq_convert", "bwd_dkdv", "bwd_dq"):
         n, ms = attn.prof_collect(name)
@@ -451,6 +472,8 @@ def main():
         "flops_per_launch": dom_flops,
         "avg_launch_ms": round(dom_ms, 4),
         "launches_timed": kern[dom]["launches"],
+        "timed_in": f"a second run of the {args.steps} steps with HIP events around each non-causal launch "
+                    f"({ms_per_step_hooked:.4f} ms per step there)",
     }
 
     result = {
@@ -467,10 +490,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "exact attention forward+backward, non-causal and causal, bf16, "
-                        "B=2 H=16 S=8192 D=128 (Q,K N(0,1) with 1% x20 outliers; V,dO N(0,1); seed 2)",
-            "B": B, "H": H, "S": S, "D": D, "exp_mode": args.exp_mode, "rescale_tau": args.tau,
-            "bwd_mode": args.bwd_mode,
+            "workload": "exact attention forward+backward, non-causal and causal, bf16, B=2 H=16 S=8192 D=128; "
+                        "forward on Q,K N(0,1) with 1% x20 outliers, V N(0,1) (seed 2); backward on Q,K,V,dO "
+                        "iid N(0,1) (seed 7) with O, LSE from one forward call before timing",
+            "B": B, "H": H, "S": S, "D": D, "exp_mode": args.exp_mode, "poly_fraction": args.poly_fraction,
+            "rescale_tau": args.tau, "bwd_mode": args.bwd_mode, "seed_fwd": SEED, "seed_bwd": SEED_BWD,
         },
         "frac_of_peak": round(value / PEAK_TFLOPS, 4),
         "breakdown": breakdown,
@@ -484,7 +508,7 @@ def main():
         result["fp8"] = fp8_measure(torch, attn, dev, B, H, S, D)
         result["workloads"] = workloads_measure(torch, attn, dev)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(q, k, v, do)
+        result["cpu_baseline"] = cpu_baseline(qb, kb, vb, dob)
     print(json.dumps(result), flush=True)
 
 

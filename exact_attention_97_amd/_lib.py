@@ -35,7 +35,8 @@ FP8_REGIONS = ("q8", "k8", "v8t", "qs", "ks", "vs", "scratch")
 
 
 class AttnOpts(ctypes.Structure):
-    _fields_ = [("exp_mode", ctypes.c_int), ("rescale_tau", ctypes.c_float), ("bwd_mode", ctypes.c_int)]
+    _fields_ = [("exp_mode", ctypes.c_int), ("poly_fraction", ctypes.c_float), ("rescale_tau", ctypes.c_float),
+                ("bwd_mode", ctypes.c_int)]
 
 
 class AttnError(RuntimeError):
@@ -102,9 +103,10 @@ def _check(fn, code):
         raise AttnError(fn, code, load().attn_strerror(code).decode())
 
 
-def make_opts(exp_mode="native", rescale_tau=8.0, bwd_mode="split") -> AttnOpts:
+def make_opts(exp_mode="native", rescale_tau=8.0, bwd_mode="split", poly_fraction=0.5) -> AttnOpts:
     o = AttnOpts()
     o.exp_mode = EXP_MODES[exp_mode] if isinstance(exp_mode, str) else int(exp_mode)
+    o.poly_fraction = float(poly_fraction)
     o.rescale_tau = float(rescale_tau)
     o.bwd_mode = BWD_MODES[bwd_mode] if isinstance(bwd_mode, str) else int(bwd_mode)
     return o
@@ -130,7 +132,7 @@ def _check_qkv(*ts):
 
 
 def attn_fwd(q, k, v, scale=None, causal=False, exp_mode="native", rescale_tau=8.0,
-             out=None, lse=None, stream=None):
+             out=None, lse=None, stream=None, poly_fraction=0.5):
     """Forward pass; returns (O bf16 [B,H,S,D], LSE fp32 [B,H,S])."""
     import torch
 
@@ -142,7 +144,7 @@ def attn_fwd(q, k, v, scale=None, causal=False, exp_mode="native", rescale_tau=8
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    opts = make_opts(exp_mode, rescale_tau)
+    opts = make_opts(exp_mode, rescale_tau, poly_fraction=poly_fraction)
     _check("attn_fwd", lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                     lse.data_ptr(), B, H, S, D, float(scale), int(bool(causal)),
                                     ctypes.byref(opts), _stream_ptr(stream)))
@@ -154,7 +156,7 @@ def fwd_splitkv_workspace_bytes(B, H, Sq, Sk, D, causal=False, num_splits=0):
 
 
 def attn_fwd_splitkv(q, k, v, scale=None, causal=False, num_splits=0, exp_mode="native", rescale_tau=8.0,
-                     workspace=None, out=None, lse=None, stream=None):
+                     workspace=None, out=None, lse=None, stream=None, poly_fraction=0.5):
     """Split-KV forward: q [B,H,Sq,D], k/v [B,H,Sk,D]; returns (O bf16 [B,H,Sq,D], LSE fp32 [B,H,Sq])."""
     import torch
 
@@ -175,7 +177,7 @@ def attn_fwd_splitkv(q, k, v, scale=None, causal=False, num_splits=0, exp_mode="
     need = fwd_splitkv_workspace_bytes(B, H, Sq, Sk, D, causal, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    opts = make_opts(exp_mode, rescale_tau)
+    opts = make_opts(exp_mode, rescale_tau, poly_fraction=poly_fraction)
     _check("attn_fwd_splitkv", lib.attn_fwd_splitkv(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), B, H, Sq, Sk, D, float(scale), int(bool(causal)),
@@ -294,7 +296,7 @@ def exp2_eval(x, mode="native", stream=None):
 
 
 def set_variant(kernel, variant):
-    """Select a measured kernel variant ("fwd", "bwd_dkdv", "bwd_dq"); -1 = back to the environment's choice."""
+    """Select a measured kernel variant ("fwd", "bwd_dq"); -1 = back to the environment's choice."""
     _check("attn_set_variant", load().attn_set_variant(kernel.encode(), int(variant)))
 
 

@@ -28,14 +28,33 @@ attn_status check_shape(int B, int H, int S, int D) {
   return ATTN_OK;
 }
 
+// Largest accepted rescale threshold (log2 units).  An unnormalised
+// probability is at most 2^tau and a row sums at most S of them, so with
+// tau <= 64 the fp32 row sum and accumulators stay below 2^64 * 2^31 * |v|,
+// far from fp32 overflow (2^128), for every supported length.
+constexpr float kMaxTau = 64.0f;
+
 attn_status read_opts(const attn_opts* in, attn_opts* out) {
   attn_default_opts(out);
   if (in == nullptr) return ATTN_OK;
   if (in->exp_mode < 0 || in->exp_mode > 2) return ATTN_ERR_UNSUPPORTED;
   if (in->bwd_mode < 0 || in->bwd_mode > 1) return ATTN_ERR_UNSUPPORTED;
-  if (!(in->rescale_tau >= 0.0f) || !isfinite(in->rescale_tau)) return ATTN_ERR_VALUE;
+  if (!(in->rescale_tau >= 0.0f && in->rescale_tau <= kMaxTau)) return ATTN_ERR_VALUE;
+  if (!(in->poly_fraction >= 0.0f && in->poly_fraction <= 1.0f)) return ATTN_ERR_VALUE;
   *out = *in;
   return ATTN_OK;
+}
+
+// Kernel exp2 mode of validated options: the mixed mode's fraction is
+// rounded to the nearest quarter (ties to even); a fraction that rounds to 0
+// or 1 runs the native or the polynomial kernel.
+int kernel_exp_mode(const attn_opts& o) {
+  if (o.exp_mode == ATTN_EXP_NATIVE) return attn97::kExpNative;
+  if (o.exp_mode == ATTN_EXP_POLY) return attn97::kExpPoly;
+  const long q = lrintf(o.poly_fraction * 4.0f);
+  if (q <= 0) return attn97::kExpNative;
+  if (q >= 4) return attn97::kExpPoly;
+  return attn97::exp_mix((int)q);
 }
 
 // ---- timing hooks -----------------------------------------------------------
@@ -50,8 +69,8 @@ size_t g_prof_used = 0;
 size_t g_prof_open = (size_t)-1;
 
 // kernel variant overrides (-1: not set, use the environment)
-int g_variant[attn97::VAR_COUNT] = {-1, -1, -1, -1};
-int g_variant_env[attn97::VAR_COUNT] = {-1, -1, -1, -1};
+int g_variant[attn97::VAR_COUNT] = {-1, -1};
+int g_variant_env[attn97::VAR_COUNT] = {-1, -1};
 
 }  // namespace
 
@@ -61,8 +80,7 @@ int kernel_variant(int slot) {
   if (slot < 0 || slot >= VAR_COUNT) return 0;
   if (g_variant[slot] >= 0) return g_variant[slot];
   if (g_variant_env[slot] < 0) {
-    static const char* names[VAR_COUNT] = {"ATTN97_FWD_VARIANT", "ATTN97_DKDV_VARIANT", "ATTN97_DQ_VARIANT",
-                                           "ATTN97_FWD_FP8_VARIANT"};
+    static const char* names[VAR_COUNT] = {"ATTN97_FWD_VARIANT", "ATTN97_DQ_VARIANT"};
     const char* e = getenv(names[slot]);
     const int v = e ? atoi(e) : 0;
     g_variant_env[slot] = v < 0 ? 0 : v;
@@ -104,6 +122,7 @@ extern "C" {
 void attn_default_opts(attn_opts* opts) {
   if (opts == nullptr) return;
   opts->exp_mode = ATTN_EXP_NATIVE;
+  opts->poly_fraction = 0.5f;
   opts->rescale_tau = 8.0f;
   opts->bwd_mode = ATTN_BWD_SPLIT;
 }
@@ -148,7 +167,7 @@ attn_status attn_fwd(const void* Q, const void* K, const void* V, void* O, float
   a.S = S;
   a.D = D;
   a.causal = causal ? 1 : 0;
-  a.exp_mode = o.exp_mode;
+  a.exp_mode = kernel_exp_mode(o);
   a.C = fabsf(scale) * kLog2eHost;
   a.qsign = (scale < 0.0f) ? 0x80008000u : 0u;
   a.tau = o.rescale_tau;
@@ -230,7 +249,7 @@ attn_status attn_fwd_splitkv(const void* Q, const void* K, const void* V, void* 
   a.S = Sq;
   a.D = D;
   a.causal = causal ? 1 : 0;
-  a.exp_mode = o.exp_mode;
+  a.exp_mode = kernel_exp_mode(o);
   a.C = fabsf(scale) * kLog2eHost;
   a.qsign = (scale < 0.0f) ? 0x80008000u : 0u;
   a.tau = o.rescale_tau;
@@ -362,8 +381,8 @@ attn_status attn_exp2_eval(const float* x, float* y, long n, int mode, void* str
 
 attn_status attn_set_variant(const char* kernel, int variant) {
   if (!kernel) return ATTN_ERR_NULL;
-  static const char* names[attn97::VAR_COUNT] = {"fwd", "bwd_dkdv", "bwd_dq", "fwd_fp8"};
-  static const int count[attn97::VAR_COUNT] = {6, 6, 3, 2};  // variants 0 .. count-1
+  static const char* names[attn97::VAR_COUNT] = {"fwd", "bwd_dq"};
+  static const int count[attn97::VAR_COUNT] = {2, 2};  // variants 0 .. count-1
   for (int i = 0; i < attn97::VAR_COUNT; ++i) {
     if (strcmp(kernel, names[i]) != 0) continue;
     if (variant < -1 || variant >= count[i]) return ATTN_ERR_VALUE;

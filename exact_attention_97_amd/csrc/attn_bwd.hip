@@ -659,8 +659,7 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
 // tile reads or loads into is known at compile time: the compiler then sees
 // that the next tile's loads cannot alias this tile's LDS transpose reads and
 // does not make those reads wait for the loads, which lets the loads be
-// spread over the tile's MFMA work (SPREAD; otherwise they are issued
-// together at the tile's start).
+// spread over the tile's MFMA work.
 //
 // Only unmasked tiles sit in the loop (two copies of the tile code, one per
 // buffer set; four would not fit the register budget): with S a multiple of
@@ -668,7 +667,7 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
 // workgroup's first two query tiles (queries k0 .. k0 + 127, the diagonal
 // block), which are peeled off before the loop.  RAGGED (S not a multiple of
 // 128) masks every tile instead.
-template <bool CAUSAL, bool RAGGED, bool SPREAD = true>
+template <bool CAUSAL, bool RAGGED>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ nlse2, const float* __restrict__ delta,
@@ -786,14 +785,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       // after the last tile the pieces reload it into the free set (in bounds,
       // never read), which keeps the tile branch-free
       auto part = [&](int p) {
-        if (SPREAD && p < NPIECE) piece(has_next ? qt + 1 : qt, Next{}, p);
+        if (p < NPIECE) piece(has_next ? qt + 1 : qt, Next{}, p);
       };
-      if constexpr (!SPREAD) {
-        if (has_next) {
-#pragma unroll
-          for (int p = 0; p < NPIECE; ++p) piece(qt + 1, Next{}, p);
-        }
-      }
       const uint16_t* Qb = set ? Qs1 : Qs0;
       const uint16_t* dOb = set ? dOs1 : dOs0;
       const float* nl = set ? nl1 : nl0;
@@ -847,22 +840,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   }
 }
 
-template <bool CAUSAL, bool RAGGED, bool SPREAD>
+template <bool CAUSAL, bool RAGGED>
 static hipError_t launch_dkdv_pipe_rt(const BwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   const int nkt = (a.S + 127) / 128;
   prof_begin(KID_BWD_DKDV, st);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<CAUSAL, RAGGED, SPREAD>), dim3(nkt * BH), dim3(256), 0, st, (const uint16_t*)a.Q,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<CAUSAL, RAGGED>), dim3(nkt * BH), dim3(256), 0, st, (const uint16_t*)a.Q,
                      (const uint16_t*)a.K, (const uint16_t*)a.V, (const uint16_t*)a.dO, a.nlse2, a.delta,
                      (uint16_t*)a.dK, (uint16_t*)a.dV, BH, a.S, a.scale, a.scale * kLog2e);
   prof_end(KID_BWD_DKDV, st);
   return hipGetLastError();
 }
 
-template <bool CAUSAL, bool SPREAD = true>
+template <bool CAUSAL>
 static hipError_t launch_dkdv_pipe_t(const BwdArgs& a, hipStream_t st) {
-  return (a.S % 128 == 0) ? launch_dkdv_pipe_rt<CAUSAL, false, SPREAD>(a, st)
-                          : launch_dkdv_pipe_rt<CAUSAL, true, SPREAD>(a, st);
+  return (a.S % 128 == 0) ? launch_dkdv_pipe_rt<CAUSAL, false>(a, st) : launch_dkdv_pipe_rt<CAUSAL, true>(a, st);
 }
 
 // Delta_i = sum_d dO_id O_id (fp32), nlse2_i = -LSE_i log2(e), and zero the
@@ -944,22 +936,9 @@ static hipError_t launch_pre_t(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Tile-configuration variants of the split-mode dK/dV kernel, selectable
-// for measurement (attn_set_variant("bwd_dkdv", v) or ATTN97_DKDV_VARIANT;
-// 0 = default).
-static int dkdv_variant() { return kernel_variant(VAR_DKDV); }
-
 template <int D, bool CAUSAL>
 static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
   if constexpr (D == 128) {
-    switch (dkdv_variant()) {
-      case 1: return launch_main_t<D, 32, CAUSAL, false, true, 2>(a, st);
-      case 2: return launch_main_t<D, 32, CAUSAL, false, false, 1>(a, st);
-      case 3: return launch_main_t<D, 64, CAUSAL, false, true, 1>(a, st);
-      case 4: return launch_main_t<D, 64, CAUSAL, false, false, 1>(a, st);  // one-pass tile, no pipeline
-      case 5: return launch_dkdv_pipe_t<CAUSAL, false>(a, st);              // next tile loaded at tile start
-      default: break;
-    }
     return launch_dkdv_pipe_t<CAUSAL>(a, st);
   } else if constexpr (D == 256) {
     // 32-query tiles, V tile in LDS, each workgroup forms 128 of the 256 columns

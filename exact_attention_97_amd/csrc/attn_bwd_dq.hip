@@ -353,24 +353,19 @@ static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Tile-configuration variants of the D = 128 kernel, selectable for
-// measurement (attn_set_variant("bwd_dq", v) or ATTN97_DQ_VARIANT).  0 =
-// default: the cooperative big tile, one workgroup of eight wavefronts (256
+// D = 128: the cooperative big tile, one workgroup of eight wavefronts (256
 // queries) per CU sharing each K / V tile in LDS, 64-key tiles in the
 // pipelined step (measured 3-4 % faster than four wavefronts at S = 4096 and
-// 8192, 2.5 % at 32768).  Variant 1: 32-key tiles, one block per step;
-// variant 2: two workgroups of four wavefronts per CU.
+// 8192, 2.5 % at 32768).  Variant 1 (attn_set_variant("bwd_dq", 1) or
+// ATTN97_DQ_VARIANT=1): two workgroups of four wavefronts per CU.
 static int dq_variant() { return kernel_variant(VAR_DQ); }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
   switch (a.D) {
     case 64: return launch_dq_t<FwdCfg<64, 64, 4, 2>, 2>(a, st);  // two workgroups (eight wavefronts) per CU
     case 128:
-      switch (dq_variant()) {
-        case 1: return launch_dq_t<FwdCfg<128, 32, 4, 2>, 2>(a, st);        // 32-key tiles, one block per step
-        case 2: return launch_dq_t<FwdCfg<128, 64, 4, 2>, 2, true>(a, st);  // four wavefronts per workgroup
-        default: return launch_dq_t<FwdCfg<128, 64, 8, 2>, 1, true>(a, st);
-      }
+      if (dq_variant() == 1) return launch_dq_t<FwdCfg<128, 64, 4, 2>, 2, true>(a, st);
+      return launch_dq_t<FwdCfg<128, 64, 8, 2>, 1, true>(a, st);
     case 256: return launch_dq_t<FwdCfg<256, 32, 4, 2>, 1>(a, st);  // 32-key tiles, one workgroup per CU
     default: return hipErrorInvalidValue;
   }

@@ -604,16 +604,10 @@ hipError_t launch_fp8_quantize(const void* Q, const void* K, const void* V, cons
 hipError_t launch_fwd_fp8(const Fp8Buf& f, void* O, float* LSE, int B, int H, int S, float C, uint32_t qsign,
                           float tau, int causal, hipStream_t st) {
   const int BH = B * H;
-  // variant 1: eight wavefronts (256 query rows) per workgroup
-  const int nw = kernel_variant(VAR_FWD_FP8) == 1 ? 8 : 4;
-  const int nqt = (f.Sp + 32 * nw - 1) / (32 * nw);
+  const int nqt = (f.Sp + 127) / 128;  // four wavefronts, 128 query rows per workgroup
   prof_begin(KID_FWD_FP8, st);
-  if (nw == 8)
-    hipLaunchKernelGGL(fwd_fp8_kernel<8>, dim3(nqt * BH), dim3(512), 0, st, f, (uint16_t*)O, LSE, BH, S, nqt, C,
-                       qsign, tau, causal);
-  else
-    hipLaunchKernelGGL(fwd_fp8_kernel<4>, dim3(nqt * BH), dim3(256), 0, st, f, (uint16_t*)O, LSE, BH, S, nqt, C,
-                       qsign, tau, causal);
+  hipLaunchKernelGGL(fwd_fp8_kernel<4>, dim3(nqt * BH), dim3(256), 0, st, f, (uint16_t*)O, LSE, BH, S, nqt, C,
+                     qsign, tau, causal);
   prof_end(KID_FWD_FP8, st);
   return hipGetLastError();
 }

@@ -150,18 +150,44 @@ struct FwdWave {
     }
   }
 
-  // Region 1 of one tile (no branches): row max and the rescale decision,
-  // the next tile's scores on the MFMA unit interleaved with this tile's
-  // exponentials on the VALU.  Returns P (bf16) and the rescale decision for
-  // region 2.  The next tile's scores are computed even after the wave's
-  // last tile (from a stale buffer, never used) so that region 1 has no
-  // branch.
+  // Schedule of the score MFMAs of the next tile interleaved with this
+  // tile's softmax: the K fragment reads run four ahead of the MFMAs that use
+  // them, and each MFMA is followed by NV VALU instructions.
+  template <int NV>
+  __device__ __forceinline__ static void region1_schedule() {
+    constexpr int NS = NKS * NKB;  // score MFMAs of the next tile
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < NS - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+    }
+  }
+
+  // The optimistic form of region 1 keeps the tile's scores live until its
+  // check; with more than two 32-key blocks per tile (D = 64, 128-key tiles)
+  // that does not fit the register budget, and every tile takes the exact
+  // form.
+  static constexpr bool kOptimistic = NKB <= 2;
+
+  // Region 1, exact form (masked tiles: causal diagonal, ragged end): mask,
+  // exact row max and the rescale decision first, then the next tile's
+  // scores on the MFMA unit interleaved with this tile's exponentials on the
+  // VALU.  Returns P (bf16) and the rescale decision for region 2.  The next
+  // tile's scores are computed even after the wave's last tile (from a stale
+  // buffer, never used) so that region 1 has no branch.
   template <bool MASK>
-  __device__ __forceinline__ static void region1(const uint16_t* knext, const FwdOffsets<Cfg>& of,
-                                                 const bf16x8 (&qreg)[NKS], f32x16 (&scur)[NKB],
-                                                 f32x16 (&snext)[NKB], float& m_run, float& l_part, int k0, int lim,
-                                                 int hh, float C, float tau, bf16x8 (&pb)[2 * NKB], bool& grow,
-                                                 float& alpha) {
+  __device__ __forceinline__ static void region1_exact(const uint16_t* knext, const FwdOffsets<Cfg>& of,
+                                                        const bf16x8 (&qreg)[NKS], f32x16 (&scur)[NKB],
+                                                        f32x16 (&snext)[NKB], float& m_run, float& l_part, int k0,
+                                                        int lim, int hh, float C, float tau, bf16x8 (&pb)[2 * NKB],
+                                                        bool& grow, float& alpha) {
     const float mx = tile_max<MASK>(scur, k0, lim, hh);
     const float mxs = (mx == kNegInf) ? kNegInf : mx * C;
     const float m_new = __builtin_fmaxf(m_run, mxs);
@@ -173,26 +199,11 @@ struct FwdWave {
     l_part *= alpha;
     // Region 1 runs at raised wave priority: of the two wavefronts sharing a
     // SIMD, the one issuing score MFMAs interleaved with softmax work is
-    // preferred over one in its P V phase, which keeps the matrix unit fed
-    // (measured: about 4% faster than equal priority).
+    // preferred over one in its P V phase, which keeps the matrix unit fed.
     __builtin_amdgcn_s_setprio(1);
     scores(knext, of, qreg, snext);
     probs<MASK>(scur, C, m_run, pb, l_part);
-    // Schedule: the K fragment reads run four ahead of the MFMAs that use
-    // them, and each MFMA is followed by a share of the softmax VALU work.
-    constexpr int NS = NKS * NKB;  // score MFMAs of the next tile
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i = 0; i < NS - 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-    }
+    region1_schedule<6>();
     // keep the exponentials and the packed P above the (rare) rescale branch
 #pragma unroll
     for (int t = 0; t < 2 * NKB; ++t) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pb[t])));
@@ -200,19 +211,47 @@ struct FwdWave {
     __builtin_amdgcn_s_setprio(0);
   }
 
-  // Region 2: the (rare) rescale of the output accumulator, then P V with
-  // its transpose loads.
-  __device__ __forceinline__ static void region2(const uint16_t* vcur, const FwdOffsets<Cfg>& of,
-                                                 const bf16x8 (&pb)[2 * NKB], f32x16 (&oacc)[NDB], bool grow,
-                                                 float alpha) {
-    if (grow) {
+  // Region 1 of an unmasked tile, optimistic form.  The exponentials use the
+  // running max as it stands, with no row max taken first; every probability
+  // of the tile is at most its lane's partial row sum over the tile, so when
+  // no partial sum exceeds thr = 2^tau no probability does either and the
+  // running max may stay (the conditional rescaling condition).  Otherwise
+  // (rare after the first tiles, and always on a wave's first tile, where the
+  // running max is -inf and every partial sum is infinite) the exact tile max
+  // is taken, the accumulator and row sum are rescaled and the tile's
+  // exponentials are recomputed.  `!(l <= thr)` also catches a NaN.
+  __device__ __forceinline__ static void region1_fast(const uint16_t* knext, const FwdOffsets<Cfg>& of,
+                                                      const bf16x8 (&qreg)[NKS], f32x16 (&scur)[NKB],
+                                                      f32x16 (&snext)[NKB], float& m_run, float& l_part, float C,
+                                                      float thr, bf16x8 (&pb)[2 * NKB], f32x16 (&oacc)[NDB]) {
+    float l_tile = 0.0f;
+    __builtin_amdgcn_s_setprio(1);
+    scores(knext, of, qreg, snext);
+    probs<false>(scur, C, m_run, pb, l_tile);
+    region1_schedule<7>();
+#pragma unroll
+    for (int t = 0; t < 2 * NKB; ++t) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pb[t])));
+    asm volatile("" ::"v"(l_tile));
+    __builtin_amdgcn_s_setprio(0);
+    if (__any(!(l_tile <= thr))) {
+      const float mx = tile_max<false>(scur, 0, 0, 0);
+      const float m_new = __builtin_fmaxf(m_run, mx * C);
+      const float alpha = exp2_native(m_run - m_new);  // 0 while m_run is -inf (l_part and oacc are 0 then)
+      l_part *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+      l_tile = 0.0f;
+      probs<false>(scur, C, m_run, pb, l_tile);
     }
+    l_part += l_tile;
+  }
+
+  // P V with its transpose loads: the reads run eight ahead (two per MFMA
+  // operand, so three MFMAs of look-ahead under the exact LDS wait counts).
+  __device__ __forceinline__ static void region2(const uint16_t* vcur, const FwdOffsets<Cfg>& of,
+                                                 const bf16x8 (&pb)[2 * NKB], f32x16 (&oacc)[NDB]) {
     pv(vcur, of, pb, oacc);
-    // PV: transpose reads run eight ahead (two per MFMA operand, so three
-    // MFMAs of look-ahead under the exact LDS wait counts; measured 0.4 %
-    // faster than four ahead at B=2, H=16, S=8192, D=128).
     constexpr int NP = 2 * NKB * NDB, PVA = 8;
     __builtin_amdgcn_sched_group_barrier(0x100, PVA, 1);
 #pragma unroll
@@ -223,17 +262,25 @@ struct FwdWave {
     __builtin_amdgcn_sched_group_barrier(0x008, PVA / 2, 1);
   }
 
-  // One whole tile: region 1 then region 2.
+  // One whole tile: region 1 then region 2.  thr = 2^tau.
   template <bool MASK>
   __device__ __forceinline__ static void step(const uint16_t* knext, const uint16_t* vcur, const FwdOffsets<Cfg>& of,
                                               const bf16x8 (&qreg)[NKS], f32x16 (&scur)[NKB],
                                               f32x16 (&snext)[NKB], f32x16 (&oacc)[NDB], float& m_run,
-                                              float& l_part, int k0, int lim, int hh, float C, float tau) {
+                                              float& l_part, int k0, int lim, int hh, float C, float tau, float thr) {
     bf16x8 pb[2 * NKB];
-    bool grow;
-    float alpha;
-    region1<MASK>(knext, of, qreg, scur, snext, m_run, l_part, k0, lim, hh, C, tau, pb, grow, alpha);
-    region2(vcur, of, pb, oacc, grow, alpha);
+    if constexpr (MASK || !kOptimistic) {
+      bool grow;
+      float alpha;
+      region1_exact<MASK>(knext, of, qreg, scur, snext, m_run, l_part, k0, lim, hh, C, tau, pb, grow, alpha);
+      if (grow) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      }
+    } else {
+      region1_fast(knext, of, qreg, scur, snext, m_run, l_part, C, thr, pb, oacc);
+    }
+    region2(vcur, of, pb, oacc);
   }
 };
 
@@ -357,6 +404,7 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
   float m_run = kNegInf;  // running max, in units of log2 (scores times C)
   float l_part = 0.0f;    // this lane's partial row sum
+  const float thr = exp2_native(tau);  // bound on one tile's partial row sum (unmasked tiles)
 
   FwdOffsets<Cfg> of;
   of.init(wave, lane);
@@ -416,10 +464,10 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
     if (kt < nkt_w) {
       if (kt < nfull)
         W::template step<false>(kbuf(kn), vbuf(vc), of, qreg, scur, snext, oacc, m_run, l_part, kb + kt * BC, lim,
-                                hh, C, tau);
+                                hh, C, tau, thr);
       else
         W::template step<true>(kbuf(kn), vbuf(vc), of, qreg, scur, snext, oacc, m_run, l_part, kb + kt * BC, lim,
-                               hh, C, tau);
+                               hh, C, tau, thr);
     }
     wait_loads(n_last);
     barrier_keep_loads();
@@ -649,43 +697,35 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// a.exp_mode is the kernel exp2 mode (kExpNative, kExpPoly or exp_mix(q)).
 template <class Cfg>
 static hipError_t launch_fwd_e(const FwdArgs& a, hipStream_t st) {
   switch (a.exp_mode) {
-    case 1: return launch_fwd_t<Cfg, 1>(a, st);
-    case 2: return launch_fwd_t<Cfg, 2>(a, st);
-    default: return launch_fwd_t<Cfg, 0>(a, st);
+    case kExpPoly: return launch_fwd_t<Cfg, kExpPoly>(a, st);
+    case exp_mix(1): return launch_fwd_t<Cfg, exp_mix(1)>(a, st);
+    case exp_mix(2): return launch_fwd_t<Cfg, exp_mix(2)>(a, st);
+    case exp_mix(3): return launch_fwd_t<Cfg, exp_mix(3)>(a, st);
+    default: return launch_fwd_t<Cfg, kExpNative>(a, st);
   }
 }
 
-// Tile-configuration variants of the D = 128 kernel, selectable for
-// measurement (attn_set_variant("fwd", v) or ATTN97_FWD_VARIANT; 0 = default).
-// The default and variant 1 are the cooperative big tile: eight wavefronts
-// (256 queries) share each K / V tile in LDS, half the tile loads per query;
-// variant 3 is the four-wavefront tile of the split-KV kernel.
+// The D = 128 tile by sequence length (measured on MI355X): up to 4096
+// queries four wavefronts (128 queries) per workgroup; longer sequences take
+// the cooperative big tile, eight wavefronts (256 queries) sharing each K / V
+// tile in LDS (1-2 % faster at B=2, H=16, S=8192 with the outlier inputs;
+// shorter sequences have few 256-query tiles per head and balance better with
+// four wavefronts: 4-6 % faster at S = 2048, 0.5-2 % at 4096).  Variant 1
+// (attn_set_variant("fwd", 1) or ATTN97_FWD_VARIANT=1) takes the eight-
+// wavefront tile at every length, so that its ragged and short cases can be
+// tested.  Split-KV keeps four, which suits few query rows.
 static int fwd_variant() { return kernel_variant(VAR_FWD); }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   switch (a.D) {
     case 64: return launch_fwd_e<FwdDefault<64>::type>(a, st);
     case 128:
-      switch (fwd_variant()) {
-        case 1: return launch_fwd_e<FwdCfg<128, 64, 8, 3>>(a, st);
-        case 2: return launch_fwd_e<FwdCfg<128, 32, 4, 3>>(a, st);
-        case 3: return launch_fwd_e<FwdDefault<128>::type>(a, st);  // four wavefronts (the split-KV tile)
-        case 4: return launch_fwd_e<FwdCfg<128, 64, 4, 3>>(a, st);
-        case 5: return launch_fwd_e<FwdCfg<128, 64, 8, 2>>(a, st);  // eight wavefronts at any length
-        // default: from 8192 queries on the cooperative tile, eight
-        // wavefronts (256 queries) per workgroup sharing each K / V tile
-        // (1-2 % faster than four at B=2, H=16, S=8192 with the outlier
-        // inputs); shorter sequences have few 256-query tiles per head and
-        // balance better with four wavefronts (measured 4-6 % faster at
-        // S = 2048, 0.5-2 % at 4096).  Split-KV keeps four, which suits few
-        // query rows.
-        default:
-          return a.S <= 4096 ? launch_fwd_e<FwdDefault<128>::type>(a, st)
-                             : launch_fwd_e<FwdCfg<128, 64, 8, 2>>(a, st);
-      }
+      if (fwd_variant() == 1 || a.S > 4096) return launch_fwd_e<FwdCfg<128, 64, 8, 2>>(a, st);
+      return launch_fwd_e<FwdDefault<128>::type>(a, st);
     case 256: return launch_fwd_e<FwdDefault<256>::type>(a, st);
     default: return hipErrorInvalidValue;
   }
@@ -732,9 +772,11 @@ static hipError_t launch_splitkv_t(const FwdArgs& a, const SplitKvLaunch& p, hip
 template <class Cfg>
 static hipError_t launch_splitkv_e(const FwdArgs& a, const SplitKvLaunch& p, hipStream_t st) {
   switch (a.exp_mode) {
-    case 1: return launch_splitkv_t<Cfg, 1>(a, p, st);
-    case 2: return launch_splitkv_t<Cfg, 2>(a, p, st);
-    default: return launch_splitkv_t<Cfg, 0>(a, p, st);
+    case kExpPoly: return launch_splitkv_t<Cfg, kExpPoly>(a, p, st);
+    case exp_mix(1): return launch_splitkv_t<Cfg, exp_mix(1)>(a, p, st);
+    case exp_mix(2): return launch_splitkv_t<Cfg, exp_mix(2)>(a, p, st);
+    case exp_mix(3): return launch_splitkv_t<Cfg, exp_mix(3)>(a, p, st);
+    default: return launch_splitkv_t<Cfg, kExpNative>(a, p, st);
   }
 }
 

@@ -7,6 +7,12 @@
 
 namespace attn97 {
 
+// Kernel exp2 modes of the forward kernels: native v_exp_f32, the polynomial
+// on the FMA pipe, or mixed with the polynomial taking q of every four
+// elements (q = 1, 2, 3: a quarter, half, three quarters).
+constexpr int kExpNative = 0, kExpPoly = 1;
+constexpr int exp_mix(int q) { return 1 + q; }  // q = 1..3 -> 2..4
+
 struct FwdArgs {
   const void* Q;
   const void* K;
@@ -15,7 +21,7 @@ struct FwdArgs {
   float* LSE;
   int B, H, S, D;
   int causal;
-  int exp_mode;
+  int exp_mode;    // kernel exp2 mode (kExpNative, kExpPoly, exp_mix(q))
   float C;         // |scale| * log2(e)
   uint32_t qsign;  // 0x80008000 flips the sign of Q (negative scale), else 0
   float tau;       // conditional rescale threshold, log2 units
@@ -96,9 +102,8 @@ enum KernelId {
 
 // Kernel variants kept for measurement (0 = the default kernel).  The
 // choice comes from attn_set_variant, else from the environment variables
-// ATTN97_FWD_VARIANT, ATTN97_DKDV_VARIANT, ATTN97_DQ_VARIANT,
-// ATTN97_FWD_FP8_VARIANT (read once).
-enum VariantSlot { VAR_FWD = 0, VAR_DKDV, VAR_DQ, VAR_FWD_FP8, VAR_COUNT };
+// ATTN97_FWD_VARIANT, ATTN97_DQ_VARIANT (read once).
+enum VariantSlot { VAR_FWD = 0, VAR_DQ, VAR_COUNT };
 int kernel_variant(int slot);
 
 // Called by the launchers around each kernel launch (no-ops unless timing is on).

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn_kernels.hpp"
+
 namespace attn97 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -98,14 +100,19 @@ __device__ __forceinline__ float exp2_poly(float x) {
   return __builtin_amdgcn_ldexpf(p, n);
 }
 
+// Kernel exp2 modes (kExpNative, kExpPoly, exp_mix(q), attn_kernels.hpp):
+// in the mixed modes the polynomial takes q of every four elements (element
+// idx with idx % 4 < q) and the native unit the rest.
 template <int MODE>
 __device__ __forceinline__ float exp2_mode(float x, int idx) {
-  if constexpr (MODE == 0) {
+  if constexpr (MODE == kExpNative) {
     return exp2_native(x);
-  } else if constexpr (MODE == 1) {
+  } else if constexpr (MODE == kExpPoly) {
     return exp2_poly(x);
   } else {
-    return (idx & 1) ? exp2_poly(x) : exp2_native(x);
+    constexpr int q = MODE - 1;
+    static_assert(q >= 1 && q <= 3, "mixed mode: one to three of every four elements polynomial");
+    return ((idx & 3) < q) ? exp2_poly(x) : exp2_native(x);
   }
 }
 

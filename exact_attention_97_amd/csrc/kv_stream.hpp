@@ -39,23 +39,19 @@ struct FwdCfg {
 // matrix) into the swizzled LDS tile `dst`: lane l of load n fills physical
 // chunk 64 * (wave * DMA_PER_WAVE + n) + l.  `loff[n]` is that chunk's
 // logical element offset inside the tile (row * D + 8 * chunk), fixed per
-// lane.  In a ragged last tile, rows past S are clamped to S-1 (finite data;
-// the scores of those keys are masked).
+// lane.  The buffer resource ends at row S, so in a ragged last tile the rows
+// past S read as zero (a range-checked buffer load returns zero and the LDS
+// copy stores it); the scores of those keys are masked, and zero V rows
+// contribute nothing.  No per-tile offset arithmetic is needed.
 // dma_tile_part issues only this wave's n-th 1 KiB piece: a kernel can spread
 // a tile's pieces over its MFMA work (issued back to back they fill the
 // memory pipeline and stall the wavefront).
 template <class Cfg>
 __device__ __forceinline__ void dma_tile_part(const uint16_t* __restrict__ src, int k0, int S, uint16_t* dst,
                                               int wave, const uint32_t (&loff)[Cfg::DMA_PER_WAVE], int n) {
-  constexpr int NPW = Cfg::DMA_PER_WAVE, BC = Cfg::BC, D = Cfg::D;
+  constexpr int NPW = Cfg::DMA_PER_WAVE, D = Cfg::D;
   const uint16_t* tile = src + (size_t)k0 * D;
-  uint32_t off = loff[n];
-  if (k0 + BC > S) {
-    const uint32_t row = off / D;
-    const uint32_t last = (uint32_t)(S - 1 - k0);
-    off = (row > last ? last : row) * D + off % D;
-  }
-  lds_dma<16>(tile, (uint32_t)(S - k0) * (uint32_t)(D * 2), off * 2, dst + 512 * (wave * NPW + n));
+  lds_dma<16>(tile, (uint32_t)(S - k0) * (uint32_t)(D * 2), loff[n] * 2, dst + 512 * (wave * NPW + n));
 }
 
 template <class Cfg>

@@ -24,9 +24,10 @@
  *    tile size.  B*H*S*D must fit in 2^31 - 1 elements per tensor.
  *  - scale must be finite (any sign; 0 gives the mean of the visible rows).
  *  - stream is a hipStream_t (NULL = the default stream).  Calls are
- *    asynchronous with respect to the host; the library never synchronises,
- *    never allocates device memory and keeps no per-call state, so calls on
- *    different streams may run concurrently.
+ *    asynchronous with respect to the host; the library never synchronises
+ *    and never allocates device memory.  Its only state is process-global
+ *    diagnostics (attn_set_variant, the timing hooks attn_prof_*); with those
+ *    left alone, calls on different streams and threads may run concurrently.
  *  - Errors are return codes only.  Argument errors are detected before
  *    anything is launched.  A failed launch returns ATTN_ERR_HIP; a fault
  *    inside a kernel surfaces at the caller's next synchronisation.
@@ -58,9 +59,9 @@ typedef enum {
  * экспоненты"; abstract of "FlashAttention-4: Algorithm and Kernel Pipelining
  * Co-Design for Asymmetric Hardware Scaling"). */
 typedef enum {
-    ATTN_EXP_NATIVE = 0, /* hardware v_exp_f32 for every element                  */
-    ATTN_EXP_POLY = 1,   /* range reduction + degree-3 polynomial on the FMA pipe  */
-    ATTN_EXP_MIXED = 2   /* half of each lane's scores native, half polynomial     */
+    ATTN_EXP_NATIVE = 0, /* hardware v_exp_f32 for every element                           */
+    ATTN_EXP_POLY = 1,   /* range reduction + degree-3 polynomial on the FMA pipe           */
+    ATTN_EXP_MIXED = 2   /* a fraction poly_fraction of the scores polynomial, the rest native */
 } attn_exp_mode;
 
 /* How the backward pass forms dQ.  The pages name the atomic additions of
@@ -73,18 +74,26 @@ typedef enum {
 } attn_bwd_mode;
 
 typedef struct {
-    int exp_mode;      /* attn_exp_mode; default ATTN_EXP_NATIVE                               */
-    float rescale_tau; /* conditional rescaling threshold in log2 units, >= 0; default 8.
-                          The running row maximum used to shift the scores is only moved when
-                          some row of a wavefront sees its maximum grow by more than tau, so
-                          unnormalised probabilities stay below 2^tau.  0 = always rescale.
-                          (Conditional softmax rescaling: abstract of "FlashAttention-4:
-                          Algorithm and Kernel Pipelining Co-Design for Asymmetric Hardware
-                          Scaling".)  The result is the same for every tau up to rounding.  */
-    int bwd_mode;      /* attn_bwd_mode; default ATTN_BWD_SPLIT                                */
+    int exp_mode;        /* attn_exp_mode; default ATTN_EXP_NATIVE                              */
+    float poly_fraction; /* ATTN_EXP_MIXED only: share of each lane's scores whose exp2 takes the
+                            polynomial, in [0, 1], rounded to the nearest quarter (ties to even);
+                            0 runs the native kernel and 1 the polynomial one.  The software
+                            exponential covers only part of the exponentials (page
+                            "FlashAttention-3 и FlashAttention-4", section "Программная эмуляция
+                            экспоненты").  Default 0.5.  Outside [0, 1] or NaN: ATTN_ERR_VALUE. */
+    float rescale_tau;   /* conditional rescaling threshold in log2 units, in [0, 64]; default 8.
+                            The running row maximum used to shift the scores is only moved when
+                            some score of a wavefront's rows could exceed it by more than tau, so
+                            unnormalised probabilities stay at most 2^tau.  0 = always rescale.
+                            (Conditional softmax rescaling: abstract of "FlashAttention-4:
+                            Algorithm and Kernel Pipelining Co-Design for Asymmetric Hardware
+                            Scaling".)  The result is the same for every tau up to rounding.
+                            Above 64 (where 2^tau times S probabilities could approach the fp32
+                            range), negative or NaN: ATTN_ERR_VALUE.                          */
+    int bwd_mode;        /* attn_bwd_mode; default ATTN_BWD_SPLIT                               */
 } attn_opts;
 
-/* Defaults: {ATTN_EXP_NATIVE, 8.0f, ATTN_BWD_SPLIT}. */
+/* Defaults: {ATTN_EXP_NATIVE, 0.5f, 8.0f, ATTN_BWD_SPLIT}. */
 void attn_default_opts(attn_opts* opts);
 
 /*
@@ -232,14 +241,15 @@ attn_status attn_fwd_fp8(const void* buf, size_t buf_bytes, void* O, float* LSE,
 attn_status attn_exp2_eval(const float* x, float* y, long n, int mode, void* stream);
 
 /*
- * Diagnostic: select a kernel variant kept for measurement (tile shapes,
- * wavefronts per workgroup, load schedules), for subsequent calls in this
- * process.  kernel: "fwd" (D = 128 forward: 0 default, 1..5), "bwd_dkdv"
- * (D = 128 split-mode dK/dV: 0 default, 1..5), "bwd_dq" (D = 128 dQ: 0
- * default, 1..2), "fwd_fp8" (FP8 forward: 0 default, 1); variant -1
- * returns to the choice of the environment variables ATTN97_FWD_VARIANT /
- * ATTN97_DKDV_VARIANT / ATTN97_DQ_VARIANT / ATTN97_FWD_FP8_VARIANT
- * (default 0).  Every variant computes the same result.  Not thread-safe.
+ * Diagnostic: select a kernel variant kept for measurement, for subsequent
+ * calls in this process.  kernel: "fwd" (D = 128 forward: 0 default, 1 the
+ * eight-wavefront tile at every length), "bwd_dq" (D = 128 dQ of the split
+ * backward: 0 default, 1 four wavefronts per workgroup); variant -1 returns
+ * to the choice of the environment variables ATTN97_FWD_VARIANT /
+ * ATTN97_DQ_VARIANT (default 0).  Every variant computes the same result.
+ * The choice is process-global state shared by every thread and stream of
+ * the process; it is not synchronised, so set it only while no other thread
+ * calls the library.
  * Errors: ATTN_ERR_NULL, ATTN_ERR_UNSUPPORTED (unknown kernel name),
  * ATTN_ERR_VALUE (variant out of range).
  */
@@ -252,10 +262,12 @@ attn_status attn_set_variant(const char* kernel, int variant);
  * the kernel named `kernel` ("fwd", "bwd_pre", "bwd_main", "bwd_dq", "bwd_dkdv",
  * "dq_convert", "fwd_splitkv", "splitkv_merge", "fp8_quantize" (all three
  * kernels of attn_fp8_quantize), "fwd_fp8"), the number of launches and the
- * summed milliseconds since the
- * last reset.  Events are created on first use and kept; at most 65536
- * launches are recorded between resets (later ones are not timed).
- * Not thread-safe; meant for single-threaded benchmark drivers.
+ * summed milliseconds since the last reset.  Events are created on first use
+ * and kept; at most 65536 launches are recorded between resets (later ones
+ * are not timed).  The enable flag and the event pool are process-global
+ * state, not synchronised: meant for a single-threaded benchmark driver, and
+ * while timing is enabled the library is not safe to call from several
+ * threads.  With timing disabled (the default) the library keeps no state.
  */
 attn_status attn_prof_enable(int on);
 attn_status attn_prof_reset(void);

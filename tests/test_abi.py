@@ -47,9 +47,12 @@ def test_version_and_strerror():
 def test_default_opts():
     lib = L.load()
     o = L.AttnOpts()
-    o.exp_mode, o.rescale_tau, o.bwd_mode = 7, -1.0, 7
+    o.exp_mode, o.poly_fraction, o.rescale_tau, o.bwd_mode = 7, 3.0, -1.0, 7
     lib.attn_default_opts(ctypes.byref(o))
-    assert (o.exp_mode, o.rescale_tau, o.bwd_mode) == (0, 8.0, 1)
+    assert (o.exp_mode, o.poly_fraction, o.rescale_tau, o.bwd_mode) == (0, 0.5, 8.0, 1)
+    # the struct layout of include/attn97.h: int, float, float, int
+    assert [f[0] for f in L.AttnOpts._fields_] == ["exp_mode", "poly_fraction", "rescale_tau", "bwd_mode"]
+    assert ctypes.sizeof(L.AttnOpts) == 16
 
 
 def fwd(**kw):
@@ -92,6 +95,12 @@ def test_fwd_bad_options():
     assert fwd(opts=L.make_opts(rescale_tau=-1.0)) == VALUE
     assert fwd(opts=L.make_opts(rescale_tau=float("nan"))) == VALUE
     assert fwd(opts=L.make_opts(rescale_tau=float("inf"))) == VALUE
+    # tau above 64 could let 2^tau times S probabilities approach the fp32 range
+    assert fwd(opts=L.make_opts(rescale_tau=64.5)) == VALUE
+    assert fwd(opts=L.make_opts(rescale_tau=200.0)) == VALUE
+    for frac in (-0.1, 1.01, float("nan"), float("inf")):
+        assert fwd(opts=L.make_opts(exp_mode="mixed", poly_fraction=frac)) == VALUE
+        assert fwd(opts=L.make_opts(exp_mode="native", poly_fraction=frac)) == VALUE
 
 
 @pytest.mark.parametrize("name", ["Q", "K", "V", "O", "dO", "LSE", "dQ", "dK", "dV"])
@@ -237,17 +246,16 @@ def test_fwd_fp8_rejects(kw, code):
 
 def test_set_variant():
     lib = L.load()
-    assert lib.attn_set_variant(b"fwd", 3) == OK
-    assert lib.attn_set_variant(b"fwd", 5) == OK
-    assert lib.attn_set_variant(b"fwd", 6) == VALUE
+    assert lib.attn_set_variant(b"fwd", 1) == OK
+    assert lib.attn_set_variant(b"fwd", 2) == VALUE
     assert lib.attn_set_variant(b"fwd", -1) == OK
-    assert lib.attn_set_variant(b"bwd_dq", 2) == OK
-    assert lib.attn_set_variant(b"bwd_dq", 3) == VALUE
-    assert lib.attn_set_variant(b"bwd_dkdv", 6) == VALUE
-    assert lib.attn_set_variant(b"bwd_dkdv", -2) == VALUE
-    assert lib.attn_set_variant(b"fwd_fp8", 1) == OK
-    assert lib.attn_set_variant(b"fwd_fp8", 2) == VALUE
+    assert lib.attn_set_variant(b"bwd_dq", 1) == OK
+    assert lib.attn_set_variant(b"bwd_dq", 2) == VALUE
+    assert lib.attn_set_variant(b"bwd_dq", -2) == VALUE
+    # the measured losers are no longer built
+    assert lib.attn_set_variant(b"bwd_dkdv", 0) == UNSUP
+    assert lib.attn_set_variant(b"fwd_fp8", 0) == UNSUP
     assert lib.attn_set_variant(b"nope", 0) == UNSUP
     assert lib.attn_set_variant(None, 0) == NULL
-    for k in (b"fwd", b"bwd_dq", b"bwd_dkdv", b"fwd_fp8"):
+    for k in (b"fwd", b"bwd_dq"):
         assert lib.attn_set_variant(k, -1) == OK

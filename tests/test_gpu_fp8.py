@@ -265,26 +265,3 @@ def test_fwd_fp8_deterministic():
         o1, l1 = L.attn_fwd_fp8_quantized(b1, 2, 2, 700, 128, causal=causal)
         o2, l2 = L.attn_fwd_fp8_quantized(b1, 2, 2, 700, 128, causal=causal)
         assert bool((o1 == o2).all()) and bool((l1 == l2).all()), "FP8 forward not bitwise repeatable"
-
-
-@pytest.mark.parametrize("S", [64, 130, 777, 1024])
-def test_fwd_fp8_eight_wave_variant_bitwise(S):
-    """The eight-wavefront workgroup (variant 1) gives each wavefront the same
-    rows, tiles and order as the default, so its output is bitwise the
-    default's, also where the last workgroup overhangs the padded length
-    (S = 777 and 130: an odd number of 128-row blocks)."""
-    import torch
-
-    print(f"[fp8 fwd variant 1] S={S}", flush=True)
-    q, k, v, _ = make_qkvdo(1, 3, S, 128, seed=37)
-    buf = L.fp8_quantize(q.cuda(), k.cuda(), v.cuda(), _signs(128).cuda())
-    try:
-        for causal in (False, True):
-            L.set_variant("fwd_fp8", 0)
-            o0, l0 = L.attn_fwd_fp8_quantized(buf, 1, 3, S, 128, causal=causal)
-            L.set_variant("fwd_fp8", 1)
-            o1, l1 = L.attn_fwd_fp8_quantized(buf, 1, 3, S, 128, causal=causal)
-            torch.cuda.synchronize()
-            assert bool((o0 == o1).all()) and bool((l0 == l1).all()), f"causal={causal}: variant 1 differs"
-    finally:
-        L.set_variant("fwd_fp8", -1)

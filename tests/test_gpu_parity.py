@@ -51,6 +51,47 @@ def _gpu(*ts):
     return [t.to("cuda") for t in ts]
 
 
+def _bwd_rounding_bound(q, k, v, do, scale, causal, b, h):
+    """Per-element error bound of the GPU backward pass for head (b, h), from
+    the roundings it makes.  The kernels round P and dS to bf16 (relative
+    2^-9) before the products dV = P^T dO, dK = scale dS^T Q and
+    dQ = scale dS K, and those products then carry an error up to 2^-9 times
+    the matching sum of absolute terms (e.g. |scale| |dS| |K| for dQ).  Delta_i
+    is formed as sum_d dO_id O_id from the bf16 output O, off by up to
+    e_i = 2^-9 sum_d |dO_id O_id|; that enters dS_ij as P_ij e_i and hence dQ_i
+    as |scale| e_i sum_j P_ij |K_j| and dK_j as |scale| sum_i P_ij e_i |Q_i|.
+    The bound is these first-order terms with a factor 2 margin, plus one bf16
+    step of the output (2^-8 |ref|) and the usual 2e-2.  The terms are formed
+    in float32 from the plain definitions."""
+    import torch
+
+    qf, kf, vf, dof = (x[b, h].float() for x in (q, k, v, do))
+    sc = (qf @ kf.T) * scale
+    if causal:
+        sc = sc.masked_fill(torch.ones_like(sc, dtype=torch.bool).triu(1), float("-inf"))
+    pr = torch.softmax(sc, dim=-1)
+    dpr = dof @ vf.T
+    dsr = pr * (dpr - (pr * dpr).sum(-1, keepdim=True))
+    of = pr @ vf
+    e = (dof * of).abs().sum(-1, keepdim=True)  # sum_d |dO O|; times 2^-9 in the bound
+    a = abs(scale)
+    terms = {"dQ": a * (dsr.abs() @ kf.abs() + (pr * e) @ kf.abs()),
+             "dK": a * (dsr.abs().T @ qf.abs() + (pr * e).T @ qf.abs()),
+             "dV": pr.T @ dof.abs()}
+    return {nm: 2.0 * 2.0**-9 * t.double().numpy() for nm, t in terms.items()}
+
+
+def _assert_within_bound(name, got, ref, extra, check_mean=True):
+    err = np.abs(got - ref)
+    bound = O_MAX + 2.0**-8 * np.abs(ref) + extra
+    worst = float(np.max(err - bound))
+    print(f"    {name}: max-abs {err.max():.3e} (|ref| max {np.abs(ref).max():.1f}) mean-abs {err.mean():.3e} "
+          f"worst-vs-bound {worst:.3e}", flush=True)
+    assert worst <= 0.0
+    if check_mean:
+        assert err.mean() <= O_MEAN
+
+
 # ----------------------------------------------------------------------------
 # small and ragged shapes, every element against the float64 oracle
 # ----------------------------------------------------------------------------
@@ -71,16 +112,40 @@ def test_fwd_small(D, S, causal):
     _assert_lse(_np(lse), rl)
 
 
-@pytest.mark.parametrize("exp_mode", ("native", "poly", "mixed"))
+@pytest.mark.parametrize("exp_mode,poly_fraction", (("native", 0.5), ("poly", 0.5), ("mixed", 0.25),
+                                                    ("mixed", 0.5), ("mixed", 0.75)))
 @pytest.mark.parametrize("tau", (0.0, 8.0))
 @pytest.mark.parametrize("causal", (False, True))
-def test_fwd_exp_modes_and_tau(exp_mode, tau, causal):
-    print(f"[fwd modes] exp={exp_mode} tau={tau} causal={causal}", flush=True)
+def test_fwd_exp_modes_and_tau(exp_mode, poly_fraction, tau, causal):
+    print(f"[fwd modes] exp={exp_mode} frac={poly_fraction} tau={tau} causal={causal}", flush=True)
     q, k, v, _ = make_qkvdo(2, 2, 300, 128, seed=7, outlier_frac=0.01)
-    o, lse = L.attn_fwd(*_gpu(q, k, v), causal=causal, exp_mode=exp_mode, rescale_tau=tau)
+    o, lse = L.attn_fwd(*_gpu(q, k, v), causal=causal, exp_mode=exp_mode, rescale_tau=tau,
+                        poly_fraction=poly_fraction)
     ro, rl = oracle.attention_fwd(q, k, v, 1.0 / math.sqrt(128), causal)
     _assert_close("O", _np(o), ro)
     _assert_lse(_np(lse), rl)
+
+
+@pytest.mark.parametrize("tau", (0.0, 3.0, 8.0, 64.0))
+def test_fwd_tau_long_rows_with_outliers(tau):
+    """Unmasked tiles take the exponentials against the running max as it
+    stands and rescale only when a partial row sum of the tile exceeds 2^tau;
+    rows of 4096 keys with the x20 outliers make the running max jump many
+    times, at every tau the ABI accepts (0 .. 64), through the eight-
+    wavefront tile."""
+    print(f"[fwd tau long] tau={tau}", flush=True)
+    q, k, v, _ = make_qkvdo(1, 2, 4100, 128, seed=17, outlier_frac=0.01)
+    L.set_variant("fwd", 1)
+    try:
+        for causal in (False, True):
+            o, lse = L.attn_fwd(*_gpu(q, k, v), causal=causal, rescale_tau=tau)
+            rows = [(0, h, i) for h in range(2) for i in range(0, 4100, 37)] + [(0, 1, 4099)]
+            ro, rl = oracle.attention_fwd_rows(q, k, v, 1.0 / math.sqrt(128), causal, rows)
+            idx = tuple(np.array(rows).T)
+            _assert_close("O rows", o.cpu()[idx].double().numpy(), ro)
+            _assert_lse(lse.cpu()[idx].double().numpy(), rl)
+    finally:
+        L.set_variant("fwd", -1)
 
 
 @pytest.mark.parametrize("scale", (0.0, -0.3, 2.0))
@@ -92,6 +157,35 @@ def test_fwd_unusual_scale(scale):
         ro, rl = oracle.attention_fwd(q, k, v, scale, causal)
         _assert_close("O", _np(o), ro)
         _assert_lse(_np(lse), rl)
+
+
+@pytest.mark.parametrize("scale", (0.0, -0.3, 2.0))
+@pytest.mark.parametrize("D,bwd_mode", ((64, "split"), (128, "split"), (128, "atomic"), (256, "split")))
+def test_bwd_unusual_scale(scale, D, bwd_mode):
+    """Backward with scale 0 (uniform P; dQ = dK = 0 exactly), a negative
+    scale and a large one, against the float64 oracle.  At |scale| = 0.3 and
+    2 the gradients of N(0,1) inputs reach 5 to 90, where a flat 2e-2 is at
+    or below one bf16 step, so every element is held to the rounding bound of
+    the kernels' arithmetic (_bwd_rounding_bound) instead; at scale 0 to the
+    plain tolerances."""
+    print(f"[bwd scale] {scale} D={D} mode={bwd_mode}", flush=True)
+    q, k, v, do = make_qkvdo(1, 2, 200, D, seed=4)
+    qg, kg, vg, dog = _gpu(q, k, v, do)
+    for causal in (False, True):
+        o, lse = L.attn_fwd(qg, kg, vg, scale=scale, causal=causal)
+        dq, dk, dv = L.attn_bwd(qg, kg, vg, o, dog, lse, scale=scale, causal=causal, bwd_mode=bwd_mode)
+        rdq, rdk, rdv = oracle.attention_bwd(q, k, v, do, scale, causal)
+        if scale == 0.0:
+            _assert_close("dQ", _np(dq), rdq)
+            _assert_close("dK", _np(dk), rdk)
+            _assert_close("dV", _np(dv), rdv)
+            assert float(dq.abs().max()) == 0.0 and float(dk.abs().max()) == 0.0
+            continue
+        for h in range(2):
+            bnd = _bwd_rounding_bound(q, k, v, do, scale, causal, 0, h)
+            for nm, g, r in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+                _assert_within_bound(f"{nm} head {h} causal={causal}", _np(g[0, h]), r[0, h], bnd[nm],
+                                     check_mean=False)
 
 
 def test_fwd_deterministic_and_row0():
@@ -242,12 +336,11 @@ def test_workload_full_size(name):
         print(f"  causal={causal}", flush=True)
         o, lse = L.attn_fwd(qg, kg, vg, scale=w.scale, causal=causal)
         torch.cuda.synchronize()
-        _check_fwd_rows(w, q, k, v, o, lse, causal)
+        _check_fwd_rows(w, q, k, v, o, lse, causal, nrows=1024)
         if "bwd" in w.passes:
             dq, dk, dv = L.attn_bwd(qg, kg, vg, o, dog, lse, scale=w.scale, causal=causal)
             torch.cuda.synchronize()
-            heads = [(0, 0)] if w.S > 8192 else [(0, 0), (w.B - 1, w.H - 1)]
-            _check_bwd_heads(w, q, k, v, do, dq, dk, dv, causal, heads)
+            _check_bwd_heads(w, q, k, v, do, dq, dk, dv, causal, [(0, 0), (w.B - 1, w.H - 1)])
         del o, lse
 
 
@@ -280,41 +373,52 @@ def test_bwd_outliers_rounding_bound():
         torch.cuda.synchronize()
         rdq, rdk, rdv = oracle.attention_bwd_f32(q, k, v, do, w.scale, causal, heads=[(0, 0), (0, 1)])
         for n, h in enumerate((0, 1)):
-            qf, kf, vf, dof = (x[0, h].float() for x in (q, k, v, do))
-            sc = (qf @ kf.T) * w.scale
-            if causal:
-                sc = sc.masked_fill(torch.ones_like(sc, dtype=torch.bool).triu(1), float("-inf"))
-            pr = torch.softmax(sc, dim=-1)
-            dpr = dof @ vf.T
-            dsr = pr * (dpr - (pr * dpr).sum(-1, keepdim=True))
-            of = (pr @ vf)
-            e = (dof * of).abs().sum(-1, keepdim=True)  # sum_d |dO O|; times 2^-9 in the bound
-            terms = {"dQ": w.scale * (dsr.abs() @ kf.abs() + (pr * e) @ kf.abs()),
-                     "dK": w.scale * (dsr.abs().T @ qf.abs() + (pr * e).T @ qf.abs()),
-                     "dV": pr.T @ dof.abs()}
+            bnd = _bwd_rounding_bound(q, k, v, do, w.scale, causal, 0, h)
             for nm, g, r in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
-                got = _np(g[0, h])
-                ref = r[n].double().numpy()
-                err = np.abs(got - ref)
-                bound = O_MAX + 2.0**-8 * np.abs(ref) + 2.0 * 2.0**-9 * terms[nm].double().numpy()
-                worst = float(np.max(err - bound))
-                print(f"    {nm} head {h} causal={causal}: max-abs {err.max():.3e} "
-                      f"(|ref| max {np.abs(ref).max():.1f}) mean-abs {err.mean():.3e} worst-vs-bound {worst:.3e}",
-                      flush=True)
-                assert worst <= 0.0 and err.mean() <= O_MEAN
+                _assert_within_bound(f"{nm} head {h} causal={causal}", _np(g[0, h]), r[n].double().numpy(),
+                                     bnd[nm])
 
 
 def test_exp2_eval_against_exact():
+    """The kernels' exp2 against float64 exp2: 1.6e7 evenly spaced points over
+    [-127, 0] plus the positive range the kernels can meet (up to 2^8 with
+    the conditional rescale), and every float32 value in [-1, 0]
+    (1 065 353 217 values, evaluated in chunks on the device and compared
+    there with torch's float64 exp2).  Native: the hardware instruction;
+    poly: the degree-3 fit, max relative error 8.6e-5 by its fit.  Below
+    x = -126 the exact result is a float32 subnormal, which the device
+    flushes to zero: there the error is held to the smallest normal float32
+    (2^-126) in absolute terms, a contribution no softmax row can see next to
+    its largest term, 1."""
     import torch
 
-    x = torch.linspace(-120.0, 8.0, 2_000_001, dtype=torch.float32)
+    x = torch.cat([torch.linspace(-127.0, 0.0, 16_000_001, dtype=torch.float32),
+                   torch.linspace(0.0, 8.0, 1_000_001, dtype=torch.float32)])
     want = oracle.exp2_exact(x.numpy())
+    tiny = 2.0**-126
+    normal = want >= tiny
     for mode, bound in (("native", 2e-6), ("poly", 1.0e-4)):
         y = L.exp2_eval(x.cuda(), mode).cpu().double().numpy()
-        rel = np.max(np.abs(y / want - 1.0))
-        print(f"    exp2 {mode}: max rel err {rel:.3e}", flush=True)
-        assert rel <= bound
+        rel = np.max(np.abs(y[normal] / want[normal] - 1.0))
+        sub = np.max(np.abs(y[~normal] - want[~normal]))
+        print(f"    exp2 {mode} on {x.numel()} points: max rel err {rel:.3e} (normal results), "
+              f"max abs err {sub:.3e} below 2^-126", flush=True)
+        assert rel <= bound and sub <= tiny
+    # every float32 in [-1, 0]: the bit patterns of [0, 1] with the sign bit set
+    top = 0x3F800000  # bits of 1.0f
+    chunk = 1 << 26
+    worst = {"native": 0.0, "poly": 0.0}
+    for start in range(0, top + 1, chunk):
+        bits = torch.arange(start, min(start + chunk, top + 1), dtype=torch.int32, device="cuda")
+        xs = (bits | torch.tensor(-0x80000000, dtype=torch.int32, device="cuda")).view(torch.float32)
+        ref = torch.exp2(xs.double())
+        for mode in worst:
+            y = L.exp2_eval(xs, mode).double()
+            worst[mode] = max(worst[mode], float((y / ref - 1.0).abs().max()))
+    print(f"    exp2 on every float32 in [-1, 0]: max rel err {worst}", flush=True)
+    assert worst["native"] <= 2e-6 and worst["poly"] <= 1.0e-4
     assert float(L.exp2_eval(torch.zeros(1, device="cuda"), "poly").item()) == 1.0
+    assert float(L.exp2_eval(torch.full((1,), -0.0, device="cuda"), "poly").item()) == 1.0
 
 
 # ----------------------------------------------------------------------------
@@ -396,15 +500,12 @@ def test_splitkv_workload_full_size(name):
 
 
 # ----------------------------------------------------------------------------
-# kernel variants kept for measurement (tile shapes, wavefronts per workgroup,
-# load schedules; fwd 1 / 5 are the eight-wavefront cooperative tiles, fwd 3
-# the four-wavefront tile the default takes up to S = 4096, dQ 2 the
-# four-wavefront dQ tile):
+# kernel variants kept for measurement (fwd 1: the eight-wavefront cooperative
+# tile at every length; dQ 1: the four-wavefront dQ tile):
 # each against the float64 oracle, ragged length, both causal settings
 # ----------------------------------------------------------------------------
 
-VARIANTS = [("fwd", v) for v in range(1, 6)] + [("bwd_dkdv", v) for v in range(1, 6)] + \
-           [("bwd_dq", v) for v in range(1, 3)]
+VARIANTS = [("fwd", 1), ("bwd_dq", 1)]
 
 
 @pytest.mark.parametrize("kernel,variant", VARIANTS)
