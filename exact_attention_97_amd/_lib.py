@@ -29,7 +29,7 @@ EXPORTS = (
     "attn_exp2_eval", "attn_prof_enable", "attn_prof_reset", "attn_prof_collect", "attn_version",
     "attn_fwd_splitkv_workspace_bytes", "attn_fwd_splitkv",
     "attn_fp8_buffer_bytes", "attn_fp8_buffer_offsets", "attn_fp8_quantize", "attn_fwd_fp8",
-    "attn_set_variant",
+    "attn_set_variant", "attn_fp8_dot_eval",
 )
 FP8_REGIONS = ("q8", "k8", "v8t", "qs", "ks", "vs", "scratch")
 
@@ -92,6 +92,8 @@ def load():
     lib.attn_fp8_quantize.restype = i
     lib.attn_fwd_fp8.argtypes = [vp, sz, vp, vp, i, i, i, i, f, i, optp, vp]
     lib.attn_fwd_fp8.restype = i
+    lib.attn_fp8_dot_eval.argtypes = [vp, vp, vp, ctypes.c_long, vp]
+    lib.attn_fp8_dot_eval.restype = i
     lib.attn_set_variant.argtypes = [ctypes.c_char_p, i]
     lib.attn_set_variant.restype = i
     _lib = lib
@@ -198,7 +200,7 @@ def fp8_buffer_views(buf, B, H, S, D):
     Sp = (S + 127) // 128 * 128
     BH = B * H
     shapes = {"q8": ((BH, Sp, D), torch.uint8), "k8": ((BH, Sp, D), torch.uint8), "v8t": ((BH, D, Sp), torch.uint8),
-              "qs": ((BH, Sp), torch.float32), "ks": ((BH, Sp // 64), torch.float32), "vs": ((BH, D), torch.float32)}
+              "qs": ((BH, Sp), torch.float32), "ks": ((BH,), torch.float32), "vs": ((BH, D), torch.float32)}
     out = {}
     for n, name in enumerate(FP8_REGIONS[:6]):
         shape, dt = shapes[name]
@@ -281,6 +283,23 @@ def attn_bwd(q, k, v, o, do, lse, scale=None, causal=False, bwd_mode="split",
                                     B, H, S, D, float(scale), int(bool(causal)), ctypes.byref(opts),
                                     _stream_ptr(stream)))
     return dq, dk, dv
+
+
+def fp8_dot_eval(a, bt, stream=None):
+    """The FP8 forward's score product on E4M3 codes: a, bt uint8 device tensors
+    [n, 32, 128] (bt holds B transposed); returns C = a @ bt^T, fp32 [n, 32, 32]."""
+    import torch
+
+    for t in (a, bt):
+        if not t.is_cuda or t.dtype != torch.uint8 or not t.is_contiguous() or t.dim() != 3 \
+                or tuple(t.shape[1:]) != (32, 128):
+            raise ValueError("a and bt must be contiguous uint8 device tensors [n, 32, 128]")
+    if a.shape != bt.shape:
+        raise ValueError("a and bt must have the same shape")
+    c = torch.empty((a.shape[0], 32, 32), dtype=torch.float32, device=a.device)
+    _check("attn_fp8_dot_eval", load().attn_fp8_dot_eval(a.data_ptr(), bt.data_ptr(), c.data_ptr(), a.shape[0],
+                                                         _stream_ptr(stream)))
+    return c
 
 
 def exp2_eval(x, mode="native", stream=None):

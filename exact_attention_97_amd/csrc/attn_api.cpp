@@ -33,6 +33,9 @@ attn_status check_shape(int B, int H, int S, int D) {
 // tau <= 64 the fp32 row sum and accumulators stay below 2^64 * 2^31 * |v|,
 // far from fp32 overflow (2^128), for every supported length.
 constexpr float kMaxTau = 64.0f;
+// The FP8 forward rounds unnormalised probabilities (at most 2^tau) to E4M3,
+// whose largest value is 448.
+constexpr float kMaxTauFp8 = 8.0f;
 
 attn_status read_opts(const attn_opts* in, attn_opts* out) {
   attn_default_opts(out);
@@ -363,9 +366,22 @@ attn_status attn_fwd_fp8(const void* buf, size_t buf_bytes, void* O, float* LSE,
   attn97::Fp8Buf f;
   const size_t need = attn97::fp8_layout(B, H, S, D, const_cast<void*>(buf), &f);
   if (buf == nullptr || buf_bytes < need || misaligned(buf, 256)) return ATTN_ERR_WORKSPACE;
+  // P is stored in E4M3, whose largest finite value is 448; unnormalised
+  // probabilities stay below 2^tau, so the FP8 kernel applies tau <= 8
+  // (2^8 = 256 < 448) whatever larger value the options give.
+  const float tau = o.rescale_tau < kMaxTauFp8 ? o.rescale_tau : kMaxTauFp8;
   hipError_t e = attn97::launch_fwd_fp8(f, O, LSE, B, H, S, fabsf(scale) * kLog2eHost,
-                                        (scale < 0.0f) ? 0x80808080u : 0u, o.rescale_tau, causal ? 1 : 0,
-                                        (hipStream_t)stream);
+                                        (scale < 0.0f) ? 0x80808080u : 0u, tau, causal ? 1 : 0, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_fp8_dot_eval(const void* A, const void* Bt, float* C, long nblk, void* stream) {
+  if (nblk < 0) return ATTN_ERR_SHAPE;
+  if (nblk == 0) return ATTN_OK;
+  if (!A || !Bt || !C) return ATTN_ERR_NULL;
+  if (misaligned(A, 16) || misaligned(Bt, 16) || misaligned(C, 16)) return ATTN_ERR_ALIGN;
+  if ((double)nblk * 32 * 128 > 9.0e15) return ATTN_ERR_SHAPE;
+  hipError_t e = attn97::launch_fp8_dot_eval(A, Bt, C, nblk, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -9,11 +9,13 @@
 //
 // Two steps:
 //  * quantize: Q and K rows transformed (a 128-point fast Walsh-Hadamard
-//    transform in float64 registers, one row per four lanes) and rounded to E4M3 with one
-//    scale per Q row and one per 64-key K tile; V rounded with one scale per
-//    column (a column-maximum kernel runs first) and stored
+//    transform in float64 registers, one row per four lanes) and rounded to
+//    E4M3 with one scale per Q row and one per (batch, head) for K (a pass
+//    over the transformed K finds the head's maximum first); V rounded with
+//    one scale per column (a column-maximum kernel runs first) and stored
 //    transposed, keys permuted inside each 64-key group so that the PV
-//    operand of a lane is 32 contiguous bytes.
+//    operand of a lane is 32 contiguous bytes.  Every code is the rounding
+//    of the float64 quotient x * 448 / max|x|, straight to E4M3.
 //  * forward: the online-softmax kernel of the bf16 path with both products
 //    on v_mfma_f32_32x32x64_f8f6f4 (twice the bf16 MFMA rate): S^T = K Q^T
 //    and O^T += V^T P^T with P rounded to E4M3 in registers.  The product
@@ -43,8 +45,27 @@ constexpr float kE4M3Max = 448.0f;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
-// clamp to the finite E4M3 range (the conversion turns larger values into NaN)
-__device__ __forceinline__ float clamp448(float x) { return __builtin_fminf(__builtin_fmaxf(x, -kE4M3Max), kE4M3Max); }
+// y (|y| <= 448) rounded to the nearest E4M3 value, ties to even, straight
+// from float64 (no intermediate float32 rounding, which could land a value
+// near a midpoint exactly on it).  E4M3 values are multiples of 2^(E - 3) in
+// the binade [2^E, 2^(E+1)) for E >= -6, and of 2^-9 below 2^-6, so the
+// value is rint(|y| / q) q with q that quantum (a power of two: both scalings
+// are exact).  The result is exactly representable in float32 and in E4M3;
+// its sign is y's (a negative value that rounds to zero keeps the sign).
+__device__ __forceinline__ float round_e4m3_f64(double y) {
+  const double a = __builtin_fabs(y);
+  const int e = __builtin_amdgcn_frexp_exp(a);  // a = f 2^e, f in [0.5, 1): E = e - 1
+  const int q = (e - 1 > -6 ? e - 1 : -6) - 3;
+  const float r = (float)__builtin_ldexp(__builtin_rint(__builtin_ldexp(a, -q)), q);
+  return y < 0.0 ? -r : r;
+}
+
+// E4M3 code of x relative to a group maximum amax > 0: x * 448 / amax as a
+// float64 quotient (x * 448 is exact for the inputs here; the division is
+// IEEE, correctly rounded), rounded straight to E4M3.  amax = 0: code 0.
+__device__ __forceinline__ float e4m3_value_of(double x, double amax) {
+  return amax > 0.0 ? round_e4m3_f64((x * (double)kE4M3Max) / amax) : 0.0f;
+}
 
 // four floats to four E4M3 bytes (round to nearest even), byte i = x_i
 __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
@@ -89,9 +110,15 @@ __device__ __forceinline__ double lane_xor_f64(double x, bool upper) {
 }
 
 // ---------------------------------------------------------------------------
-// Quantize Q and K.  Grid (Sp / 64, B*H, 2): z = 0 Q, z = 1 K; four
-// wavefronts of 16 rows; lane l handles quarter qd = l >> 4 (elements
-// 32 qd .. 32 qd + 31) of row l & 15.  Rows past S are zero (Q scale 1).
+// Transform and quantize Q and K.  Grid (Sp / 64, B*H, NZ), four wavefronts
+// of 16 rows; lane l handles quarter qd = l >> 4 (elements 32 qd .. 32 qd +
+// 31) of row l & 15.  Rows past S are zero (Q scale 1).
+//
+// PASS 0 (NZ = 1, K only): the maximum of |transformed K| of each head, by a
+// workgroup reduction and one 64-bit atomic maximum per workgroup into the
+// scratch region (non-negative doubles order like their bit patterns).
+// PASS 1 (NZ = 2; z = 0 Q, z = 1 K): codes and scales; Q rows against their
+// own maximum, K rows against their head's maximum from pass 0.
 //
 // The transform runs in float64: its outputs are sums of 128 bf16 values
 // with signs, which float64 holds exactly (float32 would round them once
@@ -100,11 +127,12 @@ __device__ __forceinline__ double lane_xor_f64(double x, bool upper) {
 // quarters are exchanges between lanes (H_2n x = [H_n (a + b); H_n (a - b)]
 // for x = [a; b]), the other five run inside each lane.
 // ---------------------------------------------------------------------------
+template <int PASS>
 __global__ __launch_bounds__(256) void fp8_qk_quant_kernel(const uint16_t* __restrict__ Q,
                                                            const uint16_t* __restrict__ K,
                                                            const float* __restrict__ signs, Fp8Buf f, int S) {
   __shared__ double wave_max[4];
-  const int which = blockIdx.z;
+  const int which = PASS == 0 ? 1 : blockIdx.z;
   const int bh = blockIdx.y;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -113,8 +141,6 @@ __global__ __launch_bounds__(256) void fp8_qk_quant_kernel(const uint16_t* __res
   const int row = blockIdx.x * 64 + 16 * wave + (lane & 15);
   const int Sp = f.Sp;
   const uint16_t* src = (which ? K : Q) + (size_t)bh * S * FD;
-  // the V column maxima start at zero (fp8_v_amax_kernel runs after this kernel)
-  if (blockIdx.x == 0 && which == 0 && tid < FD) f.vpart[(size_t)bh * FD + tid] = 0.0f;
 
   double x[32];
   if (row < S) {
@@ -174,48 +200,55 @@ __global__ __launch_bounds__(256) void fp8_qk_quant_kernel(const uint16_t* __res
   for (int i = 0; i < 32; ++i) amax = __builtin_fmax(amax, __builtin_fabs(x[i]));
   amax = __builtin_fmax(amax, __shfl_xor(amax, 16));  // the row's four quarters
   amax = __builtin_fmax(amax, __shfl_xor(amax, 32));
-  if (which == 1) {  // K: one scale per 64-key tile (all four wavefronts)
+  double* kmax = reinterpret_cast<double*>(f.kmax);
+  if constexpr (PASS == 0) {  // K: this workgroup's 64 rows, then the head
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) amax = __builtin_fmax(amax, __shfl_xor(amax, o));
     if (lane == 0) wave_max[wave] = amax;
     __syncthreads();
-    amax = __builtin_fmax(__builtin_fmax(wave_max[0], wave_max[1]), __builtin_fmax(wave_max[2], wave_max[3]));
-  }
-  // the transformed row is x * norm; its scale is max|x * norm| / 448 and its
-  // codes are E4M3(x * norm / scale) = E4M3(x * 448 / max|x|).  The quotient
-  // is formed in float64 as x * (448 / max|x|) and then rounded to float32:
-  // a quotient exactly halfway between two codes has at most 5 significant
-  // bits, and the float64 error (below 2^-52 relative) cannot move it off
-  // that float32 value, so it stays halfway (and goes to the even code)
-  const float sc = amax > 0.0 ? (float)(amax * norm / (double)kE4M3Max) : 1.0f;
-  const double r = amax > 0.0 ? (double)kE4M3Max / amax : 0.0;
-
-  uint8_t* dst = (which ? f.k8 : f.q8) + ((size_t)bh * Sp + row) * FD + 32 * qd;
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    u32x4 w;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int d = 16 * c + 4 * e;
-      float y[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) y[u] = clamp448((float)(x[d + u] * r));
-      w[e] = pack_e4m3x4(y[0], y[1], y[2], y[3]);
+    if (tid == 0) {
+      const double m = __builtin_fmax(__builtin_fmax(wave_max[0], wave_max[1]), __builtin_fmax(wave_max[2], wave_max[3]));
+      atomicMax(reinterpret_cast<unsigned long long*>(kmax + bh), __builtin_bit_cast(unsigned long long, m));
     }
-    *reinterpret_cast<u32x4*>(dst + 16 * c) = w;
+    return;
+  } else {
+    if (which == 1) amax = kmax[bh];  // the head's maximum
+    // the transformed row is x * norm; its scale is max|x * norm| / 448 and
+    // its codes are E4M3(x * norm / scale) = E4M3(x * 448 / max|x|), in which
+    // the factor norm cancels
+    const float sc = amax > 0.0 ? (float)(amax * norm / (double)kE4M3Max) : 1.0f;
+    uint8_t* dst = (which ? f.k8 : f.q8) + ((size_t)bh * Sp + row) * FD + 32 * qd;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 16 * c + 4 * e;
+        w[e] = pack_e4m3x4(e4m3_value_of(x[d], amax), e4m3_value_of(x[d + 1], amax), e4m3_value_of(x[d + 2], amax),
+                           e4m3_value_of(x[d + 3], amax));
+      }
+      *reinterpret_cast<u32x4*>(dst + 16 * c) = w;
+    }
+    if (which == 0) {
+      if (qd == 0) f.qs[(size_t)bh * Sp + row] = sc;
+    } else if (blockIdx.x == 0 && tid == 0) {
+      f.ks[bh] = sc;
+    }
   }
-  if (which == 0) {
-    if (qd == 0) f.qs[(size_t)bh * Sp + row] = sc;
-  } else if (tid == 0) {
-    f.ks[(size_t)bh * (Sp / FBC) + blockIdx.x] = sc;
-  }
+}
+
+// The scratch maxima start at zero: V's column maxima and K's head maxima.
+__global__ __launch_bounds__(256) void fp8_clear_kernel(Fp8Buf f, int BH) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < BH * FD) f.vpart[i] = 0.0f;
+  if (i < BH) reinterpret_cast<double*>(f.kmax)[i] = 0.0;
 }
 
 // Column maxima of V.  Grid (Sp / 128, B*H), 256 threads: thread t reads
 // the 16-byte chunk t % 16 (columns 8 (t % 16) .. + 7) of rows t / 16 + 16 i
 // of the 128-row chunk; the 16 row groups reduce through LDS, and each
 // column's maximum goes into the scratch region with an integer atomicMax
-// (non-negative floats order like their bit patterns).  fp8_qk_quant_kernel,
+// (non-negative floats order like their bit patterns).  fp8_clear_kernel,
 // launched before on the same stream, zeroed those maxima.
 __global__ __launch_bounds__(256) void fp8_v_amax_kernel(const uint16_t* __restrict__ V, Fp8Buf f, int S) {
   __shared__ float part[16][FD];
@@ -270,16 +303,16 @@ __global__ __launch_bounds__(256) void fp8_v_quant_kernel(const uint16_t* __rest
   const int d = t & 127, kb = t >> 7;
   const float m = __builtin_bit_cast(float, reinterpret_cast<const unsigned int*>(f.vpart)[(size_t)bh * FD + d]);
   if (tile == 0 && kb == 0) f.vs[(size_t)bh * FD + d] = m > 0.0f ? m / kE4M3Max : 1.0f;
-  // v * 448 / m as in the Q / K quantizer: float64 product with the
-  // reciprocal, then float32 (exact halfway cases stay exact)
-  const double r = m > 0.0f ? (double)kE4M3Max / (double)m : 0.0;
+  // v * 448 / m as in the Q / K quantizer: float64 quotient, rounded
+  // straight to E4M3
+  const double md = (double)m;
   u32x4 w[2];  // [h]: words r4 = 0..3
 #pragma unroll
   for (int g8 = 0; g8 < 8; ++g8) {  // key group g = 8 kb + g8: keys 4 g .. 4 g + 3
     const int h = g8 & 1, r4 = g8 >> 1, key0 = 32 * kb + 4 * g8;
     float v[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = clamp448((float)((double)bf16_lo((uint32_t)tv[key0 + e][d]) * r));
+    for (int e = 0; e < 4; ++e) v[e] = e4m3_value_of((double)bf16_lo((uint32_t)tv[key0 + e][d]), md);
     w[h][r4] = pack_e4m3x4(v[0], v[1], v[2], v[3]);
   }
   uint8_t* dst = f.v8t + ((size_t)bh * FD + d) * f.Sp + k0;
@@ -377,7 +410,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_fp8_kernel(Fp8Buf f, uint
   const int qread = min(qrow, Sp - 1);
   const uint8_t* Kh = f.k8 + (size_t)bh * Sp * FD;
   const uint8_t* Vh = f.v8t + (size_t)bh * FD * Sp;
-  const float* ksh = f.ks + (size_t)bh * (Sp / FBC);
 
   // Q^T operand: lane holds bytes 64 t + 32 hh .. + 31 of row qrow
   i32x8 qreg[2];
@@ -392,7 +424,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_fp8_kernel(Fp8Buf f, uint
       qreg[t] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
     }
   }
-  const float cq = C * f.qs[(size_t)bh * Sp + qread];  // scale * log2(e) * this row's Q scale
+  // scale * log2(e) * this row's Q scale * the head's K scale: the score
+  // factor of every tile (log2 units)
+  const float ct = C * f.qs[(size_t)bh * Sp + qread] * f.ks[bh];
 
   const int kend = causal ? min(S, q0 + BR) : S;
   const int nkt = (kend + FBC - 1) / FBC;
@@ -437,10 +471,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_fp8_kernel(Fp8Buf f, uint
   float m_run = kNegInf;  // running max in log2 units
   float l_part = 0.0f;    // this lane's partial row sum (unrounded P)
 
-  // the tile's K scale is loaded an iteration ahead: the wait for all loads
-  // that ends each iteration then covers it (a wait for it inside the tile
-  // would also wait for the tile loads issued after it)
-  float ks_cur = ksh[0];
   issue(-2, std::integral_constant<int, 0>{});
   issue(-1, std::integral_constant<int, 1>{});
   wait_vm_lds<0>();
@@ -450,13 +480,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_fp8_kernel(Fp8Buf f, uint
   wait_vm_lds<63>();
   barrier_keep_loads();
 
-  auto step = [&](auto maskc, auto P, int kt, float ks_t, f32x16(&scur)[2], f32x16(&snext)[2]) {
+  auto step = [&](auto maskc, auto P, int kt, f32x16(&scur)[2], f32x16(&snext)[2]) {
     constexpr int par = decltype(P)::value;  // kt & 1
     constexpr bool MASK = decltype(maskc)::value;
     // distinct code at the top of each copy: keeps the compiler from hoisting
     // the two copies' common reads out of the masked / unmasked branch
     tile_marker<MASK>();
-    const float ct = cq * ks_t;  // score factor of this tile (log2 units)
     // Region 1 (raised wave priority): the next tile's four score MFMAs
     // interleaved with this tile's softmax.  Back to back, each MFMA would
     // hold the wavefront until the previous one leaves the matrix pipe.
@@ -517,15 +546,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_fp8_kernel(Fp8Buf f, uint
   };
 
   auto iteration = [&](int kt, auto P, f32x16(&scur)[2], f32x16(&snext)[2]) {
-    const float ks_t = ks_cur;
-    ks_cur = kt + 1 < nkt ? ksh[kt + 1] : 0.0f;  // used by the next iteration
     issue(kt, P);
     __builtin_amdgcn_sched_barrier(0);
     if (kt < nkt_w) {
       if (kt < nfull)
-        step(std::false_type{}, P, kt, ks_t, scur, snext);
+        step(std::false_type{}, P, kt, scur, snext);
       else
-        step(std::true_type{}, P, kt, ks_t, scur, snext);
+        step(std::true_type{}, P, kt, scur, snext);
     }
     wait_vm_lds<0>();
     barrier_keep_loads();
@@ -555,6 +582,32 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_fp8_kernel(Fp8Buf f, uint
   }
 }
 
+// ---------------------------------------------------------------------------
+// Diagnostic: the forward kernel's score product on given codes.  Wavefront
+// w computes C_w = A_w B_w for an A_w of 32 x 128 codes (row-major) and a
+// B_w of 128 x 32 codes given transposed (Bt_w, 32 x 128, row-major), as
+// two chained v_mfma_f32_32x32x64_f8f6f4 with the operand layout of
+// fwd_fp8_kernel's S^T = K Q^T (lane half h and byte j of both operands
+// carry contraction index 64 t + 32 h + j).  C_w is 32 x 32 fp32, row-major.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fp8_dot_eval_kernel(const uint8_t* __restrict__ A,
+                                                           const uint8_t* __restrict__ Bt, float* __restrict__ C,
+                                                           long nblk) {
+  const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= nblk) return;  // whole wavefronts
+  const int lane = threadIdx.x & 63, hh = lane >> 5, c32 = lane & 31;
+  const uint8_t* a = A + (size_t)w * 32 * FD + (size_t)c32 * FD;
+  const uint8_t* b = Bt + (size_t)w * 32 * FD + (size_t)c32 * FD;
+  f32x16 acc = f32x16{};
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    acc = mfma_fp8(lds_frag32(a + 64 * t + 32 * hh, a + 64 * t + 32 * hh + 16),
+                   lds_frag32(b + 64 * t + 32 * hh, b + 64 * t + 32 * hh + 16), acc);
+  float* c = C + (size_t)w * 32 * 32;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) c[(8 * (r >> 2) + 4 * hh + (r & 3)) * 32 + c32] = acc[r];
+}
+
 }  // namespace
 
 size_t fp8_layout(int B, int H, int S, int D, void* base, Fp8Buf* f) {
@@ -562,13 +615,14 @@ size_t fp8_layout(int B, int H, int S, int D, void* base, Fp8Buf* f) {
   auto r256 = [](size_t n) { return (n + 255) & ~(size_t)255; };
   const size_t BH = (size_t)B * H;
   const int Sp = (S + FBR - 1) / FBR * FBR;
-  const size_t sz[7] = {r256(BH * Sp * FD),                      // q8
-                        r256(BH * Sp * FD),                      // k8
-                        r256(BH * FD * Sp),                      // v8t
-                        r256(BH * Sp * sizeof(float)),           // qs
-                        r256(BH * (Sp / FBC) * sizeof(float)),   // ks
-                        r256(BH * FD * sizeof(float)),           // vs
-                        r256(BH * (Sp / 128) * FD * sizeof(float))};  // vpart
+  const size_t vmax_bytes = r256(BH * FD * sizeof(float));
+  const size_t sz[7] = {r256(BH * Sp * FD),             // q8
+                        r256(BH * Sp * FD),             // k8
+                        r256(BH * FD * Sp),             // v8t
+                        r256(BH * Sp * sizeof(float)),  // qs
+                        r256(BH * sizeof(float)),       // ks
+                        r256(BH * FD * sizeof(float)),  // vs
+                        vmax_bytes + r256(BH * sizeof(double))};  // scratch: V column maxima, K head maxima
   size_t off[7], total = 0;
   for (int i = 0; i < 7; ++i) {
     off[i] = total;
@@ -584,6 +638,7 @@ size_t fp8_layout(int B, int H, int S, int D, void* base, Fp8Buf* f) {
     f->ks = reinterpret_cast<float*>(p + off[4]);
     f->vs = reinterpret_cast<float*>(p + off[5]);
     f->vpart = reinterpret_cast<float*>(p + off[6]);
+    f->kmax = reinterpret_cast<void*>(p + off[6] + vmax_bytes);
     for (int i = 0; i < 7; ++i) f->offsets[i] = off[i];
   }
   return total;
@@ -593,11 +648,20 @@ hipError_t launch_fp8_quantize(const void* Q, const void* K, const void* V, cons
                                int B, int H, int S, hipStream_t st) {
   const int BH = B * H;
   prof_begin(KID_FP8_QUANT, st);
-  hipLaunchKernelGGL(fp8_qk_quant_kernel, dim3(f.Sp / 64, BH, 2), dim3(256), 0, st, (const uint16_t*)Q,
+  hipLaunchKernelGGL(fp8_clear_kernel, dim3((BH * FD + 255) / 256), dim3(256), 0, st, f, BH);
+  hipLaunchKernelGGL(fp8_qk_quant_kernel<0>, dim3(f.Sp / 64, BH, 1), dim3(256), 0, st, (const uint16_t*)Q,
                      (const uint16_t*)K, signs, f, S);
   hipLaunchKernelGGL(fp8_v_amax_kernel, dim3(f.Sp / 128, BH), dim3(256), 0, st, (const uint16_t*)V, f, S);
+  hipLaunchKernelGGL(fp8_qk_quant_kernel<1>, dim3(f.Sp / 64, BH, 2), dim3(256), 0, st, (const uint16_t*)Q,
+                     (const uint16_t*)K, signs, f, S);
   hipLaunchKernelGGL(fp8_v_quant_kernel, dim3(f.Sp / 64, BH), dim3(256), 0, st, (const uint16_t*)V, f, S);
   prof_end(KID_FP8_QUANT, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_dot_eval(const void* A, const void* Bt, float* C, long nblk, hipStream_t st) {
+  hipLaunchKernelGGL(fp8_dot_eval_kernel, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, st, (const uint8_t*)A,
+                     (const uint8_t*)Bt, C, nblk);
   return hipGetLastError();
 }
 

@@ -170,24 +170,18 @@ struct FwdWave {
     }
   }
 
-  // The optimistic form of region 1 keeps the tile's scores live until its
-  // check; with more than two 32-key blocks per tile (D = 64, 128-key tiles)
-  // that does not fit the register budget, and every tile takes the exact
-  // form.
-  static constexpr bool kOptimistic = NKB <= 2;
-
-  // Region 1, exact form (masked tiles: causal diagonal, ragged end): mask,
-  // exact row max and the rescale decision first, then the next tile's
-  // scores on the MFMA unit interleaved with this tile's exponentials on the
-  // VALU.  Returns P (bf16) and the rescale decision for region 2.  The next
-  // tile's scores are computed even after the wave's last tile (from a stale
-  // buffer, never used) so that region 1 has no branch.
+  // Region 1 of one tile (no branches): mask (diagonal or ragged tiles),
+  // row max and the rescale decision first, then the next tile's scores on
+  // the MFMA unit interleaved with this tile's exponentials on the VALU.
+  // Returns P (bf16) and the rescale decision for region 2.  The next tile's
+  // scores are computed even after the wave's last tile (from a stale buffer,
+  // never used) so that region 1 has no branch.
   template <bool MASK>
-  __device__ __forceinline__ static void region1_exact(const uint16_t* knext, const FwdOffsets<Cfg>& of,
-                                                        const bf16x8 (&qreg)[NKS], f32x16 (&scur)[NKB],
-                                                        f32x16 (&snext)[NKB], float& m_run, float& l_part, int k0,
-                                                        int lim, int hh, float C, float tau, bf16x8 (&pb)[2 * NKB],
-                                                        bool& grow, float& alpha) {
+  __device__ __forceinline__ static void region1(const uint16_t* knext, const FwdOffsets<Cfg>& of,
+                                                 const bf16x8 (&qreg)[NKS], f32x16 (&scur)[NKB],
+                                                 f32x16 (&snext)[NKB], float& m_run, float& l_part, int k0, int lim,
+                                                 int hh, float C, float tau, bf16x8 (&pb)[2 * NKB], bool& grow,
+                                                 float& alpha) {
     const float mx = tile_max<MASK>(scur, k0, lim, hh);
     const float mxs = (mx == kNegInf) ? kNegInf : mx * C;
     const float m_new = __builtin_fmaxf(m_run, mxs);
@@ -211,42 +205,6 @@ struct FwdWave {
     __builtin_amdgcn_s_setprio(0);
   }
 
-  // Region 1 of an unmasked tile, optimistic form.  The exponentials use the
-  // running max as it stands, with no row max taken first; every probability
-  // of the tile is at most its lane's partial row sum over the tile, so when
-  // no partial sum exceeds thr = 2^tau no probability does either and the
-  // running max may stay (the conditional rescaling condition).  Otherwise
-  // (rare after the first tiles, and always on a wave's first tile, where the
-  // running max is -inf and every partial sum is infinite) the exact tile max
-  // is taken, the accumulator and row sum are rescaled and the tile's
-  // exponentials are recomputed.  `!(l <= thr)` also catches a NaN.
-  __device__ __forceinline__ static void region1_fast(const uint16_t* knext, const FwdOffsets<Cfg>& of,
-                                                      const bf16x8 (&qreg)[NKS], f32x16 (&scur)[NKB],
-                                                      f32x16 (&snext)[NKB], float& m_run, float& l_part, float C,
-                                                      float thr, bf16x8 (&pb)[2 * NKB], f32x16 (&oacc)[NDB]) {
-    float l_tile = 0.0f;
-    __builtin_amdgcn_s_setprio(1);
-    scores(knext, of, qreg, snext);
-    probs<false>(scur, C, m_run, pb, l_tile);
-    region1_schedule<7>();
-#pragma unroll
-    for (int t = 0; t < 2 * NKB; ++t) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pb[t])));
-    asm volatile("" ::"v"(l_tile));
-    __builtin_amdgcn_s_setprio(0);
-    if (__any(!(l_tile <= thr))) {
-      const float mx = tile_max<false>(scur, 0, 0, 0);
-      const float m_new = __builtin_fmaxf(m_run, mx * C);
-      const float alpha = exp2_native(m_run - m_new);  // 0 while m_run is -inf (l_part and oacc are 0 then)
-      l_part *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-      m_run = m_new;
-      l_tile = 0.0f;
-      probs<false>(scur, C, m_run, pb, l_tile);
-    }
-    l_part += l_tile;
-  }
-
   // P V with its transpose loads: the reads run eight ahead (two per MFMA
   // operand, so three MFMAs of look-ahead under the exact LDS wait counts).
   __device__ __forceinline__ static void region2(const uint16_t* vcur, const FwdOffsets<Cfg>& of,
@@ -262,23 +220,20 @@ struct FwdWave {
     __builtin_amdgcn_sched_group_barrier(0x008, PVA / 2, 1);
   }
 
-  // One whole tile: region 1 then region 2.  thr = 2^tau.
+  // One whole tile: region 1, the (rare) rescale of the output accumulator,
+  // region 2.
   template <bool MASK>
   __device__ __forceinline__ static void step(const uint16_t* knext, const uint16_t* vcur, const FwdOffsets<Cfg>& of,
                                               const bf16x8 (&qreg)[NKS], f32x16 (&scur)[NKB],
                                               f32x16 (&snext)[NKB], f32x16 (&oacc)[NDB], float& m_run,
-                                              float& l_part, int k0, int lim, int hh, float C, float tau, float thr) {
+                                              float& l_part, int k0, int lim, int hh, float C, float tau) {
     bf16x8 pb[2 * NKB];
-    if constexpr (MASK || !kOptimistic) {
-      bool grow;
-      float alpha;
-      region1_exact<MASK>(knext, of, qreg, scur, snext, m_run, l_part, k0, lim, hh, C, tau, pb, grow, alpha);
-      if (grow) {
+    bool grow;
+    float alpha;
+    region1<MASK>(knext, of, qreg, scur, snext, m_run, l_part, k0, lim, hh, C, tau, pb, grow, alpha);
+    if (grow) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-      }
-    } else {
-      region1_fast(knext, of, qreg, scur, snext, m_run, l_part, C, thr, pb, oacc);
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
     }
     region2(vcur, of, pb, oacc);
   }
@@ -404,7 +359,6 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
   float m_run = kNegInf;  // running max, in units of log2 (scores times C)
   float l_part = 0.0f;    // this lane's partial row sum
-  const float thr = exp2_native(tau);  // bound on one tile's partial row sum (unmasked tiles)
 
   FwdOffsets<Cfg> of;
   of.init(wave, lane);
@@ -464,10 +418,10 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
     if (kt < nkt_w) {
       if (kt < nfull)
         W::template step<false>(kbuf(kn), vbuf(vc), of, qreg, scur, snext, oacc, m_run, l_part, kb + kt * BC, lim,
-                                hh, C, tau, thr);
+                                hh, C, tau);
       else
         W::template step<true>(kbuf(kn), vbuf(vc), of, qreg, scur, snext, oacc, m_run, l_part, kb + kt * BC, lim,
-                               hh, C, tau, thr);
+                               hh, C, tau);
     }
     wait_loads(n_last);
     barrier_keep_loads();

@@ -73,15 +73,17 @@ struct Fp8Buf {
   uint8_t* k8;   // [B*H, Sp, 128] E4M3, transformed K
   uint8_t* v8t;  // [B*H, 128, Sp] E4M3, V transposed, keys permuted in 64-groups
   float* qs;     // [B*H, Sp] per-row Q scales
-  float* ks;     // [B*H, Sp / 64] per-tile K scales
+  float* ks;     // [B*H] per-head K scales
   float* vs;     // [B*H, 128] per-column V scales
-  float* vpart;  // scratch; its first B*H*128 floats hold V's column maxima
+  float* vpart;  // scratch: V's column maxima, [B*H, 128] float
+  void* kmax;    // scratch: K's head maxima (of the transformed rows), [B*H] double
   size_t offsets[7];
 };
 // Byte size of the buffer; fills *f from `base` when f is not null.
 size_t fp8_layout(int B, int H, int S, int D, void* base, Fp8Buf* f);
 hipError_t launch_fp8_quantize(const void* Q, const void* K, const void* V, const float* signs, const Fp8Buf& f,
                                int B, int H, int S, hipStream_t st);
+hipError_t launch_fp8_dot_eval(const void* A, const void* Bt, float* C, long nblk, hipStream_t st);
 hipError_t launch_fwd_fp8(const Fp8Buf& f, void* O, float* LSE, int B, int H, int S, float C, uint32_t qsign,
                           float tau, int causal, hipStream_t st);
 

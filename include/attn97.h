@@ -182,7 +182,9 @@ const char* attn_strerror(attn_status s);
  * spreads outlier values over the coordinates, which lowers the FP8 error.
  * The transform here is x -> (x * signs) H / sqrt(128), H the 128 x 128
  * Sylvester-Hadamard matrix (orthogonal, so Q K^T is unchanged).  The
- * format is OCP FP8 E4M3 (largest value 448, round to nearest even).
+ * format is OCP FP8 E4M3 (largest value 448, round to nearest even); the
+ * scales are per Q row, per (batch, head) for K and per V column, none of
+ * them tied to a tile of the kernel.
  *
  * Two calls: attn_fp8_quantize fills a caller-owned buffer with the
  * quantized operands, attn_fwd_fp8 computes O and LSE from it.  A buffer
@@ -197,11 +199,12 @@ const char* attn_strerror(attn_status s);
  *           group of 64 keys, key 32 kb + 8 r + 4 h + e (kb, h in {0,1};
  *           r, e in 0..3) is stored at position 32 h + 16 kb + 4 r + e
  *   [3] qs  fp32 [B*H, Sp]        one scale per Q row
- *   [4] ks  fp32 [B*H, Sp / 64]   one scale per tile of 64 keys
+ *   [4] ks  fp32 [B*H]            one scale per (batch, head) for K
  *   [5] vs  fp32 [B*H, 128]       one scale per V column
- *   [6] scratch (V's column maxima)
+ *   [6] scratch (V's column maxima, K's head maxima)
  * A value x is represented as scale * e4m3(code); each scale is the
- * group's max |x| / 448 (1 for an all-zero group).
+ * group's max |x| / 448 (1 for an all-zero group), and each code is the
+ * float64 quotient x * 448 / max|x| rounded to nearest E4M3 (ties to even).
  */
 size_t attn_fp8_buffer_bytes(int B, int H, int S, int D);
 attn_status attn_fp8_buffer_offsets(int B, int H, int S, int D, size_t offsets[7]);
@@ -225,11 +228,26 @@ attn_status attn_fp8_quantize(const void* Q, const void* K, const void* V, const
  * O = acc / l (bf16), LSE = m + ln l (fp32, natural log).
  *   in : buf from attn_fp8_quantize with the same B, H, S, D
  *   out: O bf16 [B,H,S,D]; LSE fp32 [B,H,S]
- *   opts: rescale_tau as in attn_fwd; exp_mode and bwd_mode are ignored.
+ *   opts: rescale_tau as in attn_fwd, but at most 8 is applied (P is rounded
+ *   to E4M3, whose largest value is 448, and unnormalised probabilities stay
+ *   below 2^tau); exp_mode and bwd_mode are ignored.
  *   Errors: as attn_fp8_quantize, plus ATTN_ERR_VALUE for a non-finite scale.
  */
 attn_status attn_fwd_fp8(const void* buf, size_t buf_bytes, void* O, float* LSE, int B, int H, int S, int D,
                          float scale, int causal, const attn_opts* opts, void* stream);
+
+/*
+ * Diagnostic: the FP8 forward's score product on given E4M3 codes.  For
+ * each of nblk blocks, C = A B with A 32 x 128 codes (row-major), B 128 x 32
+ * codes passed transposed as Bt (32 x 128, row-major) and C 32 x 32 fp32
+ * (row-major), computed by the same two chained v_mfma_f32_32x32x64_f8f6f4
+ * and operand layout as one 32 x 32 block of S = Q K^T at D = 128.  A, Bt, C
+ * are device pointers of nblk * 4096, nblk * 4096 bytes and nblk * 1024
+ * floats, 16-byte aligned; nblk = 0 launches nothing.  Codes 0x7F and 0xFF
+ * (NaN) give NaN.  Errors: ATTN_ERR_NULL, ATTN_ERR_SHAPE (nblk < 0),
+ * ATTN_ERR_ALIGN, ATTN_ERR_HIP.
+ */
+attn_status attn_fp8_dot_eval(const void* A, const void* Bt, float* C, long nblk, void* stream);
 
 /*
  * Diagnostic: evaluate the kernels' exp2 on n fp32 values, y[i] = 2^x[i],

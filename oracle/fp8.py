@@ -11,7 +11,8 @@ that spreads outlier values over the coordinates, so that the FP8 rounding
 error is smaller and less concentrated in single elements (the page reports
 2.6 times less numerical error than a naive FP8 attention).
 
-The page fixes none of the details.  The readings taken here:
+The page fixes none of the details.  The readings taken here, in the page's
+order (transform, then quantize, then attention):
 
 * Transform: x -> (x * s) H / sqrt(D) on every row of Q and of K, with H the
   D x D Sylvester-Hadamard matrix and s a vector of random signs.  The matrix
@@ -20,22 +21,28 @@ The page fixes none of the details.  The readings taken here:
   transformed.
 * Format: OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa
   bits; no infinities; the all-ones pattern of each sign is NaN; largest
-  finite value 448).  Rounding to nearest, ties to the even code.  Values
-  are clamped to [-448, 448] after scaling, so nothing reaches the NaN code.
-* Scales (float): Q one per row, K one per tile of 64 keys, V one per
-  column (element of the head dimension); each is max|x| / 448 over its
-  group, or 1 when the group is all zero.  x ~= scale * e4m3(x / scale).
-* Both products in FP8: S = Q8 K8^T and O += P8 V8.  P is rounded to E4M3
-  without a scale: its values lie in (0, 1] relative to the running max.
-* Online softmax over tiles of 64 keys with a per-row running max m:
-  P~ = exp(S - m_new) per tile, rounded to E4M3 for the product with V; the
-  accumulator and the row sum are multiplied by exp(m_old - m_new) when the
-  max grows; the row sum adds the unrounded P~.  O = acc / l and
-  LSE = m + ln l.
+  finite value 448).  Rounding to nearest, ties to the even code.
+* Scales (float): Q one per row, K one per (batch, head), V one per column
+  (element of the head dimension); each is max|x| / 448 over its group, or 1
+  when the group is all zero.  x ~= scale * e4m3(x / scale).  None of these
+  groups depends on how a kernel tiles the sequence.  The code of x is the
+  rounding of the float64 quotient x * 448 / max|x| (one correctly rounded
+  division of an exact numerator), straight to E4M3.
+* Attention (fp8_reference_fwd): S = scale * Q8 K8^T on the dequantized
+  operands, m = the row max, P~ = exp(S - m) in (0, 1], O = E4M3(P~) V8 / l
+  with l the row sum of the unrounded P~, LSE = m + ln l.  P is rounded to
+  E4M3 without a scale, relative to the row's final max.
 
-Because P is rounded relative to the running max of the tiles seen so far,
-the result depends on the tile size; 64 keys is the tile of the GPU kernel.
-Every step above is exact in float64 except the roundings it names.
+A kernel that walks the keys in tiles rounds P~ against the running max
+instead: relative to a max that may still lag the final one, so on a grid
+that is finer in absolute terms, tile by tile.  p_rounding_bound gives, per
+output element, a bound that one rounding of P keeps to, whether against the
+final max or against any running max not above it (any tiling, any
+conditional-rescale threshold up to 8); two such results differ by at most
+twice it.  online_softmax_fwd is the tiled form
+of the same attention for a given tile size, rounding P per tile against the
+running max (an emulation of that schedule, used as a second, tighter check).
+Every step is exact in float64 except the roundings it names.
 """
 
 from __future__ import annotations
@@ -45,7 +52,6 @@ import math
 import numpy as np
 
 E4M3_MAX = 448.0
-TILE = 64
 
 
 def e4m3_table() -> np.ndarray:
@@ -122,12 +128,14 @@ def _scale_of(amax):
 
 
 def _codes(x, amax):
-    """E4M3 codes of x / (amax / 448), formed as x * 448 / amax: one rounding,
-    so a value exactly halfway between two codes stays exactly halfway (and
-    goes to the even code).  amax = 0 gives code 0."""
+    """E4M3 codes of x / (amax / 448), formed as the float64 quotient
+    (x * 448) / amax (the numerator is exact for the inputs here, the division
+    is correctly rounded) and rounded from float64 straight to E4M3: a value
+    exactly halfway between two codes stays exactly halfway (and goes to the
+    even code).  amax = 0 gives code 0."""
     amax = np.asarray(amax, dtype=np.float64)
     safe = np.where(amax > 0, amax, 1.0)
-    return quantize_e4m3(np.where(amax > 0, x * E4M3_MAX / safe, 0.0))
+    return quantize_e4m3(np.where(amax > 0, (x * E4M3_MAX) / safe, 0.0))
 
 
 def quantize_rows(x, norm: float = 1.0):
@@ -137,17 +145,11 @@ def quantize_rows(x, norm: float = 1.0):
     return _codes(x, amax[:, None]), _scale_of(amax * norm)
 
 
-def quantize_tiles(x, tile: int = TILE, norm: float = 1.0):
-    """One scale per tile of `tile` rows (the last tile may be shorter): codes and scales
-    [ceil(S / tile)] of the rows x * norm."""
+def quantize_whole(x, norm: float = 1.0):
+    """One scale for the whole matrix: codes [S, D] and a scale (0-d array) of x * norm."""
     x = np.asarray(x, dtype=np.float64)
-    n = x.shape[0]
-    nt = (n + tile - 1) // tile
-    amax = np.array([np.abs(x[t * tile:(t + 1) * tile]).max() for t in range(nt)])
-    codes = np.empty(x.shape, dtype=np.uint8)
-    for t in range(nt):
-        codes[t * tile:(t + 1) * tile] = _codes(x[t * tile:(t + 1) * tile], amax[t])
-    return codes, _scale_of(amax * norm)
+    amax = np.abs(x).max()
+    return _codes(x, amax), _scale_of(amax * norm)
 
 
 def quantize_cols(x):
@@ -157,11 +159,11 @@ def quantize_cols(x):
     return _codes(x, amax[None, :]), _scale_of(amax)
 
 
-def quantize_head(q, k, v, signs=None, tile: int = TILE):
+def quantize_head(q, k, v, signs=None):
     """Transform (when signs are given) and quantize one head's Q, K, V.
 
-    Returns dict with codes (q8, k8, v8) and scales (qs [S], ks [ceil(S/tile)],
-    vs [D]) and the dequantized float64 matrices (qh, kh, vh).
+    Returns dict with codes (q8, k8, v8), scales (qs [S], ks (one, for the
+    head), vs [D]) and the dequantized float64 matrices (qh, kh, vh).
 
     The codes of a transformed row y = (x * s) H / sqrt(D) are the rounding of
     y * 448 / max|y|, in which the factor 1 / sqrt(D) cancels; they are formed
@@ -181,19 +183,72 @@ def quantize_head(q, k, v, signs=None, tile: int = TILE):
         k = (k * s_) @ h
         norm = 1.0 / math.sqrt(d)
     q8, qs = quantize_rows(q, norm)
-    k8, ks = quantize_tiles(k, tile, norm)
+    k8, ks = quantize_whole(k, norm)
     v8, vs = quantize_cols(v)
-    kt = np.repeat(ks, tile)[: k.shape[0]]
     return {
         "q8": q8, "qs": qs, "k8": k8, "ks": ks, "v8": v8, "vs": vs,
         "qh": dequantize_e4m3(q8) * qs[:, None],
-        "kh": dequantize_e4m3(k8) * kt[:, None],
+        "kh": dequantize_e4m3(k8) * ks,
         "vh": dequantize_e4m3(v8) * vs[None, :],
     }
 
 
-def online_softmax_fwd(qh, kh, vh, scale: float, causal: bool, round_p=round_e4m3, tile: int = TILE,
-                       q_rows=None):
+def _causal_mask(n, sk, q_rows):
+    """True where key j is hidden from query row i (queries are the last rows of sk positions)."""
+    i = (np.arange(n) if q_rows is None else np.asarray(q_rows))[:, None]
+    sq = n if q_rows is None else sk
+    return np.arange(sk)[None, :] > i + (sk - sq)
+
+
+def fp8_reference_fwd(qh, kh, vh, scale: float, causal: bool, round_p=None, q_rows=None):
+    """Attention of one head on given (dequantized) operands with P rounded to
+    E4M3 against each row's final max; no tiling.
+
+    S = scale * Q K^T (causal: key j > query i is -inf), m = rowmax S,
+    P~ = exp(S - m), O = round_p(P~) V / rowsum(P~), LSE = m + ln rowsum(P~).
+    round_p defaults to round_e4m3; with the identity it is the softmax
+    attention of the operands.  q_rows: the positions of the given query rows
+    in a square problem (for the causal mask) when qh holds only some rows.
+    Returns O, LSE and the unrounded P~ (for p_rounding_bound).
+    """
+    rp = round_e4m3 if round_p is None else round_p
+    qh = np.asarray(qh, dtype=np.float64)
+    kh = np.asarray(kh, dtype=np.float64)
+    vh = np.asarray(vh, dtype=np.float64)
+    s = scale * (qh @ kh.T)
+    if causal:
+        s = np.where(_causal_mask(qh.shape[0], kh.shape[0], q_rows), -np.inf, s)
+    m = s.max(axis=1)
+    p = np.exp(s - m[:, None])
+    l = p.sum(axis=1)
+    o = (rp(p) @ vh) / l[:, None]
+    return o, m + np.log(l), p
+
+
+def e4m3_error_bound(x) -> np.ndarray:
+    """Largest |E4M3(x) - x| for 0 <= x <= 448: half a unit in the last place,
+    2^-4 x for normal values (x >= 2^-6), 2^-10 below, and never more than x
+    itself (a value under 2^-10 rounds to zero)."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.maximum(2.0 ** -4 * x, np.minimum(x, 2.0 ** -10))
+
+
+def p_rounding_bound(p, vh) -> np.ndarray:
+    """Per-element bound on how far rounding P to E4M3 moves O, for P~ = p
+    (rows relative to their final max, values in (0, 1]) and operand V = vh:
+        B_id = sum_j e(p_ij) |v_jd| / sum_j p_ij,   e = e4m3_error_bound.
+    It holds for the rounding against the final max (fp8_reference_fwd) and,
+    as well, for a rounding against any running max m_t <= m of a tiled
+    kernel whose unnormalised probabilities stay at most 2^8 (no clamping at
+    448): there the term c e4m3(p / c), c = exp(m_t - m) <= 1, is off from p
+    by at most c e(p / c) <= max(2^-4 p, min(p, 2^-10 c)) <= e(p).  So two
+    such results differ by at most 2 B."""
+    p = np.asarray(p, dtype=np.float64)
+    l = p.sum(axis=1)
+    return (e4m3_error_bound(p) @ np.abs(np.asarray(vh, dtype=np.float64))) / l[:, None]
+
+
+def online_softmax_fwd(qh, kh, vh, scale: float, causal: bool, round_p, tile: int, q_rows=None):
     """Tiled online-softmax forward of one head on given (dequantized) operands.
 
     For each tile of `tile` keys: S = scale * Q K_t^T (causal: key j > query i
@@ -208,18 +263,14 @@ def online_softmax_fwd(qh, kh, vh, scale: float, causal: bool, round_p=round_e4m
     kh = np.asarray(kh, dtype=np.float64)
     vh = np.asarray(vh, dtype=np.float64)
     n, sk = qh.shape[0], kh.shape[0]
-    sq = n if q_rows is None else None
+    mask = _causal_mask(n, sk, q_rows) if causal else None
     m = np.full(n, -np.inf)
     l = np.zeros(n)
     acc = np.zeros((n, vh.shape[1]))
-    i = (np.arange(n) if q_rows is None else np.asarray(q_rows))[:, None]
     for t0 in range(0, sk, tile):
         s = scale * (qh @ kh[t0:t0 + tile].T)
         if causal:
-            if sq is None:  # rows of a square problem
-                sq = sk
-            j = np.arange(t0, min(sk, t0 + tile))[None, :]
-            s = np.where(j > i + (sk - sq), -np.inf, s)
+            s = np.where(mask[:, t0:t0 + tile], -np.inf, s)
         m_new = np.maximum(m, s.max(axis=1))
         # rows with every key so far masked keep m = -inf and contribute nothing
         live = np.isfinite(m_new)
@@ -233,18 +284,24 @@ def online_softmax_fwd(qh, kh, vh, scale: float, causal: bool, round_p=round_e4m
     return o, lse
 
 
-def fp8_attention_fwd(q, k, v, scale: float, causal: bool, signs=None, tile: int = TILE, rows=None):
-    """FP8 forward of one head ([S, D] each): transform, quantize, online softmax with P in E4M3.
+def fp8_attention_fwd(q, k, v, scale: float, causal: bool, signs=None, rows=None, tile=None):
+    """FP8 forward of one head ([S, D] each): transform, quantize, attention with P in E4M3.
 
-    rows: compute only these query rows (of a square problem); Q is quantized
-    per row, so the result is the same as those rows of the full call.
+    tile None: fp8_reference_fwd (P rounded against each row's final max, no
+    tiling); an int: online_softmax_fwd over tiles of that many keys (P
+    rounded per tile against the running max).  rows: compute only these
+    query rows (of a square problem); Q is quantized per row, so the result is
+    the same as those rows of the full call.  Returns O and LSE.
     """
-    qd = quantize_head(q, k, v, signs, tile)
+    qd = quantize_head(q, k, v, signs)
     qh = qd["qh"] if rows is None else qd["qh"][np.asarray(rows)]
+    if tile is None:
+        o, lse, _ = fp8_reference_fwd(qh, qd["kh"], qd["vh"], scale, causal, q_rows=rows)
+        return o, lse
     return online_softmax_fwd(qh, qd["kh"], qd["vh"], scale, causal, round_e4m3, tile, rows)
 
 
-def fp8_attention_fwd_heads(q, k, v, scale: float, causal: bool, signs=None, heads=None, tile: int = TILE):
+def fp8_attention_fwd_heads(q, k, v, scale: float, causal: bool, signs=None, heads=None, tile=None):
     """fp8_attention_fwd over [B, H, S, D] arrays (float64 results); `heads` picks (b, h) pairs."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -255,5 +312,5 @@ def fp8_attention_fwd_heads(q, k, v, scale: float, causal: bool, signs=None, hea
     o = np.zeros((len(heads), S, D))
     lse = np.zeros((len(heads), S))
     for n, (b, h) in enumerate(heads):
-        o[n], lse[n] = fp8_attention_fwd(q[b, h], k[b, h], v[b, h], scale, causal, signs, tile)
+        o[n], lse[n] = fp8_attention_fwd(q[b, h], k[b, h], v[b, h], scale, causal, signs, tile=tile)
     return o, lse

@@ -204,13 +204,25 @@ def test_splitkv_rejects(kw, code):
                                 a["Sk"], a["D"], a["scale"], a["causal"], a["splits"], None, None) == code
 
 
+def test_fp8_dot_eval_rejects():
+    lib = L.load()
+    assert lib.attn_fp8_dot_eval(P, P, P, 0, None) == OK  # nothing to do, nothing launched
+    assert lib.attn_fp8_dot_eval(P, P, P, -1, None) == SHAPE
+    assert lib.attn_fp8_dot_eval(None, P, P, 1, None) == NULL
+    assert lib.attn_fp8_dot_eval(P, None, P, 1, None) == NULL
+    assert lib.attn_fp8_dot_eval(P, P, None, 1, None) == NULL
+    assert lib.attn_fp8_dot_eval(P + 8, P, P, 1, None) == ALIGN
+    assert lib.attn_fp8_dot_eval(P, P, P + 4, 1, None) == ALIGN
+
+
 def test_fp8_buffer_layout():
     lib = L.load()
     B, H, S, D = 2, 3, 200, 128
     Sp, BH = 256, 6
     r = lambda n: (n + 255) // 256 * 256
-    sizes = [r(BH * Sp * D), r(BH * Sp * D), r(BH * D * Sp), r(BH * Sp * 4), r(BH * (Sp // 64) * 4), r(BH * D * 4),
-             r(BH * (Sp // 128) * D * 4)]
+    # q8, k8, v8t, qs (per row), ks (per head), vs (per column), scratch (V column maxima, K head maxima)
+    sizes = [r(BH * Sp * D), r(BH * Sp * D), r(BH * D * Sp), r(BH * Sp * 4), r(BH * 4), r(BH * D * 4),
+             r(BH * D * 4) + r(BH * 8)]
     assert lib.attn_fp8_buffer_bytes(B, H, S, D) == sum(sizes)
     offs = (ctypes.c_size_t * 7)()
     assert lib.attn_fp8_buffer_offsets(B, H, S, D, offs) == OK

@@ -6,10 +6,17 @@
 * The Hadamard matrix against the closed form (-1)^popcount(i & j), and its
   orthogonality.
 * Invariance of Q K^T under the transform (the reason it may be applied).
-* With every rounding switched off, the tiled online softmax is exactly the
-  softmax attention of the plain oracle (oracle/attention.py), causal and
-  ragged included: this pins the tile loop, the running max and the rescale.
-* The rounding error bound of E4M3 (half a unit in the last place).
+* With every rounding switched off, the tile-free FP8 reference and the
+  tiled online softmax are exactly the softmax attention of the plain oracle
+  (oracle/attention.py), causal and ragged included: this pins the mask, the
+  row max, the tile loop, the running max and the rescale.
+* A worked example of the reference by hand (two keys, P = [1, 0.3] with
+  0.3 rounding to the code 0.3125, unrounded row sum), as a golden file.
+* The rounding error bound of E4M3 (half a unit in the last place) and the
+  per-element bound p_rounding_bound built on it: the rounded reference stays
+  within it of the unrounded attention, and so does a tiled computation that
+  rounds against the running max, for tiles of 1 to 200 keys and with the
+  max allowed to lag by up to 8 (log2 units) as the conditional rescale does.
 * The pages' claim, qualitatively: on inputs with outliers, the transform
   lowers the error of FP8 attention against the exact result.
 
@@ -139,10 +146,15 @@ def test_online_softmax_without_rounding_is_attention(sq, sk, causal):
     k = _rand((sk, 32), 6)
     v = _rand((sk, 32), 7)
     scale = 1.0 / math.sqrt(32)
-    o, lse = F.online_softmax_fwd(q, k, v, scale, causal, round_p=lambda p: p)
     o_ref, lse_ref = A.attention_fwd(q[None, None], k[None, None], v[None, None], scale, causal)
-    assert np.max(np.abs(o - o_ref[0, 0])) <= 1e-12
-    assert np.max(np.abs(lse - lse_ref[0, 0])) <= 1e-12
+    for tile in (1, 37, 64):
+        o, lse = F.online_softmax_fwd(q, k, v, scale, causal, lambda p: p, tile)
+        assert np.max(np.abs(o - o_ref[0, 0])) <= 1e-12
+        assert np.max(np.abs(lse - lse_ref[0, 0])) <= 1e-12
+    if sq == sk:
+        o, lse, _ = F.fp8_reference_fwd(q, k, v, scale, causal, round_p=lambda p: p)
+        assert np.max(np.abs(o - o_ref[0, 0])) <= 1e-12
+        assert np.max(np.abs(lse - lse_ref[0, 0])) <= 1e-12
 
 
 def test_fp8_attention_close_to_exact():
@@ -167,8 +179,12 @@ def test_quantized_operands_reconstruct_inputs():
     for name, x in (("qh", q), ("kh", k), ("vh", v)):
         rel = np.abs(d[name] - x).max() / np.abs(x).max()
         assert rel <= 2.0 ** -4, name
-    assert d["ks"].shape == (2,) and d["qs"].shape == (100,) and d["vs"].shape == (128,)
+    assert np.shape(d["ks"]) == () and d["qs"].shape == (100,) and d["vs"].shape == (128,)
     assert np.all(np.abs(F.dequantize_e4m3(d["q8"])) <= 448.0)
+    # the element of largest magnitude of each group is exactly +-448 times its scale
+    assert np.max(np.abs(F.dequantize_e4m3(d["k8"]))) == 448.0 and d["ks"] == np.abs(k).max() / 448.0
+    assert np.all(np.max(np.abs(F.dequantize_e4m3(d["q8"])), axis=1) == 448.0)
+    assert np.all(np.max(np.abs(F.dequantize_e4m3(d["v8"])), axis=0) == 448.0)
 
 
 def test_transform_lowers_error_on_outliers():
@@ -189,6 +205,89 @@ def test_transform_lowers_error_on_outliers():
     e_naive = rms(o_naive - o_ref[0, 0])
     e_rot = rms(o_rot - o_ref[0, 0])
     assert e_rot < e_naive, (e_rot, e_naive)
+
+
+# ----------------------------------------------------------------------------
+# the tile-free reference and the bound on the rounding of P
+# ----------------------------------------------------------------------------
+
+
+def test_reference_worked_example_golden():
+    """tests/golden/fp8_two_keys.json, worked by hand: scores [0, ln 0.3] give
+    P~ = [1, 0.3]; 0.3 lies between the E4M3 values 0.28125 and 0.3125 and is
+    nearer the latter; O = (1 * 2 + 0.3125 * 4) / 1.3 = 2.5, LSE = ln 1.3."""
+    import json
+    import os
+
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "fp8_two_keys.json")))
+    qh = np.array(g["qh"], dtype=np.float64)
+    kh = np.array([[0.0], [math.log(0.3)]])
+    vh = np.array(g["vh"], dtype=np.float64)
+    o, lse, p = F.fp8_reference_fwd(qh, kh, vh, g["scale"], False)
+    assert abs(o[0, 0] - g["O"]) <= 1e-12 and abs(lse[0] - g["LSE"]) <= 1e-12
+    assert abs(F.round_e4m3(np.array([0.3]))[0] - g["P_rounded"][1]) == 0.0
+
+
+def test_error_bound_holds_and_is_attained():
+    rng = np.random.default_rng(40)
+    x = np.concatenate([rng.uniform(0, 448, 50000), rng.uniform(0, 2.0 ** -5, 50000),
+                        np.exp2(rng.uniform(-20, 8.8, 50000))])
+    x = np.minimum(x, 448.0)
+    err = np.abs(F.round_e4m3(x) - x)
+    bnd = F.e4m3_error_bound(x)
+    assert np.all(err <= bnd)
+    # tight: at the first midpoint of a binade (1.0625 * 2^e) the error is 1 / 1.0625 of the bound
+    tab = F.e4m3_table()[:0x7F]
+    mids = (tab[1:] + tab[:-1]) / 2
+    big = mids[mids >= 2.0 ** -6]
+    assert np.max(np.abs(F.round_e4m3(big * (1 - 1e-9)) - big) / F.e4m3_error_bound(big)) > 0.94
+
+
+def _lagging_online_softmax(qh, kh, vh, scale, tile, tau):
+    """Tiled attention that moves its running max only when a row's max grows
+    by more than tau (log2 units) and rounds P to E4M3 against that max."""
+    n, sk = qh.shape[0], kh.shape[0]
+    m = np.full(n, -np.inf)
+    l = np.zeros(n)
+    acc = np.zeros((n, vh.shape[1]))
+    for t0 in range(0, sk, tile):
+        s = scale * (qh @ kh[t0:t0 + tile].T)
+        mx = s.max(axis=1)
+        grow = (mx - m) * math.log2(math.e) > tau
+        m_new = np.where(grow, mx, m)
+        alpha = np.where(np.isfinite(m), np.exp(m - m_new), 0.0)
+        p = np.exp(s - m_new[:, None])
+        assert np.all(p <= 2.0 ** tau * (1 + 1e-12))
+        acc = acc * alpha[:, None] + F.round_e4m3(p) @ vh[t0:t0 + tile]
+        l = l * alpha + p.sum(axis=1)
+        m = m_new
+    return acc / l[:, None]
+
+
+@pytest.mark.parametrize("outliers", [False, True])
+def test_p_rounding_bound_covers_every_schedule(outliers):
+    rng = np.random.default_rng(41)
+    q = rng.standard_normal((64, 128))
+    k = rng.standard_normal((200, 128))
+    v = rng.standard_normal((200, 128))
+    if outliers:
+        q = np.where(rng.random(q.shape) < 0.01, 20 * q, q)
+        k = np.where(rng.random(k.shape) < 0.01, 20 * k, k)
+    d = F.quantize_head(q, k, v, np.where(rng.random(128) < 0.5, -1.0, 1.0))
+    qh, kh, vh = d["qh"], d["kh"], d["vh"][:200]
+    scale = 1.0 / math.sqrt(128)
+    o_exact, _, p = F.fp8_reference_fwd(qh, kh, vh, scale, False, round_p=lambda x: x)
+    o_ref, _, _ = F.fp8_reference_fwd(qh, kh, vh, scale, False)
+    bnd = F.p_rounding_bound(p, vh)
+    assert np.all(np.abs(o_ref - o_exact) <= bnd * (1 + 1e-9))
+    assert np.max(np.abs(o_ref - o_exact)) > 0.0
+    for tile in (1, 16, 64, 200):
+        o_t, _ = F.online_softmax_fwd(qh, kh, vh, scale, False, F.round_e4m3, tile)
+        assert np.all(np.abs(o_t - o_exact) <= bnd * (1 + 1e-9))
+        assert np.all(np.abs(o_t - o_ref) <= 2 * bnd * (1 + 1e-9))
+        for tau in (3.0, 8.0):
+            o_l = _lagging_online_softmax(qh, kh, vh, scale, tile, tau)
+            assert np.all(np.abs(o_l - o_exact) <= bnd * (1 + 1e-9))
 
 
 # ----------------------------------------------------------------------------
@@ -241,6 +340,16 @@ def test_planted_mistakes_are_caught():
     o, _ = _softmax_without_rescale(qq, kk, vv, 0.2, False)
     o_ref, _ = A.attention_fwd(qq[None, None], kk[None, None], vv[None, None], 0.2, False)
     assert np.max(np.abs(o - o_ref[0, 0])) > 1e-6  # the online-softmax pin fails
+
+    # the reference with its row sum over the rounded P: the golden fails
+    qh, kh, vh = np.array([[1.0]]), np.array([[0.0], [math.log(0.3)]]), np.array([[2.0], [4.0]])
+    p = np.exp(qh @ kh.T)
+    o_bad = (F.round_e4m3(p) @ vh) / F.round_e4m3(p).sum(axis=1, keepdims=True)
+    assert abs(o_bad[0, 0] - 2.5) > 1e-3
+    # a bound that forgets the subnormal floor (2^-4 p only) fails the bound pin on rows with small P
+    rng = np.random.default_rng(41)
+    x = np.exp2(rng.uniform(-14, -7, 1000))
+    assert np.any(np.abs(F.round_e4m3(x) - x) > 2.0 ** -4 * x)
 
 
 def test_row_subset_equals_full_call():
