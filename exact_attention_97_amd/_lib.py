@@ -19,7 +19,9 @@ ATTN_OK = 0
 STATUS_NAMES = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
     4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_HIP", 7: "ATTN_ERR_VALUE",
+    8: "ATTN_ERR_SCRATCH_LIMIT",
 }
+NOALLOC_SCRATCH_BYTES = 32 << 20  # ATTN_NOALLOC_SCRATCH_BYTES
 EXP_MODES = {"native": 0, "poly": 1, "mixed": 2}
 BWD_MODES = {"atomic": 0, "split": 1}
 
@@ -29,7 +31,7 @@ EXPORTS = (
     "attn_exp2_eval", "attn_prof_enable", "attn_prof_reset", "attn_prof_collect", "attn_version",
     "attn_fwd_splitkv_workspace_bytes", "attn_fwd_splitkv",
     "attn_fp8_buffer_bytes", "attn_fp8_buffer_offsets", "attn_fp8_quantize", "attn_fwd_fp8",
-    "attn_set_variant", "attn_fp8_dot_eval",
+    "attn_set_variant", "attn_fp8_dot_eval", "attn_bwd_noalloc",
 )
 FP8_REGIONS = ("q8", "k8", "v8t", "qs", "ks", "vs", "scratch")
 
@@ -68,6 +70,8 @@ def load():
     lib.attn_bwd_workspace_bytes.restype = sz
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, optp, vp]
     lib.attn_bwd.restype = i
+    lib.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, optp, vp]
+    lib.attn_bwd_noalloc.restype = i
     lib.attn_strerror.argtypes = [i]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_exp2_eval.argtypes = [vp, vp, ctypes.c_long, i, vp]
@@ -300,6 +304,26 @@ def fp8_dot_eval(a, bt, stream=None):
     _check("attn_fp8_dot_eval", load().attn_fp8_dot_eval(a.data_ptr(), bt.data_ptr(), c.data_ptr(), a.shape[0],
                                                          _stream_ptr(stream)))
     return c
+
+
+def attn_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, bwd_mode="split", stream=None):
+    """Backward pass with the library's fixed device scratch as its workspace
+    (attn_bwd_noalloc): the caller passes every input and output (dq, dk, dv
+    bf16 [B,H,S,D]); nothing is allocated.  Returns (dq, dk, dv)."""
+    import torch
+
+    lib = load()
+    B, H, S, D = _check_qkv(q, k, v, o, do, dq, dk, dv)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B,H,S] tensor")
+    opts = make_opts(bwd_mode=bwd_mode)
+    _check("attn_bwd_noalloc", lib.attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                                    do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                                    dv.data_ptr(), B, H, S, D, float(scale), int(bool(causal)),
+                                                    ctypes.byref(opts), _stream_ptr(stream)))
+    return dq, dk, dv
 
 
 def exp2_eval(x, mode="native", stream=None):

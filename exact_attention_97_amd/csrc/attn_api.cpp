@@ -9,6 +9,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "attn97.h"
@@ -142,6 +143,8 @@ const char* attn_strerror(attn_status s) {
     case ATTN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case ATTN_ERR_HIP: return "HIP runtime error at launch";
     case ATTN_ERR_VALUE: return "scale or an option value is not finite or out of range";
+    case ATTN_ERR_SCRATCH_LIMIT:
+      return "the shape needs more workspace than the fixed scratch of attn_bwd_noalloc (ATTN_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -276,10 +279,15 @@ size_t attn_bwd_workspace_bytes(int B, int H, int S, int D, int causal, const at
   return n;
 }
 
-attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
-                     const float* LSE, void* dQ, void* dK, void* dV, void* workspace,
-                     size_t workspace_bytes, int B, int H, int S, int D, float scale, int causal,
-                     const attn_opts* opts, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of attn_bwd and attn_bwd_noalloc (everything but the
+// workspace); fills the options and the workspace size the call needs.
+attn_status check_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
+                      void* dQ, void* dK, void* dV, int B, int H, int S, int D, float scale, int causal,
+                      const attn_opts* opts, attn_opts* o, size_t* need) {
   if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return ATTN_ERR_NULL;
   attn_status st = check_shape(B, H, S, D);
   if (st != ATTN_OK) return st;
@@ -288,14 +296,17 @@ attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O,
       misaligned(dV, 16))
     return ATTN_ERR_ALIGN;
   if (!isfinite(scale)) return ATTN_ERR_VALUE;
-  attn_opts o;
-  st = read_opts(opts, &o);
+  st = read_opts(opts, o);
   if (st != ATTN_OK) return st;
-  if (!attn97::bwd_supported(D, o.bwd_mode == ATTN_BWD_ATOMIC)) return ATTN_ERR_UNSUPPORTED;
-  const size_t need = attn_bwd_workspace_bytes(B, H, S, D, causal, &o);
-  if (workspace == nullptr || workspace_bytes < need || misaligned(workspace, 256))
-    return ATTN_ERR_WORKSPACE;
+  if (!attn97::bwd_supported(D, o->bwd_mode == ATTN_BWD_ATOMIC)) return ATTN_ERR_UNSUPPORTED;
+  *need = attn_bwd_workspace_bytes(B, H, S, D, causal, o);
+  return ATTN_OK;
+}
 
+// The backward launches on a checked, large enough workspace.
+attn_status run_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
+                    void* dQ, void* dK, void* dV, void* workspace, int B, int H, int S, int D, float scale,
+                    int causal, const attn_opts& o, void* stream) {
   attn97::BwdArgs a;
   a.Q = Q;
   a.K = K;
@@ -320,6 +331,68 @@ attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O,
   hipError_t e = (o.bwd_mode == ATTN_BWD_ATOMIC) ? attn97::launch_bwd_atomic(a, (hipStream_t)stream)
                                                  : attn97::launch_bwd_split(a, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+// ---- the no-allocation entry point's scratch ------------------------------
+// A fixed device array in the library's code object: every GPU the library
+// runs on holds its own copy, at its own address, until the process ends.
+// In host code `scratch` is only a stand-in for the symbol: its device
+// address comes from hipGetSymbolAddress, once per device (with that device
+// current), and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The current device's scratch address (looked up on the first call there).
+attn_status current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_HIP;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) return ATTN_ERR_HIP;
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                     const float* LSE, void* dQ, void* dK, void* dV, void* workspace,
+                     size_t workspace_bytes, int B, int H, int S, int D, float scale, int causal,
+                     const attn_opts* opts, void* stream) {
+  attn_opts o;
+  size_t need = 0;
+  attn_status st = check_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, S, D, scale, causal, opts, &o, &need);
+  if (st != ATTN_OK) return st;
+  if (workspace == nullptr || workspace_bytes < need || misaligned(workspace, 256))
+    return ATTN_ERR_WORKSPACE;
+  return run_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, B, H, S, D, scale, causal, o, stream);
+}
+
+attn_status attn_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                             const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int S, int D,
+                             float scale, int causal, const attn_opts* opts, void* stream) {
+  attn_opts o;
+  size_t need = 0;
+  attn_status st = check_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, S, D, scale, causal, opts, &o, &need);
+  if (st != ATTN_OK) return st;
+  if (need > (size_t)ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  st = current_scratch(&ws);
+  if (st != ATTN_OK) return st;
+  // every byte the kernels read from the scratch is written first in this
+  // call (Delta and -LSE log2e by the preprocessing kernel, which also zeroes
+  // the dQ accumulator in the atomic mode), so what an earlier call left
+  // there does not matter
+  return run_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, ws, B, H, S, D, scale, causal, o, stream);
 }
 
 size_t attn_fp8_buffer_bytes(int B, int H, int S, int D) {

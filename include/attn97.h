@@ -49,7 +49,8 @@ typedef enum {
     ATTN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned            */
     ATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required     */
     ATTN_ERR_HIP = 6,         /* the HIP runtime rejected a launch           */
-    ATTN_ERR_VALUE = 7        /* scale or an option value is not finite / out of range */
+    ATTN_ERR_VALUE = 7,       /* scale or an option value is not finite / out of range */
+    ATTN_ERR_SCRATCH_LIMIT = 8 /* attn_bwd_noalloc: the shape needs more than its fixed scratch */
 } attn_status;
 
 /* How the forward kernel computes exp2 of the shifted scores.  The pages
@@ -137,6 +138,29 @@ attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O,
                      void* workspace, size_t workspace_bytes,
                      int B, int H, int S, int D, float scale, int causal,
                      const attn_opts* opts, void* stream);
+
+/*
+ * Backward pass that allocates nothing, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): attn_bwd with its workspace taken from a
+ * fixed device array inside the library, ATTN_NOALLOC_SCRATCH_BYTES per GPU,
+ * held by every GPU the library runs on until the process ends.  The caller
+ * still passes inputs and outputs.  Arguments and results as attn_bwd.
+ *   The scratch of the current device is used (its address is looked up once
+ *   per device, on the first call there); the stream must belong to that
+ *   device.  Shapes whose attn_bwd_workspace_bytes(...) exceed
+ *   ATTN_NOALLOC_SCRATCH_BYTES return ATTN_ERR_SCRATCH_LIMIT before anything
+ *   is launched: in the split mode (default) up to 4 194 240 rows B*H*S, in
+ *   the atomic mode far fewer (its fp32 dQ accumulator is B*H*S*D floats).
+ *   All calls on one GPU share its scratch and each leaves its contents
+ *   behind: calls that overlap on one GPU (other streams, other threads)
+ *   race and must not be issued; calls ordered on one stream are safe.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+attn_status attn_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                             const float* LSE, void* dQ, void* dK, void* dV,
+                             int B, int H, int S, int D, float scale, int causal,
+                             const attn_opts* opts, void* stream);
 
 /*
  * Split-KV forward pass: the same O and LSE as attn_fwd, computed by splitting

@@ -17,7 +17,7 @@ from exact_attention_97_amd import _lib as L  # noqa: E402
 
 pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="libattn97.so not built")
 
-OK, NULL, SHAPE, UNSUP, ALIGN, WS, HIP, VALUE = range(8)
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, HIP, VALUE, SCRATCH = range(9)
 P = 0x10000  # a fake, 256-byte aligned device address: never dereferenced on these paths
 
 
@@ -39,8 +39,8 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_strerror():
     lib = L.load()
     assert b"gfx950" in lib.attn_version()
-    texts = {lib.attn_strerror(c) for c in range(8)}
-    assert len(texts) == 8
+    texts = {lib.attn_strerror(c) for c in range(9)}
+    assert len(texts) == 9
     assert lib.attn_strerror(99) == b"unknown status"
 
 
@@ -202,6 +202,36 @@ def test_splitkv_rejects(kw, code):
     a.update(kw)
     assert lib.attn_fwd_splitkv(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["ws"], a["wsb"], a["B"], a["H"], a["Sq"],
                                 a["Sk"], a["D"], a["scale"], a["causal"], a["splits"], None, None) == code
+
+
+def bwd_noalloc(**kw):
+    a = dict(Q=P, K=P, V=P, O=P, dO=P, LSE=P, dQ=P, dK=P, dV=P, B=1, H=1, S=16, D=64, scale=0.125, causal=0,
+             opts=None, stream=None)
+    a.update(kw)
+    opts = ctypes.byref(a["opts"]) if a["opts"] is not None else None
+    return L.load().attn_bwd_noalloc(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["LSE"], a["dQ"], a["dK"], a["dV"],
+                                     a["B"], a["H"], a["S"], a["D"], a["scale"], a["causal"], opts, a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), NULL), (dict(dV=None), NULL), (dict(S=0), SHAPE), (dict(D=96), UNSUP), (dict(dK=P + 2), ALIGN),
+    (dict(scale=float("nan")), VALUE), (dict(D=256, opts=L.make_opts(bwd_mode="atomic")), UNSUP),
+    # beyond the fixed scratch: split needs 2 * 4 bytes per row, atomic also 4 * D per row
+    (dict(B=1, H=65, S=65536, D=64), SCRATCH),
+    (dict(B=1, H=16, S=8192, D=128, opts=L.make_opts(bwd_mode="atomic")), SCRATCH),
+])
+def test_bwd_noalloc_rejects(kw, code):
+    """Argument errors and the scratch limit are reported before any device call."""
+    assert bwd_noalloc(**kw) == code
+
+
+def test_noalloc_limit_matches_workspace_rule():
+    lib = L.load()
+    split = L.make_opts(bwd_mode="split")
+    assert lib.attn_bwd_workspace_bytes(1, 65, 65536, 64, 0, ctypes.byref(split)) > L.NOALLOC_SCRATCH_BYTES
+    assert lib.attn_bwd_workspace_bytes(1, 64, 65536, 64, 0, ctypes.byref(split)) == L.NOALLOC_SCRATCH_BYTES
+    assert lib.attn_bwd_workspace_bytes(2, 16, 8192, 128, 0, ctypes.byref(split)) <= L.NOALLOC_SCRATCH_BYTES
+    assert lib.attn_bwd_workspace_bytes(1, 32, 32768, 128, 0, ctypes.byref(split)) <= L.NOALLOC_SCRATCH_BYTES
 
 
 def test_fp8_dot_eval_rejects():
