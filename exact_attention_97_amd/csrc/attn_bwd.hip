@@ -335,11 +335,21 @@ __device__ __forceinline__ void dkdv_elem(const f32x16& sacc, const f32x16& dpac
 // LDS.  issue_part(p) issues piece p of the next tile's loads; the pieces go
 // out over phases A and B, one every other step (issued back to back they
 // fill the memory pipeline and stall the wavefront for hundreds of cycles).
-template <int D, class Cfg, bool CAUSAL, bool MASK, class IssuePart>
+// Hooks of the fused atomic mode (DqHooks in bwd_dkdv_kernel): store(qb,
+// dsb) puts block qb's dS (bf16) into LDS once it is formed; step(i), in
+// each of phase D's eight steps, runs one k-step of the previous tile's dQ
+// product.  NoDq is the split mode's: nothing.
+struct NoDq {
+  __device__ __forceinline__ void store(int, const bf16x8 (&)[2]) {}
+  __device__ __forceinline__ void step(int) {}
+};
+
+template <int D, class Cfg, bool CAUSAL, bool MASK, class IssuePart, class Dq = NoDq>
 __device__ __forceinline__ void dkdv_tile(const uint16_t* Qb, const uint16_t* dOb, const float* nl, const float* dl,
                                           const BwdOffsets<D, Cfg>& of, const bf16x8 (&kreg)[D / 16],
                                           const bf16x8 (&vreg)[D / 16], f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32],
-                                          int q0, int key, int S, float C, int hh, IssuePart&& issue_part) {
+                                          int q0, int key, int S, float C, int hh, IssuePart&& issue_part,
+                                          Dq&& dq = Dq{}) {
   static_assert(Cfg::NQB == 2 && D / 16 == 8 && D / 32 == 4, "two 32-query blocks, D = 128");
   constexpr int NKS = Cfg::NKS, NDB = Cfg::NDB, CPR = Cfg::CPR;
   tile_marker<MASK>();
@@ -410,6 +420,7 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* Qb, const uint16_t* dO
     pb0[1] = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
     dsb0[0] = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
     dsb0[1] = to_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
+    dq.store(0, dsb0);
   }
   // C: dV, dK with block 0, each MFMA with one element of block 1's softmax
   {
@@ -444,8 +455,10 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* Qb, const uint16_t* dO
     pb1[1] = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
     dsb1[0] = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
     dsb1[1] = to_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
+    dq.store(1, dsb1);
   }
-  // D: dV, dK with block 1; transposed operands one step ahead
+  // D: dV, dK with block 1 (and, fused, a k-step of the previous tile's dQ
+  // per step); transposed operands one step ahead
   {
     bf16x8 ta[2 * NDB], tb[2 * NDB];
     ta[0] = trdo(2, 0); tb[0] = trq(2, 0);
@@ -456,6 +469,7 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* Qb, const uint16_t* dO
       if (i + 1 < 2 * NDB) { ta[i + 1] = trdo(2 + (i + 1) / NDB, (i + 1) % NDB); tb[i + 1] = trq(2 + (i + 1) / NDB, (i + 1) % NDB); }
       dv[db] = mfma32(pb1[t], ta[i], dv[db]);
       dk[db] = mfma32(dsb1[t], tb[i], dk[db]);
+      dq.step(i);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -651,15 +665,15 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
   }
 }
 
-// Split-mode dK/dV kernel for D = 128: the software-pipelined tile of
-// dkdv_tile over 64-query tiles.  One workgroup of four wavefronts owns 128
-// keys; each wavefront keeps its 32 keys' K and V rows and dK, dV
-// accumulators in registers.  The two query-tile buffers are separate
-// __shared__ arrays and the loop is unrolled by two, so that every buffer a
-// tile reads or loads into is known at compile time: the compiler then sees
-// that the next tile's loads cannot alias this tile's LDS transpose reads and
-// does not make those reads wait for the loads, which lets the loads be
-// spread over the tile's MFMA work.
+// dK/dV kernel for D = 128: the software-pipelined tile of dkdv_tile over
+// 64-query tiles.  One workgroup of four wavefronts owns 128 keys; each
+// wavefront keeps its 32 keys' K and V rows and dK, dV accumulators in
+// registers.  The two query-tile buffers are separate __shared__ arrays and
+// the loop is unrolled by two, so that every buffer a tile reads or loads
+// into is known at compile time: the compiler then sees that the next tile's
+// loads cannot alias this tile's LDS transpose reads and does not make those
+// reads wait for the loads, which lets the loads be spread over the tile's
+// MFMA work.
 //
 // Only unmasked tiles sit in the loop (two copies of the tile code, one per
 // buffer set; four would not fit the register budget): with S a multiple of
@@ -667,16 +681,35 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
 // workgroup's first two query tiles (queries k0 .. k0 + 127, the diagonal
 // block), which are peeled off before the loop.  RAGGED (S not a multiple of
 // 128) masks every tile instead.
-template <bool CAUSAL, bool RAGGED>
+//
+// DQ (the fused atomic mode): the kernel also forms dQ, so no second kernel
+// recomputes S and dP.  Each tile's dS goes to LDS transposed (dS^T[key][q],
+// two buffers); in the next tile's phase D every wavefront multiplies it, for
+// its 32 columns of dQ, by the workgroup's 128 K rows (K^T fragments held in
+// AGPRs since the start): dQ[q, 32 w + c] = sum_k dS[q, k] K[k, 32 w + c],
+// 16 MFMAs per tile, and adds the 64 x 32 result, times scale, to the fp32
+// accumulator in global memory with no-return buffer atomics (one workgroup
+// per key tile, so each element of dQ receives one addition per key tile).
+// The result is kept in registers over the barrier and its 32 atomics go
+// out at the start of the following tile, so the end-of-tile wait for that
+// tile's loads (the vector-memory counter does not order loads and stores)
+// finds them long complete.  Non-causal workgroups start their walk over
+// the query tiles at different tiles (rotated by key tile), so that the
+// workgroups of one head running together add into different rows.
+template <bool CAUSAL, bool RAGGED, bool DQ>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ nlse2, const float* __restrict__ delta,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int S, float scale, float C) {
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ dq32, int BH, int S, float scale,
+    float C) {
   constexpr int D = 128;
   using Cfg = BwdCfg<D, 64>;
   constexpr int BK = Cfg::BK, BQ = Cfg::BQ, NKS = Cfg::NKS, NDB = Cfg::NDB, DMA_Q = Cfg::DMA_Q;
   constexpr int NPIECE = 2 * DMA_Q + 1;  // Q pieces, dO pieces, then -LSE log2e / Delta
   static_assert(NPIECE == NKS + 1, "pieces are issued over phases A and B");
+  // dS^T row stride (elements): 64 queries + 8, so that the rows of a
+  // transpose read fall in distinct banks
+  constexpr int DRS = BQ + 8;
 
   __shared__ __attribute__((aligned(1024))) uint16_t Qs0[Cfg::QTILE];
   __shared__ __attribute__((aligned(1024))) uint16_t Qs1[Cfg::QTILE];
@@ -686,6 +719,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(256))) float nl1[Cfg::LROWS];
   __shared__ __attribute__((aligned(256))) float dl0[Cfg::LROWS];
   __shared__ __attribute__((aligned(256))) float dl1[Cfg::LROWS];
+  __shared__ __attribute__((aligned(256))) uint16_t dsT0[DQ ? BK * DRS : 8];
+  __shared__ __attribute__((aligned(256))) uint16_t dsT1[DQ ? BK * DRS : 8];
 
   const int id = blockIdx.x;
   const int bh = id % BH;
@@ -717,6 +752,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   BwdOffsets<D, Cfg> of;
   of.init(wave, lane);
 
+  // query tiles in walking order: causal from the diagonal on, non-causal
+  // (fused mode) rotated by key tile
+  const int nqt = (S + BQ - 1) / BQ;
+  const int qt0 = CAUSAL ? (k0 / BQ) : 0;
+  const int ntiles = nqt - qt0;
+  const int rot = (!CAUSAL && DQ) ? (ktile * (nqt >= 8 ? nqt / 8 : 1)) % nqt : 0;
+  auto qt_at = [&](int i) { return CAUSAL ? qt0 + i : (i + rot < nqt ? i + rot : i + rot - nqt); };
+
   // piece p of query tile qt's loads into buffer set P (0: Qs0 ..., 1: Qs1 ...)
   auto piece = [&](int qt, auto P, int p) {
     constexpr int set = decltype(P)::value;
@@ -735,10 +778,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     }
   };
 
-  const int nqt = (S + BQ - 1) / BQ;
-  const int qt0 = CAUSAL ? (k0 / BQ) : 0;
 #pragma unroll
-  for (int p = 0; p < NPIECE; ++p) piece(qt0, std::integral_constant<int, 0>{}, p);
+  for (int p = 0; p < NPIECE; ++p) piece(qt_at(0), std::integral_constant<int, 0>{}, p);
 
   // K / V rows of this lane's key as MFMA operands (rows past the end are
   // clamped; their P is masked).  The pipelined tile needs more than the 256
@@ -762,6 +803,49 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       vreg[ks] = __builtin_bit_cast(bf16x8, vv[ks]);
     }
   }
+
+  // ---- fused dQ: operands, offsets, the atomic target ---------------------
+  // B operand of k-step t: K[k0 + 16 t + slot key][32 wave + c32] with slot j
+  // of lane half hh holding key 8 (j / 4) + 4 hh + j % 4 (the key order of the
+  // dS^T transpose reads); keys past S are zero.
+  bf16x8 kT[DQ ? 8 : 1];
+  // A operand reads: dS^T rows (keys) 16 t + 8 r2 + 4 hh + (i >> 2), columns
+  // (queries) 32 qb + 16 (g16 & 1) + 4 (i & 3): byte offsets for r2 = 0, 1
+  int dso[2] = {0, 0};
+  int dsw = 0;  // this lane's dS^T row (its key) in bytes
+  // the head's fp32 dQ rows as a buffer resource: rows past S fall outside
+  // it, so the atomics of a ragged tile's missing rows are dropped
+  const __amdgpu_buffer_rsrc_t dqrs = __builtin_amdgcn_make_buffer_rsrc(
+      DQ ? (void*)(dq32 + (size_t)bh * S * D) : (void*)dq32, (short)0, DQ ? S * D * 4 : 0, kBufRsrcWord3);
+  uint32_t dqlane = 0;  // byte offset of this lane's dQ element in row 0 of a 4-row group
+  if constexpr (DQ) {
+    const int i16 = lane & 15, g16 = lane >> 4;
+#pragma unroll
+    for (int r2 = 0; r2 < 2; ++r2)
+      dso[r2] = ((8 * r2 + 4 * (g16 >> 1) + (i16 >> 2)) * DRS + 16 * (g16 & 1) + 4 * (i16 & 3)) * 2;
+    dsw = (32 * wave + c32) * DRS * 2;
+    const int dcol = 32 * wave + c32;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      uint32_t w[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        uint16_t h2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int j = 2 * m + u;
+          const int kk = k0 + 16 * t + 8 * (j >> 2) + 4 * hh + (j & 3);
+          h2[u] = kk < S ? Kh[(size_t)kk * D + dcol] : (uint16_t)0;
+        }
+        w[m] = (uint32_t)h2[0] | ((uint32_t)h2[1] << 16);
+      }
+      u32x4 v = {w[0], w[1], w[2], w[3]};
+      asm volatile("" : "+a"(v));
+      kT[t] = __builtin_bit_cast(bf16x8, v);
+    }
+    dqlane = (uint32_t)((4 * hh) * D + dcol) * 4u;
+  }
+
   f32x16 dk[NDB], dv[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
@@ -771,21 +855,95 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   wait_vm_lds<0>();
   barrier_keep_loads();
 
+  // dQ of a finished tile (its dS^T in `src`, queries q0 ..): per k-step t,
+  // the A operands of both 32-query blocks by transpose reads, two MFMAs;
+  // then the atomics (scale applied).
+  auto dq_read = [&](const uint16_t* src, int t, int qb) {
+    const int o = (16 * t * DRS + 32 * qb) * 2;
+    return tr_operand(at_bytes(src, dso[0] + o), at_bytes(src, dso[1] + o));
+  };
+  auto dq_atomics = [&](const f32x16 (&acc)[2], int q0) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t voff = dqlane + (uint32_t)((q0 + 32 * qb + 8 * g) * D) * 4u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[qb][4 * g + e] * scale, dqrs, voff + e * D * 4, 0, 0);
+      }
+    }
+  };
+
+  // Hooks for dkdv_tile in the fused mode: this tile's dS^T into `cur`, the
+  // previous tile's dQ from `prev` in phase D.
+  struct Hooks {
+    uint16_t* cur;
+    const uint16_t* prev;
+    int dsw, hh;
+    const int* dso;
+    const bf16x8* kT;
+    f32x16 acc[2];
+    bf16x8 a[2][2];  // [parity of k-step][qb]
+    int DRS_;
+    __device__ __forceinline__ bf16x8 rd(int t, int qb) {
+      const int o = (16 * t * DRS_ + 32 * qb) * 2;
+      return tr_operand(at_bytes(prev, dso[0] + o), at_bytes(prev, dso[1] + o));
+    }
+    __device__ __forceinline__ void store(int qb, const bf16x8 (&d)[2]) {
+      // register 8 h2 + e4 (h2 = 0, 1) of pair half holds query 32 qb + 8 (2 half + h2) + 4 hh + e4:
+      // four consecutive queries per 8-byte store
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const u32x4 w = __builtin_bit_cast(u32x4, d[half]);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int col = 32 * qb + 8 * (2 * half + h2) + 4 * hh;
+          *reinterpret_cast<u32x2*>(reinterpret_cast<char*>(cur) + dsw + col * 2) = u32x2{w[2 * h2], w[2 * h2 + 1]};
+        }
+      }
+    }
+    __device__ __forceinline__ void step(int i) {
+      if (i == 0) {
+        acc[0] = f32x16{};
+        acc[1] = f32x16{};
+        a[0][0] = rd(0, 0);
+        a[0][1] = rd(0, 1);
+      }
+      if (i + 1 < 8) {
+        a[(i + 1) & 1][0] = rd(i + 1, 0);
+        a[(i + 1) & 1][1] = rd(i + 1, 1);
+      }
+      acc[0] = mfma32(a[i & 1][0], kT[i], acc[0]);
+      acc[1] = mfma32(a[i & 1][1], kT[i], acc[1]);
+    }
+  };
+
+  // dQ of tile i - 1, formed during tile i, waiting for its atomics
+  f32x16 pend[2] = {f32x16{}, f32x16{}};
+
   // one tile: reads buffer set P, loads the next tile into set 1 - P.  M:
   // masked tile (diagonal or ragged), where a causal wave may also have no
-  // query at or after its keys (inactive: it only issues its loads).
-  auto tile = [&](int qt, auto P, auto M) {
+  // query at or after its keys (inactive: it only issues its loads; in the
+  // fused mode every wave stays active, its masked dS being the zeros the
+  // dQ product needs).
+  auto tile = [&](int i, auto P, auto M) {
     constexpr int set = decltype(P)::value;
     constexpr bool MASK = decltype(M)::value;
     using Next = std::integral_constant<int, 1 - set>;
+    const int qt = qt_at(i);
     const int q0 = qt * BQ;
-    const bool has_next = qt + 1 < nqt;
-    const bool active = !(CAUSAL && MASK) || (q0 + BQ - 1 >= kw0);  // wave-uniform
+    const bool has_next = i + 1 < ntiles;
+    const int qtn = has_next ? qt_at(i + 1) : qt;
+    const bool active = DQ || !(CAUSAL && MASK) || (q0 + BQ - 1 >= kw0);  // wave-uniform
+    if constexpr (DQ) {
+      if (i >= 2) dq_atomics(pend, qt_at(i - 2) * BQ);  // formed during the previous tile
+    }
     if (active) {
       // after the last tile the pieces reload it into the free set (in bounds,
       // never read), which keeps the tile branch-free
       auto part = [&](int p) {
-        if (p < NPIECE) piece(has_next ? qt + 1 : qt, Next{}, p);
+        if (p < NPIECE) piece(qtn, Next{}, p);
       };
       const uint16_t* Qb = set ? Qs1 : Qs0;
       const uint16_t* dOb = set ? dOs1 : dOs0;
@@ -800,29 +958,55 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(ot.arow[ks]));
 #pragma unroll
       for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(ot.trq[db][0]), "+v"(ot.trq[db][1]));
-      dkdv_tile<D, Cfg, CAUSAL, MASK>(Qb, dOb, nl, dl, ot, kreg, vreg, dk, dv, q0, key, S, C, hh, part);
+      if constexpr (DQ) {
+        int dso_t[2] = {dso[0], dso[1]};
+        int dsw_t = dsw;
+        asm volatile("" : "+v"(dso_t[0]), "+v"(dso_t[1]), "+v"(dsw_t));
+        Hooks hk{set ? dsT1 : dsT0, set ? dsT0 : dsT1, dsw_t, hh, dso_t, kT, {}, {}, DRS};
+        dkdv_tile<D, Cfg, CAUSAL, MASK>(Qb, dOb, nl, dl, ot, kreg, vreg, dk, dv, q0, key, S, C, hh, part, hk);
+        // the previous tile's dQ (a first tile has none: its MFMAs read a
+        // buffer no tile has written yet, and the result is never added)
+        pend[0] = hk.acc[0];
+        pend[1] = hk.acc[1];
+      } else {
+        dkdv_tile<D, Cfg, CAUSAL, MASK>(Qb, dOb, nl, dl, ot, kreg, vreg, dk, dv, q0, key, S, C, hh, part);
+      }
     } else if (has_next) {
 #pragma unroll
-      for (int p = 0; p < NPIECE; ++p) piece(qt + 1, Next{}, p);
+      for (int p = 0; p < NPIECE; ++p) piece(qtn, Next{}, p);
     }
-    // the next tile's loads landed (this wave's) and all LDS reads done; the
-    // barrier publishes the tile and frees this one
+    // the next tile's loads landed (this wave's) and all LDS reads and dS
+    // stores done; the barrier publishes the tile and frees this one
     __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (0 << 14));  // vmcnt(0) lgkmcnt(0)
     barrier_keep_loads();
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   using M = std::integral_constant<bool, RAGGED>;
-  int qt = qt0;
+  int i = 0;
   if constexpr (CAUSAL && !RAGGED) {  // diagonal block: qt0 even, nqt >= qt0 + 2
-    tile(qt, P0{}, std::true_type{});
-    tile(qt + 1, P1{}, std::true_type{});
-    qt += 2;
+    tile(0, P0{}, std::true_type{});
+    tile(1, P1{}, std::true_type{});
+    i = 2;
   }
-  for (; qt < nqt; qt += 2) {
-    tile(qt, P0{}, M{});
-    if (RAGGED && qt + 1 >= nqt) break;  // without RAGGED the tile count is even
-    tile(qt + 1, P1{}, M{});
+  for (; i < ntiles; i += 2) {
+    tile(i, P0{}, M{});
+    if (RAGGED && i + 1 >= ntiles) break;  // without RAGGED the tile count is even
+    tile(i + 1, P1{}, M{});
+  }
+
+  // ---- fused: the last two tiles' dQ --------------------------------------
+  if constexpr (DQ) {
+    if (ntiles >= 2) dq_atomics(pend, qt_at(ntiles - 2) * BQ);
+    const int last = ntiles - 1;
+    const uint16_t* src = (last & 1) ? dsT1 : dsT0;
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      acc[0] = mfma32(dq_read(src, t, 0), kT[t], acc[0]);
+      acc[1] = mfma32(dq_read(src, t, 1), kT[t], acc[1]);
+    }
+    dq_atomics(acc, qt_at(last) * BQ);
   }
 
   // ---- epilogue: dK = scale * acc, dV = acc (bf16) -------------------------
@@ -840,21 +1024,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   }
 }
 
-template <bool CAUSAL, bool RAGGED>
+template <bool CAUSAL, bool RAGGED, bool DQ>
 static hipError_t launch_dkdv_pipe_rt(const BwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   const int nkt = (a.S + 127) / 128;
-  prof_begin(KID_BWD_DKDV, st);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<CAUSAL, RAGGED>), dim3(nkt * BH), dim3(256), 0, st, (const uint16_t*)a.Q,
+  const int kid = DQ ? KID_BWD_MAIN : KID_BWD_DKDV;
+  prof_begin(kid, st);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<CAUSAL, RAGGED, DQ>), dim3(nkt * BH), dim3(256), 0, st, (const uint16_t*)a.Q,
                      (const uint16_t*)a.K, (const uint16_t*)a.V, (const uint16_t*)a.dO, a.nlse2, a.delta,
-                     (uint16_t*)a.dK, (uint16_t*)a.dV, BH, a.S, a.scale, a.scale * kLog2e);
-  prof_end(KID_BWD_DKDV, st);
+                     (uint16_t*)a.dK, (uint16_t*)a.dV, a.dq32, BH, a.S, a.scale, a.scale * kLog2e);
+  prof_end(kid, st);
   return hipGetLastError();
 }
 
 template <bool CAUSAL>
 static hipError_t launch_dkdv_pipe_t(const BwdArgs& a, hipStream_t st) {
-  return (a.S % 128 == 0) ? launch_dkdv_pipe_rt<CAUSAL, false>(a, st) : launch_dkdv_pipe_rt<CAUSAL, true>(a, st);
+  return (a.S % 128 == 0) ? launch_dkdv_pipe_rt<CAUSAL, false, false>(a, st)
+                          : launch_dkdv_pipe_rt<CAUSAL, true, false>(a, st);
 }
 
 // Delta_i = sum_d dO_id O_id (fp32), nlse2_i = -LSE_i log2(e), and zero the
@@ -956,8 +1142,15 @@ static hipError_t launch_main(const BwdArgs& a, hipStream_t st) {
     switch (a.D * 2 + (a.causal ? 1 : 0)) {
       case 128: return launch_main_t<64, 64, false, true, false, 1>(a, st);
       case 129: return launch_main_t<64, 64, true, true, false, 1>(a, st);
-      case 256: return launch_main_t<128, 64, false, true, false, 1>(a, st);
-      case 257: return launch_main_t<128, 64, true, true, false, 1>(a, st);
+      // S a multiple of 128: the fused pipelined kernel; otherwise the
+      // one-pass tile (the fused tile's masked-on-every-tile form needs more
+      // registers than the compiler can allocate)
+      case 256:
+        return a.S % 128 == 0 ? launch_dkdv_pipe_rt<false, false, true>(a, st)
+                              : launch_main_t<128, 64, false, true, false, 1>(a, st);
+      case 257:
+        return a.S % 128 == 0 ? launch_dkdv_pipe_rt<true, false, true>(a, st)
+                              : launch_main_t<128, 64, true, true, false, 1>(a, st);
       default: return hipErrorInvalidValue;
     }
   } else {
