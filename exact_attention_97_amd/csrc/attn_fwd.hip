@@ -170,19 +170,29 @@ struct FwdWave {
     }
   }
 
-  // Region 1 of one tile (no branches): mask (diagonal or ragged tiles),
-  // row max and the rescale decision first, then the next tile's scores on
-  // the MFMA unit interleaved with this tile's exponentials on the VALU.
-  // Returns P (bf16) and the rescale decision for region 2.  The next tile's
-  // scores are computed even after the wave's last tile (from a stale buffer,
-  // never used) so that region 1 has no branch.
+  // Where an unmasked tile's row max is taken: with eight wavefronts (the
+  // D = 128 tile for long sequences) in the previous tile's region 2, under
+  // its P V MFMAs (1.3 % faster at S = 8192); with four wavefronts in region
+  // 1 (measured: neutral at D = 128, S = 4096, 1.5 % slower at D = 256, 7 %
+  // at D = 64).
+  static constexpr bool kMaxAhead = Cfg::NW == 8;
+
+  // Region 1 of one tile (no branches): for a masked tile (diagonal or
+  // ragged) the mask and the row max, for an unmasked one the row max (taken
+  // in the previous tile's region 2, mx_pre, when kMaxAhead); the rescale
+  // decision; then the
+  // next tile's scores on the MFMA unit interleaved with this tile's
+  // exponentials on the VALU.  Returns P (bf16) and the rescale decision for
+  // region 2.  The next tile's scores are computed even after the wave's
+  // last tile (from a stale buffer, never used) so that region 1 has no
+  // branch.
   template <bool MASK>
   __device__ __forceinline__ static void region1(const uint16_t* knext, const FwdOffsets<Cfg>& of,
                                                  const bf16x8 (&qreg)[NKS], f32x16 (&scur)[NKB],
                                                  f32x16 (&snext)[NKB], float& m_run, float& l_part, int k0, int lim,
-                                                 int hh, float C, float tau, bf16x8 (&pb)[2 * NKB], bool& grow,
-                                                 float& alpha) {
-    const float mx = tile_max<MASK>(scur, k0, lim, hh);
+                                                 int hh, float C, float tau, float mx_pre, bf16x8 (&pb)[2 * NKB],
+                                                 bool& grow, float& alpha) {
+    const float mx = (MASK || !kMaxAhead) ? tile_max<MASK>(scur, k0, lim, hh) : mx_pre;
     const float mxs = (mx == kNegInf) ? kNegInf : mx * C;
     const float m_new = __builtin_fmaxf(m_run, mxs);
     // conditional rescale: the wave moves its running max only when some
@@ -205,37 +215,46 @@ struct FwdWave {
     __builtin_amdgcn_s_setprio(0);
   }
 
-  // P V with its transpose loads: the reads run eight ahead (two per MFMA
-  // operand, so three MFMAs of look-ahead under the exact LDS wait counts).
+  // P V with its transpose loads (the reads run eight ahead: two per MFMA
+  // operand, so three MFMAs of look-ahead under the exact LDS wait counts),
+  // and, with kMaxAhead, on the VALU meanwhile, the row max of the next
+  // tile's scores (without the mask; a masked tile takes its own in region
+  // 1).  Region 1 carries the whole softmax and this region none otherwise.
   __device__ __forceinline__ static void region2(const uint16_t* vcur, const FwdOffsets<Cfg>& of,
-                                                 const bf16x8 (&pb)[2 * NKB], f32x16 (&oacc)[NDB]) {
+                                                 const bf16x8 (&pb)[2 * NKB], f32x16 (&oacc)[NDB],
+                                                 f32x16 (&snext)[NKB], float& mx_next) {
     pv(vcur, of, pb, oacc);
+    if constexpr (kMaxAhead) mx_next = tile_max<false>(snext, 0, 0, 0);
     constexpr int NP = 2 * NKB * NDB, PVA = 8;
     __builtin_amdgcn_sched_group_barrier(0x100, PVA, 1);
 #pragma unroll
     for (int i = 0; i < NP - PVA / 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      if constexpr (kMaxAhead) __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, PVA / 2, 1);
+    if constexpr (kMaxAhead) __builtin_amdgcn_sched_group_barrier(0x002, 8, 1);
   }
 
   // One whole tile: region 1, the (rare) rescale of the output accumulator,
-  // region 2.
+  // region 2.  mx_pre: this tile's unmasked row max (from the previous
+  // tile's region 2); mx_next: the next tile's, for the following step.
   template <bool MASK>
   __device__ __forceinline__ static void step(const uint16_t* knext, const uint16_t* vcur, const FwdOffsets<Cfg>& of,
                                               const bf16x8 (&qreg)[NKS], f32x16 (&scur)[NKB],
                                               f32x16 (&snext)[NKB], f32x16 (&oacc)[NDB], float& m_run,
-                                              float& l_part, int k0, int lim, int hh, float C, float tau) {
+                                              float& l_part, int k0, int lim, int hh, float C, float tau,
+                                              float mx_pre, float& mx_next) {
     bf16x8 pb[2 * NKB];
     bool grow;
     float alpha;
-    region1<MASK>(knext, of, qreg, scur, snext, m_run, l_part, k0, lim, hh, C, tau, pb, grow, alpha);
+    region1<MASK>(knext, of, qreg, scur, snext, m_run, l_part, k0, lim, hh, C, tau, mx_pre, pb, grow, alpha);
     if (grow) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
     }
-    region2(vcur, of, pb, oacc);
+    region2(vcur, of, pb, oacc, snext, mx_next);
   }
 };
 
@@ -399,7 +418,9 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
   // scores of the current and the next tile; the loop is unrolled by two so
   // that the two sets swap roles instead of being copied
   f32x16 sa[NKB], sb[NKB];
+  float ma = kNegInf, mb = kNegInf;  // unmasked row maxima of the tiles in sa / sb
   W::scores(Kb0, of, qreg, sa);
+  if constexpr (W::kMaxAhead) ma = W::template tile_max<false>(sa, 0, 0, 0);
   // iteration 0 reloads buffer 0 (with K(NBUF)): every wave's reads of K(0)
   // must be complete first
   wait_vm_lds<63>();
@@ -407,7 +428,7 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
 
   // P = kt & 1 (the loop is unrolled by two); with two buffers all indices
   // follow from it at compile time
-  auto iteration = [&](int kt, auto P, f32x16(&scur)[NKB], f32x16(&snext)[NKB]) {
+  auto iteration = [&](int kt, auto P, f32x16(&scur)[NKB], f32x16(&snext)[NKB], float& mcur, float& mnext) {
     constexpr int par = decltype(P)::value;
     const int kn = NBUF == 2 ? 1 - par : (kt + 1) % NBUF;  // K(kt + 1)
     const int vc = NBUF == 2 ? par : kt % NBUF;            // V(kt)
@@ -418,17 +439,17 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
     if (kt < nkt_w) {
       if (kt < nfull)
         W::template step<false>(kbuf(kn), vbuf(vc), of, qreg, scur, snext, oacc, m_run, l_part, kb + kt * BC, lim,
-                                hh, C, tau);
+                                hh, C, tau, mcur, mnext);
       else
         W::template step<true>(kbuf(kn), vbuf(vc), of, qreg, scur, snext, oacc, m_run, l_part, kb + kt * BC, lim,
-                               hh, C, tau);
+                               hh, C, tau, mcur, mnext);
     }
     wait_loads(n_last);
     barrier_keep_loads();
   };
   for (int kt = 0; kt < nkt; kt += 2) {
-    iteration(kt, std::integral_constant<int, 0>{}, sa, sb);
-    if (kt + 1 < nkt) iteration(kt + 1, std::integral_constant<int, 1>{}, sb, sa);
+    iteration(kt, std::integral_constant<int, 0>{}, sa, sb, ma, mb);
+    if (kt + 1 < nkt) iteration(kt + 1, std::integral_constant<int, 1>{}, sb, sa, mb, ma);
   }
 
 // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l) ----------------------

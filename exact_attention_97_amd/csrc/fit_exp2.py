@@ -6,7 +6,8 @@ exp2(0) is exactly 1 (a row's own maximum then contributes exactly one).
 The remaining coefficients minimise the maximum relative error on [0, 1)
 by a linear-programming minimax fit on a dense grid (scipy.optimize.linprog),
 then the float32-rounded coefficients are re-evaluated in float32 Horner
-form.  Run: python fit_exp2.py  (prints the constants for exp2.hpp).
+form.  Run: python fit_exp2.py  (prints the constants of exp2_poly in
+device_common.hpp; tests/test_oracle.py checks that the header holds them).
 """
 
 import numpy as np

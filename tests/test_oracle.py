@@ -470,3 +470,31 @@ def test_suffix_pin_catches_top_left_alignment():
         return o, l
 
     assert _suffix_pin_failures(fwd_top_left)
+
+
+def test_poly_exp2_constants_are_the_fit():
+    """The three constants of the kernels' software exp2 (exp2_poly in
+    device_common.hpp, Horner form c3 f^3 + c2 f^2 + c1 f + 1) are the
+    float32 rounding of fit_exp2.py's minimax fit, and that fit's maximum
+    relative error on [0, 1) is the 8.6e-5 the kernels' comments state."""
+    import importlib.util
+    import os
+    import re
+
+    here = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    csrc = os.path.join(here, "exact_attention_97_amd", "csrc")
+    spec = importlib.util.spec_from_file_location("fit_exp2", os.path.join(csrc, "fit_exp2.py"))
+    fit_exp2 = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(fit_exp2)
+    c, err = fit_exp2.fit(3)
+    text = open(os.path.join(csrc, "device_common.hpp")).read()
+    body = text[text.index("float exp2_poly(float x)"):]
+    body = body[:body.index("}")]
+    lits = [float(x) for x in re.findall(r"([0-9.]+e[-+][0-9]+)f", body)]
+    assert len(lits) == 3, lits
+    c3, c2, c1 = (np.float32(x) for x in lits)
+    assert (c1, c2, c3) == tuple(np.float32(x) for x in c)
+    assert 8.5e-5 < err < 8.65e-5
+    f = np.linspace(0, 1, 200001, endpoint=False)
+    rel = np.max(np.abs(fit_exp2.eval_f32(c, f).astype(np.float64) / np.exp2(f) - 1.0))
+    assert rel < 8.7e-5
