@@ -319,18 +319,6 @@ __device__ __forceinline__ void bwd_tile(BwdSmem<Cfg, WRITE_DS, VLDS>& sm, int b
 // softmax").  Scheduling barriers keep each phase's instructions together and
 // interleave them in fixed proportions.
 
-// One score element of the softmax: P = exp2(S c - LSE log2e), masked, and
-// dS = P (dP - Delta).  r is the accumulator register (row 8 (r/4) + 4 hh +
-// r%4 of block qb), nl / dl the block's -LSE log2e and Delta.
-template <bool MASK>
-__device__ __forceinline__ void dkdv_elem(const f32x16& sacc, const f32x16& dpacc, int r, float nl, float dl,
-                                          float C, int c, int mlo, int mhi, float& p, float& ds) {
-  float pv = exp2_native(__builtin_fmaf(sacc[r], C, nl));
-  if (MASK) pv = (c >= mlo && c < mhi) ? pv : 0.0f;
-  p = pv;
-  ds = pv * (dpacc[r] - dl);
-}
-
 // Qb, dOb, nl, dl: this tile's Q and dO tiles and -LSE log2e / Delta rows in
 // LDS.  issue_part(p) issues piece p of the next tile's loads; the pieces go
 // out over phases A and B, one every other step (issued back to back they
@@ -370,8 +358,35 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* Qb, const uint16_t* dO
     return tr_operand(at_bytes(Qb, of.trq[db][0]) + o, at_bytes(Qb, of.trq[db][1]) + o);
   };
 
-  f32x16 s0 = f32x16{}, dp0 = f32x16{}, s1 = f32x16{}, dp1 = f32x16{};
-  float p[16], ds[16];
+  // the dP accumulators start from Delta (rows 8 g + 4 hh + e of each block)
+  auto delta_init = [&](int qb) {
+    f32x16 acc;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dl[32 * qb + 8 * g + 4 * hh]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[4 * g + e] = d4[e];
+    }
+    return acc;
+  };
+  f32x16 s0 = f32x16{}, dp0 = delta_init(0), s1 = f32x16{}, dp1;
+  uint32_t pw[8], gw[8];  // P / dS of a block, two bf16 per register as they are formed
+  float pe = 0.f, ge = 0.f;
+  auto put = [&](int r, float pv, float gv) {
+    if (r & 1) {
+      pw[r >> 1] = pack_bf16x2(pe, pv);
+      gw[r >> 1] = pack_bf16x2(ge, gv);
+    } else {
+      pe = pv;
+      ge = gv;
+    }
+  };
+  auto packed = [&](bf16x8 (&pb)[2], bf16x8 (&gb)[2]) {
+    pb[0] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+    pb[1] = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
+    gb[0] = __builtin_bit_cast(bf16x8, u32x4{gw[0], gw[1], gw[2], gw[3]});
+    gb[1] = __builtin_bit_cast(bf16x8, u32x4{gw[4], gw[5], gw[6], gw[7]});
+  };
   bf16x8 pb0[2], dsb0[2], pb1[2], dsb1[2];
 
   // A: S, dP of block 0; operand reads two steps ahead
@@ -383,78 +398,102 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* Qb, const uint16_t* dO
     for (int ks = 0; ks < NKS; ++ks) {
       if (ks + 2 < NKS) { qa[ks + 2] = qfrag(0, ks + 2); da[ks + 2] = dofrag(0, ks + 2); }
       if ((ks & 1) == 0) issue_part(ks / 2);
+      if (ks == NKS - 1) dp1 = delta_init(1);
       s0 = mfma32(qa[ks], kreg[ks], s0);
       dp0 = mfma32(da[ks], vreg[ks], dp0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  // The softmax of a block runs as a three-stage software pipeline over the
+  // eight steps of a phase, two elements per step: step k forms the exponent
+  // argument of step k + 1's elements, exponentiates step k's and forms dS of
+  // step k - 1's, so that no instruction waits on the one just before it and
+  // the MFMAs issue on time.  tt: arguments, pp: P.
+  float tt[16], pp[16];
+  auto sm_arg = [&](const f32x16& sacc, const f32x4 (&l4)[4], int r) {
+    tt[r] = __builtin_fmaf(sacc[r], C, l4[(r >> 2) & 3][r & 3]);
+  };
+  auto sm_exp = [&](int r, int c) {
+    float pv = exp2_native(tt[r]);
+    if (MASK) pv = (c >= mlo && c < mhi) ? pv : 0.0f;
+    pp[r] = pv;
+  };
+  auto sm_ds = [&](const f32x16& ndacc, int r) { put(r, pp[r], -pp[r] * ndacc[r]); };
+
   // B: S, dP of block 1, each step with two elements of block 0's softmax
   {
     bf16x8 qa[NKS], da[NKS];
-    f32x4 l4[4], d4[4];
+    f32x4 l4[4];
     qa[0] = qfrag(1, 0); da[0] = dofrag(1, 0);
     l4[0] = *reinterpret_cast<const f32x4*>(&nl[4 * hh]);
-    d4[0] = *reinterpret_cast<const f32x4*>(&dl[4 * hh]);
+    l4[1] = *reinterpret_cast<const f32x4*>(&nl[8 + 4 * hh]);
     qa[1] = qfrag(1, 1); da[1] = dofrag(1, 1);
+    sm_arg(s0, l4, 0);
+    sm_arg(s0, l4, 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       if (ks + 2 < NKS) { qa[ks + 2] = qfrag(1, ks + 2); da[ks + 2] = dofrag(1, ks + 2); }
-      if ((ks & 1) == 0 && ks / 2 + 1 < 4) {
-        const int g = ks / 2 + 1;
+      if (ks == 1 || ks == 3) {  // rows of elements 8 g .. 8 g + 7 (steps 2 g - 1, 2 g: arguments)
+        const int g = ks / 2 + 2;
         l4[g] = *reinterpret_cast<const f32x4*>(&nl[8 * g + 4 * hh]);
-        d4[g] = *reinterpret_cast<const f32x4*>(&dl[8 * g + 4 * hh]);
       }
       if ((ks & 1) == 0) issue_part(NKS / 2 + ks / 2);
       if (ks == NKS - 1) issue_part(NKS);
       s1 = mfma32(qa[ks], kreg[ks], s1);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int r = 2 * ks + u, g = r >> 2, e = r & 3;
-        dkdv_elem<MASK>(s0, dp0, r, l4[g][e], d4[g][e], C, 8 * g + e, mlo, mhi, p[r], ds[r]);
+      if (ks + 1 < NKS) {
+        sm_arg(s0, l4, 2 * ks + 2);
+        sm_arg(s0, l4, 2 * ks + 3);
       }
+      sm_exp(2 * ks, 8 * (ks >> 1) + 2 * (ks & 1));
+      sm_exp(2 * ks + 1, 8 * (ks >> 1) + 2 * (ks & 1) + 1);
       dp1 = mfma32(da[ks], vreg[ks], dp1);
+      if (ks >= 1) {
+        sm_ds(dp0, 2 * ks - 2);
+        sm_ds(dp0, 2 * ks - 1);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    pb0[0] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-    pb0[1] = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
-    dsb0[0] = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
-    dsb0[1] = to_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
+    sm_ds(dp0, 14);
+    sm_ds(dp0, 15);
+    packed(pb0, dsb0);
     dq.store(0, dsb0);
   }
   // C: dV, dK with block 0, each MFMA with one element of block 1's softmax
   {
     bf16x8 ta[2 * NDB], tb[2 * NDB];  // [t][db] transposed dO / Q operands
-    f32x4 l4[4], d4[4];
+    f32x4 l4[4];
     ta[0] = trdo(0, 0); tb[0] = trq(0, 0);
     l4[0] = *reinterpret_cast<const f32x4*>(&nl[32 + 4 * hh]);
-    d4[0] = *reinterpret_cast<const f32x4*>(&dl[32 + 4 * hh]);
+    l4[1] = *reinterpret_cast<const f32x4*>(&nl[32 + 8 + 4 * hh]);
+    sm_arg(s1, l4, 0);
+    sm_arg(s1, l4, 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 2 * NDB; ++i) {  // i = 4 t + db
       const int t = i / NDB, db = i % NDB;
       if (i + 1 < 2 * NDB) { ta[i + 1] = trdo((i + 1) / NDB, (i + 1) % NDB); tb[i + 1] = trq((i + 1) / NDB, (i + 1) % NDB); }
-      if ((i & 1) == 0 && i / 2 + 1 < 4) {
-        const int g = i / 2 + 1;
+      if (i == 1 || i == 3) {
+        const int g = i / 2 + 2;
         l4[g] = *reinterpret_cast<const f32x4*>(&nl[32 + 8 * g + 4 * hh]);
-        d4[g] = *reinterpret_cast<const f32x4*>(&dl[32 + 8 * g + 4 * hh]);
       }
       dv[db] = mfma32(pb0[t], ta[i], dv[db]);
-      {
-        const int r = 2 * i, g = r >> 2, e = r & 3;
-        dkdv_elem<MASK>(s1, dp1, r, l4[g][e], d4[g][e], C, 32 + 8 * g + e, mlo, mhi, p[r], ds[r]);
+      if (i + 1 < 2 * NDB) {
+        sm_arg(s1, l4, 2 * i + 2);
+        sm_arg(s1, l4, 2 * i + 3);
       }
+      sm_exp(2 * i, 32 + 8 * (i >> 1) + 2 * (i & 1));
+      sm_exp(2 * i + 1, 32 + 8 * (i >> 1) + 2 * (i & 1) + 1);
       dk[db] = mfma32(dsb0[t], tb[i], dk[db]);
-      {
-        const int r = 2 * i + 1, g = r >> 2, e = r & 3;
-        dkdv_elem<MASK>(s1, dp1, r, l4[g][e], d4[g][e], C, 32 + 8 * g + e, mlo, mhi, p[r], ds[r]);
+      if (i >= 1) {
+        sm_ds(dp1, 2 * i - 2);
+        sm_ds(dp1, 2 * i - 1);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    pb1[0] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-    pb1[1] = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
-    dsb1[0] = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
-    dsb1[1] = to_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
+    sm_ds(dp1, 14);
+    sm_ds(dp1, 15);
+    packed(pb1, dsb1);
     dq.store(1, dsb1);
   }
   // D: dV, dK with block 1 (and, fused, a k-step of the previous tile's dQ
@@ -770,9 +809,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       dma_row_part<D, DMA_Q, RAGGED>(Qh, q0, BQ, S, qd, wave_u, of.dmaq, p);
     } else if (p < 2 * DMA_Q) {
       dma_row_part<D, DMA_Q, RAGGED>(dOh, q0, BQ, S, dd, wave_u, of.dmaq, p - DMA_Q);
-    } else if (p == 2 * DMA_Q && wave < 2) {
-      const float* src = wave == 0 ? NLh : DLh;
-      float* dst = (wave == 0) ? (set ? nl1 : nl0) : (set ? dl1 : dl0);
+    } else if (p == 2 * DMA_Q) {
+      // -LSE log2e rows from waves 0 and 2, Delta from 1 and 3 (the pairs
+      // write the same values): no branch on the wavefront index, which
+      // would split the tile into blocks the compiler moves the softmax
+      // across
+      const bool odd = (wave_u & 1) != 0;
+      const float* src = odd ? DLh : NLh;
+      float* dst = odd ? (set ? dl1 : dl0) : (set ? nl1 : nl0);
       // without RAGGED, S is a multiple of 128 and q0 + 63 < S
       lds_dma<4>(src, (uint32_t)S * 4u, (uint32_t)(RAGGED ? min(q0 + lane, S - 1) : q0 + lane) * 4u, dst);
     }
@@ -785,7 +829,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   // clamped; their P is masked).  The pipelined tile needs more than the 256
   // arch VGPRs; K and V are read only as MFMA operands, which gfx950 takes
   // from AGPRs, so they are placed there once instead of being spilled and
-  // reloaded.
+  // reloaded.  V is held negated (a sign flip, exact in bf16): the dP
+  // accumulator starts from Delta, so the MFMAs leave Delta - dP in it and
+  // dS = -P (Delta - dP) needs no subtraction per element.
   bf16x8 kreg[NKS], vreg[NKS];
   {
     const int keyc = min(key, S - 1);
@@ -794,7 +840,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     for (int ks = 0; ks < NKS; ++ks) {
       const uint32_t off = (uint32_t)keyc * D + 16 * ks + 8 * hh;
       kk[ks] = *reinterpret_cast<const u32x4*>(Kh + off);
-      vv[ks] = *reinterpret_cast<const u32x4*>(Vh + off);
+      vv[ks] = *reinterpret_cast<const u32x4*>(Vh + off) ^ 0x80008000u;
     }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
