@@ -19,6 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libattn97.so")
+UBENCH_SRC = os.path.join(HERE, "microbench", "ubench.hip")
+UBENCH = os.path.join(HERE, "microbench", "ubench")
 
 SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip", "attn_fp8.hip"]
 ARCH = "gfx950"
@@ -64,11 +66,25 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+def build_microbench() -> str:
+    """Compile the pipe-ceiling microbenchmark (a standalone program)."""
+    cmd = [_hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-I", INCLUDE, "-I", CSRC,
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", UBENCH_SRC, "-o", UBENCH + ".tmp"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed for microbench/ubench.hip:\n" + res.stdout + res.stderr)
+    os.replace(UBENCH + ".tmp", UBENCH)
+    return UBENCH
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libattn97.so; returns its path."""
+    """Compile every HIP source and link libattn97.so (and build the
+    microbenchmark program); returns the library's path."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        ub = ex.submit(build_microbench)
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+        ub.result()
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
