@@ -9,6 +9,11 @@ input set-up.
 
     python3 -m exact_attention_97_amd.profile_driver --passes fwd,bwd --iters 2 --copy-mib 1024
     python3 -m exact_attention_97_amd.profile_driver --passes fwd --exp-mode poly --tau 0 --iters 5
+    python3 -m exact_attention_97_amd.profile_driver --passes fwd,bwd --outliers --bwd-seed 7
+
+``--bwd-seed N`` gives the backward pass inputs of its own (iid N(0,1), seed
+N, with O and LSE from one forward call on them), as in the benchmark, whose
+backward leg runs on the iid workload and its forward leg on the outlier one.
 """
 
 from __future__ import annotations
@@ -34,6 +39,8 @@ def main() -> None:
     ap.add_argument("--iters", type=int, default=2)
     ap.add_argument("--bwd-mode", default="split", choices=["split", "atomic"])
     ap.add_argument("--exp-mode", default="native", choices=["native", "poly", "mixed"], help="forward exp2")
+    ap.add_argument("--poly-fraction", type=float, default=0.5, help="share of polynomial exp2 in the mixed mode")
+    ap.add_argument("--bwd-seed", type=int, default=None, help="separate iid inputs for the backward pass")
     ap.add_argument("--tau", type=float, default=8.0, help="forward rescale threshold (log2 units)")
     ap.add_argument("--copy-mib", type=int, default=0, help="MiB of the calibration copy (0 = none)")
     ap.add_argument("--outliers", action="store_true", help="1%% of Q and K entries x20 (the benchmark's inputs)")
@@ -61,8 +68,8 @@ def main() -> None:
     for p in passes:
         if p == "fwd":
             for _ in range(a.iters):
-                L.attn_fwd(q, k, v, scale=scale, causal=causal, exp_mode=a.exp_mode, rescale_tau=a.tau, out=o,
-                           lse=lse)
+                L.attn_fwd(q, k, v, scale=scale, causal=causal, exp_mode=a.exp_mode, rescale_tau=a.tau,
+                           poly_fraction=a.poly_fraction, out=o, lse=lse)
         elif p == "fp8":
             from .inputs import hadamard_signs
 
@@ -72,11 +79,16 @@ def main() -> None:
                 L.fp8_quantize(q, k, v, sg, buf=buf)
                 L.attn_fwd_fp8_quantized(buf, a.B, a.H, a.S, a.D, scale=scale, causal=causal, out=o, lse=lse)
         elif p == "bwd":
+            bq, bk, bv, bdo, bo, blse = q, k, v, do, o, lse
+            if a.bwd_seed is not None:
+                bq, bk, bv, bdo = (t.to(dev) for t in make_qkvdo(a.B, a.H, a.S, a.D, a.bwd_seed))
+                bo, blse = L.attn_fwd(bq, bk, bv, scale=scale, causal=causal)
+                torch.cuda.synchronize()
             ws = torch.empty(L.bwd_workspace_bytes(a.B, a.H, a.S, a.D, causal, bwd_mode=a.bwd_mode),
                              dtype=torch.uint8, device=dev)
             g = [torch.empty_like(q) for _ in range(3)]
             for _ in range(a.iters):
-                L.attn_bwd(q, k, v, o, do, lse, scale=scale, causal=causal, bwd_mode=a.bwd_mode,
+                L.attn_bwd(bq, bk, bv, bo, bdo, blse, scale=scale, causal=causal, bwd_mode=a.bwd_mode,
                            workspace=ws, dq=g[0], dk=g[1], dv=g[2])
         else:
             raise SystemExit(f"unknown pass {p!r}")
