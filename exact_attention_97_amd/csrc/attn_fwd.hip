@@ -684,12 +684,13 @@ static hipError_t launch_fwd_e(const FwdArgs& a, hipStream_t st) {
   }
 }
 
-// The D = 128 tile by sequence length (measured on MI355X): up to 4096
-// queries four wavefronts (128 queries) per workgroup; longer sequences take
-// the cooperative big tile, eight wavefronts (256 queries) sharing each K / V
-// tile in LDS (1-2 % faster at B=2, H=16, S=8192 with the outlier inputs;
-// shorter sequences have few 256-query tiles per head and balance better with
-// four wavefronts: 4-6 % faster at S = 2048, 0.5-2 % at 4096).  Variant 1
+// The D = 128 tile by sequence length (measured on MI355X, B=2, H=16, with
+// the outlier inputs): from S = 8192 on the cooperative big tile, eight
+// wavefronts (256 queries) sharing each K / V tile in LDS (2-3 % faster at
+// S = 8192); below that four wavefronts (128 queries) per workgroup, whose
+// smaller workgroups balance the few query tiles per head better (4-6 %
+// faster at S = 2048, 0.5-2 % at 4096, 4 % at 5120 and 3 % at 7168; at 6144
+// 3 % slower non-causal and 2 % faster causal).  Variant 1
 // (attn_set_variant("fwd", 1) or ATTN97_FWD_VARIANT=1) takes the eight-
 // wavefront tile at every length, so that its ragged and short cases can be
 // tested.  Split-KV keeps four, which suits few query rows.
@@ -699,7 +700,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   switch (a.D) {
     case 64: return launch_fwd_e<FwdDefault<64>::type>(a, st);
     case 128:
-      if (fwd_variant() == 1 || a.S > 4096) return launch_fwd_e<FwdCfg<128, 64, 8, 2>>(a, st);
+      if (fwd_variant() == 1 || a.S >= 8192) return launch_fwd_e<FwdCfg<128, 64, 8, 2>>(a, st);
       return launch_fwd_e<FwdDefault<128>::type>(a, st);
     case 256: return launch_fwd_e<FwdDefault<256>::type>(a, st);
     default: return hipErrorInvalidValue;
