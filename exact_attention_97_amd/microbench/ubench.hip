@@ -1,8 +1,8 @@
 // ubench.hip - pipe ceilings of the MI355X (gfx950) compute unit that the
 // attention kernels are designed against: matrix-core throughput per MFMA
 // shape, VALU and transcendental issue cost, the overlap of a wavefront's
-// own MFMAs with its VALU work, and LDS read bandwidth for the read forms the
-// kernels use.  None of these figures are on the pages; they are measured.
+// own MFMAs with its VALU work, LDS read bandwidth for the read forms the
+// kernels use, and the rate and placement of fp32 atomic adds.  None of these figures are on the pages; they are measured.
 //
 // Each kernel reads the shader clock (s_memtime) in every wavefront around
 // its timed loop, so per-instruction costs are in core clock cycles; HIP
@@ -13,7 +13,8 @@
 //          -Xclang -target-feature -Xclang -packed-fp32-ops
 //          -I exact_attention_97_amd/csrc ubench.hip -o ubench
 // (exact_attention_97_amd/build_lib.py builds it as microbench/ubench).
-// Run: ./ubench   prints one markdown table per section.
+// Run: ./ubench   prints one markdown table per section;
+//      ./ubench atomic   only the atomic section (for counter runs).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -213,6 +214,33 @@ __global__ __launch_bounds__(1024) void k_lds(float* __restrict__ out, long long
   }
 }
 
+// ---- fp32 atomic adds -----------------------------------------------------
+// No-return buffer atomic adds of 1.0 into an array of 8 regions of 64 K
+// floats (2 MiB): workgroup b adds into region b % 8 (pattern 0) or
+// (b / 8) % 8 (pattern 1), 256 adds per lane at addresses spread over the
+// region.  With workgroups dispatched to the eight XCDs in turn, pattern 0
+// keeps each region's adds on one XCD (its L2) and pattern 1 sends every
+// region's adds from all of them.  SC1 sets the instruction's sc1 bit (the
+// device-scope form).  Every workgroup records the XCD it ran on
+// (HW_REG_XCC_ID), so the host checks the dispatch order and the sums.
+constexpr int kAtomRegion = 65536, kAtomBlocks = 4096, kAtomIters = 256;
+template <int SC1>
+__global__ __launch_bounds__(256) void k_atomic(float* __restrict__ acc, int* __restrict__ xcc, int pattern) {
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int region = pattern == 0 ? (b & 7) : ((b >> 3) & 7);
+  if (t == 0) {
+    int id;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(id));
+    xcc[b] = id & 0xffff;
+  }
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(acc + (size_t)region * kAtomRegion, (short)0, kAtomRegion * 4, 0x00020000);
+  for (int it = 0; it < kAtomIters; ++it) {
+    const int i = (t + it * 256 + b * 97) & (kAtomRegion - 1);
+    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(1.0f, rs, i * 4, 0, SC1 ? 16 : 0);
+  }
+}
+
 // ---- host ------------------------------------------------------------------
 struct Bufs {
   float* in;
@@ -301,14 +329,64 @@ static void lds_row(const Bufs& b, const char* name, int waves) {
   printf("| %s | %d | %.1f |\n", name, waves, bytes / cyc);
 }
 
+template <int SC1>
+static void atomic_row(float* acc, int* xcc, const char* name, int pattern) {
+  const size_t n = (size_t)8 * kAtomRegion;
+  UB_CHECK(hipMemset(acc, 0, n * sizeof(float)));
+  UB_CHECK(hipDeviceSynchronize());
+  hipEvent_t e0, e1;
+  UB_CHECK(hipEventCreate(&e0));
+  UB_CHECK(hipEventCreate(&e1));
+  UB_CHECK(hipEventRecord(e0, 0));
+  hipLaunchKernelGGL((k_atomic<SC1>), dim3(kAtomBlocks), dim3(256), 0, 0, acc, xcc, pattern);
+  UB_CHECK(hipEventRecord(e1, 0));
+  UB_CHECK(hipEventSynchronize(e1));
+  UB_CHECK(hipGetLastError());
+  float ms = 0.f;
+  UB_CHECK(hipEventElapsedTime(&ms, e0, e1));
+  UB_CHECK(hipEventDestroy(e0));
+  UB_CHECK(hipEventDestroy(e1));
+  static float h[8 * kAtomRegion];
+  static int x[kAtomBlocks];
+  UB_CHECK(hipMemcpy(h, acc, n * sizeof(float), hipMemcpyDeviceToHost));
+  UB_CHECK(hipMemcpy(x, xcc, sizeof(x), hipMemcpyDeviceToHost));
+  double sum = 0;
+  for (size_t i = 0; i < n; ++i) sum += h[i];
+  const double adds = (double)kAtomBlocks * 256 * kAtomIters;
+  int rr = 0;
+  for (int i = 0; i < kAtomBlocks; ++i) rr += x[i] == (i & 7);
+  printf("| %s | %s | %.3f | %.1f | %s | %d of %d |\n", name,
+         pattern == 0 ? "each region from one XCD" : "each region from all XCDs", ms, adds / (ms * 1e-3) / 1e9,
+         sum == adds ? "exact" : "LOST", rr, kAtomBlocks);
+}
+
+static void atomic_section() {
+  float* acc;
+  int* xcc;
+  UB_CHECK(hipMalloc(&acc, (size_t)8 * kAtomRegion * sizeof(float)));
+  UB_CHECK(hipMalloc(&xcc, kAtomBlocks * sizeof(int)));
+  printf("\n## fp32 atomic adds (no return, 2 MiB target)\n\n");
+  printf("| instruction | pattern | ms | G adds/s | sum | workgroups on XCD (id mod 8) |\n|---|---|---|---|---|---|\n");
+  for (int p = 0; p < 2; ++p) {
+    atomic_row<0>(acc, xcc, "buffer_atomic_add_f32", p);
+    atomic_row<1>(acc, xcc, "buffer_atomic_add_f32 sc1", p);
+  }
+  UB_CHECK(hipFree(acc));
+  UB_CHECK(hipFree(xcc));
+}
+
 }  // namespace ub
 
-int main() {
+int main(int argc, char** argv) {
   using namespace ub;
   hipDeviceProp_t prop;
   UB_CHECK(hipGetDeviceProperties(&prop, 0));
   printf("device: %s (%s), %d CUs, max clock %.0f MHz\n\n", prop.name, prop.gcnArchName, prop.multiProcessorCount,
          prop.clockRate / 1000.0);
+  if (argc > 1 && argv[1][0] == 'a') {  // "atomic": only the atomic section (for counter runs)
+    atomic_section();
+    return 0;
+  }
   Bufs b;
   UB_CHECK(hipMalloc(&b.in, 64 * sizeof(float)));
   UB_CHECK(hipMalloc(&b.out, kBlocks * 1024 * sizeof(float)));
@@ -356,6 +434,8 @@ int main() {
   lds_row<2>(b, "ds_read_b64_tr_b16, swizzled rows", 4);
   lds_row<2>(b, "ds_read_b64_tr_b16, swizzled rows", 8);
   lds_row<2>(b, "ds_read_b64_tr_b16, swizzled rows", 16);
+
+  atomic_section();
 
   UB_CHECK(hipFree(b.in));
   UB_CHECK(hipFree(b.out));
