@@ -207,14 +207,16 @@ struct DqWavePipe {
   }
 };
 
-template <class Cfg, int OCC, bool PIPE>
+template <class Cfg, int OCC, bool PIPE, int TW = 1>
 __global__ __launch_bounds__(64 * Cfg::NW, OCC) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ nlse2v, const float* __restrict__ delta,
     uint16_t* __restrict__ dQ, int BH, int S, float scale, float C, int nqt, int causal) {
   using W = typename std::conditional<PIPE, DqWavePipe<Cfg>, DqWave<Cfg>>::type;
   constexpr int D = Cfg::D, BC = Cfg::BC, BR = Cfg::BR, NKS = Cfg::NKS, NDB = Cfg::NDB;
-  constexpr int TILE = Cfg::TILE_BYTES / 2;
+  // LDS tiles of TW steps of BC keys (one load issue and one barrier per TW steps)
+  using CfgT = FwdCfg<D, BC * TW, Cfg::NW, 2>;
+  constexpr int TILE = CfgT::TILE_BYTES / 2;
 
   // one __shared__ array per buffer; the loop below is unrolled by two, so
   // every buffer a tile reads or loads into is a compile-time constant (LDS
@@ -284,46 +286,75 @@ __global__ __launch_bounds__(64 * Cfg::NW, OCC) void bwd_dq_kernel(
 
   FwdOffsets<Cfg> of;
   of.init(wave, lane);
+  const int ntt = (kend + BC * TW - 1) / (BC * TW);  // LDS tiles
 
   f32x16 dqacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16{};
 
-  dma_tile<Cfg>(Kh, 0, S, Kb0, wave_u, of.dma);
-  dma_tile<Cfg>(Vh, 0, S, Vb0, wave_u, of.dma);
+  // a TW-step tile is loaded as TW tiles of BC keys (the swizzle repeats
+  // every 16 rows, so they stack); a part starting at or past S is not
+  // loaded (its step is never taken, and dma_tile needs k0 < S)
+  auto load_tile = [&](int k0, uint16_t* kd, uint16_t* vd) {
+#pragma unroll
+    for (int h = 0; h < TW; ++h) {
+      if (h == 0 || k0 + h * BC < S) {
+        dma_tile<Cfg>(Kh, k0 + h * BC, S, kd + h * BC * D, wave_u, of.dma);
+        dma_tile<Cfg>(Vh, k0 + h * BC, S, vd + h * BC * D, wave_u, of.dma);
+      }
+    }
+  };
+  load_tile(0, Kb0, Vb0);
   wait_vm_lds<0>();
   barrier_keep_loads();
 
   // P = kt & 1: tile kt sits in buffer P, tile kt + 1 goes to the other one
   // (last read in the previous iteration)
-  auto iteration = [&](int kt, auto P) {
+  auto iteration = [&](int tt, auto P) {
     constexpr int par = decltype(P)::value;
     const uint16_t* kc = par ? Kb1 : Kb0;
     const uint16_t* vc = par ? Vb1 : Vb0;
-    if (kt + 1 < nkt) {
-      dma_tile<Cfg>(Kh, (kt + 1) * BC, S, par ? Kb0 : Kb1, wave_u, of.dma);
-      dma_tile<Cfg>(Vh, (kt + 1) * BC, S, par ? Vb0 : Vb1, wave_u, of.dma);
-    }
+    if (tt + 1 < ntt) load_tile((tt + 1) * BC * TW, par ? Kb0 : Kb1, par ? Vb0 : Vb1);
     __builtin_amdgcn_sched_barrier(0);
-    // The offsets pass through an empty asm at each tile: the compiler then
+    // The offsets pass through an empty asm at each step: the compiler then
     // cannot precompute both buffers' addresses and hold them over the loop
     // (it adds the constant buffer base as the instruction's immediate).
+    auto fresh_offsets = [&]() {
 #pragma unroll
-    for (int ks = 0; ks < Cfg::NKS; ++ks) asm volatile("" : "+v"(of.kfrag[ks]));
+      for (int ks = 0; ks < Cfg::NKS; ++ks) asm volatile("" : "+v"(of.kfrag[ks]));
 #pragma unroll
-    for (int db = 0; db < Cfg::NDB; ++db) asm volatile("" : "+v"(of.vfrag[db][0]), "+v"(of.vfrag[db][1]));
-    if (kt < nkt_w) {
-      if (kt < nfull)
-        W::template step<false>(kc, vc, of, qreg, doreg, dqacc, C, nlse2, dlt, kt * BC, lim, hh);
-      else
-        W::template step<true>(kc, vc, of, qreg, doreg, dqacc, C, nlse2, dlt, kt * BC, lim, hh);
+      for (int db = 0; db < Cfg::NDB; ++db) asm volatile("" : "+v"(of.vfrag[db][0]), "+v"(of.vfrag[db][1]));
+    };
+    if constexpr (TW == 1) {
+      // (kept apart from the TW > 1 loop: a one-trip loop around the step
+      // changed the register allocation of these kernels)
+      fresh_offsets();
+      if (tt < nkt_w) {
+        if (tt < nfull)
+          W::template step<false>(kc, vc, of, qreg, doreg, dqacc, C, nlse2, dlt, tt * BC, lim, hh);
+        else
+          W::template step<true>(kc, vc, of, qreg, doreg, dqacc, C, nlse2, dlt, tt * BC, lim, hh);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < TW; ++h) {
+        fresh_offsets();
+        const int kt = tt * TW + h;  // BC-key step
+        const int eo = h * BC * D;   // its rows in the LDS tile
+        if (kt < nkt_w) {
+          if (kt < nfull)
+            W::template step<false>(kc + eo, vc + eo, of, qreg, doreg, dqacc, C, nlse2, dlt, kt * BC, lim, hh);
+          else
+            W::template step<true>(kc + eo, vc + eo, of, qreg, doreg, dqacc, C, nlse2, dlt, kt * BC, lim, hh);
+        }
+      }
     }
     wait_vm_lds<0>();
     barrier_keep_loads();
   };
-  for (int kt = 0; kt < nkt; kt += 2) {
-    iteration(kt, std::integral_constant<int, 0>{});
-    if (kt + 1 < nkt) iteration(kt + 1, std::integral_constant<int, 1>{});
+  for (int tt = 0; tt < ntt; tt += 2) {
+    iteration(tt, std::integral_constant<int, 0>{});
+    if (tt + 1 < ntt) iteration(tt + 1, std::integral_constant<int, 1>{});
   }
 
   // dQ = scale * acc: lane holds column qrow, rows d = 32 db + 8 g + 4 h + 0..3
@@ -341,12 +372,12 @@ __global__ __launch_bounds__(64 * Cfg::NW, OCC) void bwd_dq_kernel(
   }
 }
 
-template <class Cfg, int OCC, bool PIPE = false>
+template <class Cfg, int OCC, bool PIPE = false, int TW = 1>
 static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
   const int nqt = (a.S + Cfg::BR - 1) / Cfg::BR;
   const int BH = a.B * a.H;
   prof_begin(KID_BWD_DQ, st);
-  hipLaunchKernelGGL((bwd_dq_kernel<Cfg, OCC, PIPE>), dim3(nqt * BH), dim3(64 * Cfg::NW), 0, st, (const uint16_t*)a.Q,
+  hipLaunchKernelGGL((bwd_dq_kernel<Cfg, OCC, PIPE, TW>), dim3(nqt * BH), dim3(64 * Cfg::NW), 0, st, (const uint16_t*)a.Q,
                      (const uint16_t*)a.K, (const uint16_t*)a.V, (const uint16_t*)a.dO, a.nlse2, a.delta,
                      (uint16_t*)a.dQ, BH, a.S, a.scale, a.scale * kLog2e, nqt, a.causal);
   prof_end(KID_BWD_DQ, st);
@@ -354,9 +385,11 @@ static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
 }
 
 // D = 128: the cooperative big tile, one workgroup of eight wavefronts (256
-// queries) per CU sharing each K / V tile in LDS, 64-key tiles in the
+// queries) per CU sharing each K / V tile in LDS, 64-key steps in the
 // pipelined step (measured 3-4 % faster than four wavefronts at S = 4096 and
-// 8192, 2.5 % at 32768).  Variant 1 (attn_set_variant("bwd_dq", 1) or
+// 8192, 2.5 % at 32768), two steps per LDS tile (128 KiB of LDS: one load
+// issue and one barrier per 128 keys; 10 % faster non-causal at S = 8192,
+// 12 % at 4096, 1-3 % causal).  Variant 1 (attn_set_variant("bwd_dq", 1) or
 // ATTN97_DQ_VARIANT=1): two workgroups of four wavefronts per CU.
 static int dq_variant() { return kernel_variant(VAR_DQ); }
 
@@ -365,7 +398,7 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
     case 64: return launch_dq_t<FwdCfg<64, 64, 4, 2>, 2>(a, st);  // two workgroups (eight wavefronts) per CU
     case 128:
       if (dq_variant() == 1) return launch_dq_t<FwdCfg<128, 64, 4, 2>, 2, true>(a, st);
-      return launch_dq_t<FwdCfg<128, 64, 8, 2>, 1, true>(a, st);
+      return launch_dq_t<FwdCfg<128, 64, 8, 2>, 1, true, 2>(a, st);
     case 256: return launch_dq_t<FwdCfg<256, 32, 4, 2>, 1>(a, st);  // 32-key tiles, one workgroup per CU
     default: return hipErrorInvalidValue;
   }

@@ -1,8 +1,9 @@
 // attn_fwd.hip - forward pass of exact attention on gfx950.
 //
 // One workgroup owns a tile of query rows of one (batch, head): eight
-// wavefronts and 256 rows at D = 128 (all eight share each K / V tile in
-// LDS), four and 128 at D = 64 and 256 and in the split-KV kernel.  Each
+// wavefronts and 256 rows at D = 128 for long sequences (all eight share
+// each K / V tile in LDS), four and 128 otherwise, at D = 64 and 256 and in
+// the split-KV kernel.  Each
 // wavefront owns 32 of those rows and walks the key/value sequence one tile
 // of BC keys at a time:
 //
@@ -38,7 +39,9 @@
 // Pipeline: while the softmax of tile j runs on the VALU, the MFMA unit
 // computes the scores of tile j+1; then P_j V_j.  K tiles are loaded two
 // tiles ahead and V tiles one ahead, each into a double buffer, so one
-// barrier per tile suffices.  One-query-row calls of the split-KV path
+// barrier per tile suffices; the eight-wavefront kernel puts two such
+// steps in each LDS tile (one load issue and one barrier per 128 keys).
+// One-query-row calls of the split-KV path
 // (decoding) run splitkv_decode_kernel instead, which has no matrix tiles.
 #include <stdlib.h>
 
@@ -275,7 +278,7 @@ struct SplitKv {
 // order, tile counts, the last visible key), and one instantiation for both
 // settings keeps the compiler from restructuring the non-causal loop into a
 // version that spills registers.
-template <class Cfg, int EXPMODE, bool SPLITKV = false>
+template <class Cfg, int EXPMODE, bool SPLITKV = false, int TW = 1>
 __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 : 2) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int S, float C, uint32_t qsign, float tau, int nqt,
@@ -283,7 +286,10 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
   using W = FwdWave<Cfg, EXPMODE>;
   constexpr int D = Cfg::D, BC = Cfg::BC, BR = Cfg::BR, NKB = Cfg::NKB, NKS = Cfg::NKS, NDB = Cfg::NDB;
   constexpr int NBUF = Cfg::NBUF, DPW = Cfg::DMA_PER_WAVE;
-  constexpr int TILE = Cfg::TILE_BYTES / 2;  // elements
+  // LDS tiles of TW steps of BC keys (TW > 1: one load issue and one
+  // barrier per TW steps)
+  constexpr int TILE = Cfg::TILE_BYTES / 2 * TW;  // elements
+  static_assert(TW == 1 || (NBUF == 2 && !SPLITKV), "multi-step tiles: two buffers, no split-KV");
 
   // One __shared__ array per buffer: with two buffers every buffer choice
   // below is a compile-time constant (the loop is unrolled by two), and the
@@ -382,6 +388,68 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
   FwdOffsets<Cfg> of;
   of.init(wave, lane);
 
+  if constexpr (TW > 1) {
+    // Tiles of TW * BC keys.  V tile t holds keys TW BC t .. and K tile t
+    // is offset by one step (keys TW BC t + BC ..): iteration t takes steps
+    // TW t .. TW t + TW - 1, whose scores were computed one step earlier and
+    // whose next-step scores come from K tile t, so each iteration reads one
+    // K and one V tile and two buffers per kind suffice.  A tile is loaded
+    // as TW tiles of BC keys (the swizzle repeats every 16 rows, so they
+    // stack); a part starting at or past S is not loaded (its keys belong to
+    // no step that is taken).
+    constexpr int TK = TW * BC;
+    const int ntt = (kend + TK - 1) / TK;
+    auto load_parts = [&](const uint16_t* src, int k0, uint16_t* dst) {
+#pragma unroll
+      for (int h = 0; h < TW; ++h)
+        if (k0 + h * BC < S) dma_tile<Cfg>(src, k0 + h * BC, S, dst + h * BC * D, wave_u, of.dma);
+    };
+    dma_tile<Cfg>(Kh, 0, S, Kb1, wave_u, of.dma);  // keys 0 .. BC-1: the first step's scores
+    load_parts(Kh, BC, Kb0);
+    load_parts(Vh, 0, Vb0);
+    wait_vm_lds<0>();
+    __syncthreads();
+    f32x16 sa[NKB], sb[NKB];
+    float ma = kNegInf, mb = kNegInf;
+    W::scores(Kb1, of, qreg, sa);
+    if constexpr (W::kMaxAhead) ma = W::template tile_max<false>(sa, 0, 0, 0);
+    // iteration 0 reloads Kb1: every wave's reads of it must be complete first
+    wait_vm_lds<63>();
+    barrier_keep_loads();
+    auto iteration = [&](int t, auto P) {
+      constexpr int par = decltype(P)::value;
+      const uint16_t* kc = par ? Kb1 : Kb0;
+      const uint16_t* vc = par ? Vb1 : Vb0;
+      if (t + 1 < ntt) {
+        load_parts(Kh, TK * (t + 1) + BC, par ? Kb0 : Kb1);
+        load_parts(Vh, TK * (t + 1), par ? Vb0 : Vb1);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the load issue out of the compute schedule
+#pragma unroll
+      for (int h = 0; h < TW; ++h) {
+        const int kt = TW * t + h;
+        f32x16(&scur)[NKB] = (h & 1) ? sb : sa;
+        f32x16(&snext)[NKB] = (h & 1) ? sa : sb;
+        float& mcur = (h & 1) ? mb : ma;
+        float& mnext = (h & 1) ? ma : mb;
+        if (kt < nkt_w) {
+          if (kt < nfull)
+            W::template step<false>(kc + h * BC * D, vc + h * BC * D, of, qreg, scur, snext, oacc, m_run, l_part,
+                                    kt * BC, lim, hh, C, tau, mcur, mnext);
+          else
+            W::template step<true>(kc + h * BC * D, vc + h * BC * D, of, qreg, scur, snext, oacc, m_run, l_part,
+                                   kt * BC, lim, hh, C, tau, mcur, mnext);
+        }
+      }
+      wait_vm_lds<0>();
+      barrier_keep_loads();
+    };
+    static_assert(TW % 2 == 0, "the score sets alternate per step");
+    for (int t = 0; t < ntt; t += 2) {
+      iteration(t, std::integral_constant<int, 0>{});
+      if (t + 1 < ntt) iteration(t + 1, std::integral_constant<int, 1>{});
+    }
+  } else {
   // Load schedule: iteration j issues K(j + NBUF) and V(j + NBUF - 1) into
   // the buffers freed by the barrier of iteration j-1, and needs K(j + 1)
   // (scores of the next tile) and V(j).  The prologue issues what iterations
@@ -451,6 +519,7 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
     iteration(kt, std::integral_constant<int, 0>{}, sa, sb, ma, mb);
     if (kt + 1 < nkt) iteration(kt + 1, std::integral_constant<int, 1>{}, sb, sa, mb, ma);
   }
+  }  // TW == 1
 
 // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l) ----------------------
   const float l_tot = l_part + wave_swap_halves(l_part);
@@ -659,13 +728,13 @@ __global__ void exp2_eval_kernel(const float* __restrict__ x, float* __restrict_
 // ---------------------------------------------------------------------------
 // host-side launchers
 // ---------------------------------------------------------------------------
-template <class Cfg, int EXPMODE>
+template <class Cfg, int EXPMODE, int TW = 1>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   const int nqt = (a.S + Cfg::BR - 1) / Cfg::BR;
   const int BH = a.B * a.H;
   dim3 grid(nqt * BH), block(64 * Cfg::NW);
   prof_begin(KID_FWD, st);
-  hipLaunchKernelGGL((fwd_kernel<Cfg, EXPMODE>), grid, block, 0, st, (const uint16_t*)a.Q, (const uint16_t*)a.K,
+  hipLaunchKernelGGL((fwd_kernel<Cfg, EXPMODE, false, TW>), grid, block, 0, st, (const uint16_t*)a.Q, (const uint16_t*)a.K,
                      (const uint16_t*)a.V, (uint16_t*)a.O, a.LSE, BH, a.S, a.C, a.qsign, a.tau, nqt, a.causal,
                      SplitKv{a.S, 0, nullptr, nullptr});
   prof_end(KID_FWD, st);
@@ -673,34 +742,55 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
 }
 
 // a.exp_mode is the kernel exp2 mode (kExpNative, kExpPoly or exp_mix(q)).
-template <class Cfg>
+template <class Cfg, int TW = 1>
 static hipError_t launch_fwd_e(const FwdArgs& a, hipStream_t st) {
   switch (a.exp_mode) {
-    case kExpPoly: return launch_fwd_t<Cfg, kExpPoly>(a, st);
-    case exp_mix(1): return launch_fwd_t<Cfg, exp_mix(1)>(a, st);
-    case exp_mix(2): return launch_fwd_t<Cfg, exp_mix(2)>(a, st);
-    case exp_mix(3): return launch_fwd_t<Cfg, exp_mix(3)>(a, st);
-    default: return launch_fwd_t<Cfg, kExpNative>(a, st);
+    case kExpPoly: return launch_fwd_t<Cfg, kExpPoly, TW>(a, st);
+    case exp_mix(1): return launch_fwd_t<Cfg, exp_mix(1), TW>(a, st);
+    case exp_mix(2): return launch_fwd_t<Cfg, exp_mix(2), TW>(a, st);
+    case exp_mix(3): return launch_fwd_t<Cfg, exp_mix(3), TW>(a, st);
+    default: return launch_fwd_t<Cfg, kExpNative, TW>(a, st);
   }
 }
 
-// The D = 128 tile by sequence length (measured on MI355X, B=2, H=16, with
-// the outlier inputs): from S = 8192 on the cooperative big tile, eight
-// wavefronts (256 queries) sharing each K / V tile in LDS (2-3 % faster at
-// S = 8192); below that four wavefronts (128 queries) per workgroup, whose
-// smaller workgroups balance the few query tiles per head better (4-6 %
-// faster at S = 2048, 0.5-2 % at 4096, 4 % at 5120 and 3 % at 7168; at 6144
-// 3 % slower non-causal and 2 % faster causal).  Variant 1
-// (attn_set_variant("fwd", 1) or ATTN97_FWD_VARIANT=1) takes the eight-
-// wavefront tile at every length, so that its ragged and short cases can be
-// tested.  Split-KV keeps four, which suits few query rows.
+// The D = 128 tile (measured on MI355X, B=2, H=16, outlier inputs, S from
+// 2048 to 8192 in steps of 1024).  The cooperative big tile, eight
+// wavefronts (256 queries) sharing each K / V tile in LDS with two 64-key
+// steps per LDS tile, is 3-3.5 % faster than four wavefronts (128 queries,
+// two workgroups per CU) when its workgroups fill whole rounds of the CUs
+// (S = 4096, 6144, 8192 at B*H = 32) and 1-8 % slower when the last round
+// is partial (S = 3072, 5120, 7168), where the smaller workgroups balance
+// better; at S = 2048 four wavefronts are 8 % faster causal.  So: eight
+// wavefronts from S = 4096 on when the 256-query workgroups are a multiple
+// of the CU count, else four.  Variant 1 (attn_set_variant("fwd", 1) or
+// ATTN97_FWD_VARIANT=1) takes the eight-wavefront tile at every length, so
+// that its ragged and short cases can be tested.  Split-KV keeps four,
+// which suits few query rows.
 static int fwd_variant() { return kernel_variant(VAR_FWD); }
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+  }
+  return cus[dev];
+}
+
+static bool fwd_big_tile(const FwdArgs& a) {
+  if (fwd_variant() == 1) return true;
+  const long wgs = (long)((a.S + 255) / 256) * a.B * a.H;
+  return a.S >= 4096 && wgs % device_cus() == 0;
+}
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   switch (a.D) {
     case 64: return launch_fwd_e<FwdDefault<64>::type>(a, st);
     case 128:
-      if (fwd_variant() == 1 || a.S >= 8192) return launch_fwd_e<FwdCfg<128, 64, 8, 2>>(a, st);
+      if (fwd_big_tile(a)) return launch_fwd_e<FwdCfg<128, 64, 8, 2>, 2>(a, st);
       return launch_fwd_e<FwdDefault<128>::type>(a, st);
     case 256: return launch_fwd_e<FwdDefault<256>::type>(a, st);
     default: return hipErrorInvalidValue;

@@ -36,7 +36,7 @@ struct FwdCfg {
 };
 
 // Issue this wave's share of one tile load (rows k0.. of a [S, D] bf16
-// matrix) into the swizzled LDS tile `dst`: lane l of load n fills physical
+// matrix, k0 < S) into the swizzled LDS tile `dst`: lane l of load n fills physical
 // chunk 64 * (wave * DMA_PER_WAVE + n) + l.  `loff[n]` is that chunk's
 // logical element offset inside the tile (row * D + 8 * chunk), fixed per
 // lane.  The buffer resource ends at row S, so in a ragged last tile the rows

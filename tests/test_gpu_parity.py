@@ -569,3 +569,36 @@ def test_kernel_variants_match_oracle(kernel, variant):
                 _assert_close("dV", _np(dv), rdv)
     finally:
         L.set_variant(kernel, -1)
+
+
+# ----------------------------------------------------------------------------
+# LDS tiles of two 64-key steps (the eight-wavefront forward, forced at every
+# length by fwd variant 1, and the default D = 128 dQ kernel): lengths whose
+# last tile ends inside its first step, at its boundary, or inside the second
+# step (whose load is skipped when it starts at or past S); the forward's K
+# tiles are offset by one step, so its boundaries fall 64 keys later
+# ----------------------------------------------------------------------------
+
+TWO_STEP_LENGTHS = (1, 33, 64, 65, 127, 128, 129, 191, 192, 193, 300, 320)
+
+
+@pytest.mark.parametrize("S", TWO_STEP_LENGTHS)
+def test_two_step_tiles_ragged(S):
+    print(f"[two-step tiles] S={S}", flush=True)
+    q, k, v, do = make_qkvdo(1, 2, S, 128, seed=300 + S)
+    scale = 1.0 / math.sqrt(128)
+    qg, kg, vg, dog = _gpu(q, k, v, do)
+    for causal in (False, True):
+        L.set_variant("fwd", 1)
+        try:
+            o, lse = L.attn_fwd(qg, kg, vg, scale=scale, causal=causal)
+        finally:
+            L.set_variant("fwd", -1)
+        ro, rl = oracle.attention_fwd(q, k, v, scale, causal)
+        _assert_close("O", _np(o), ro)
+        _assert_lse(_np(lse), rl)
+        dq, dk, dv = L.attn_bwd(qg, kg, vg, o, dog, lse, scale=scale, causal=causal, bwd_mode="split")
+        rdq, rdk, rdv = oracle.attention_bwd(q, k, v, do, scale, causal)
+        _assert_close("dQ", _np(dq), rdq)
+        _assert_close("dK", _np(dk), rdk)
+        _assert_close("dV", _np(dv), rdv)
