@@ -44,7 +44,9 @@ constexpr int kMaxWaves = 16;
 // ---- matrix core ----------------------------------------------------------
 // SHAPE 0: v_mfma_f32_32x32x16_bf16 (32768 flop), 1: v_mfma_f32_16x16x32_bf16
 // (16384 flop), 2: v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands
-// (131072 flop).  Four independent accumulator chains per wavefront.
+// (131072 flop), four independent accumulator chains per wavefront; 3 and 4:
+// v_mfma_f32_32x32x16_bf16 with one chain (each MFMA accumulates onto the
+// previous one's result) and with two chains.
 template <int SHAPE>
 __global__ __launch_bounds__(1024) void k_mfma(const float* __restrict__ in, float* __restrict__ out,
                                                long long* __restrict__ cyc, int iters) {
@@ -77,6 +79,16 @@ __global__ __launch_bounds__(1024) void k_mfma(const float* __restrict__ in, flo
         d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, d1, 0, 0, 0);
         d2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, d2, 0, 0, 0);
         d3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, d3, 0, 0, 0);
+      } else if constexpr (SHAPE == 3) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+      } else if constexpr (SHAPE == 4) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
       } else {
         c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c0, 0, 0, 0, 0, 0, 0);
         c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c1, 0, 0, 0, 0, 0, 0);
@@ -403,6 +415,8 @@ int main(int argc, char** argv) {
   mfma_row<1>(b, "v_mfma_f32_16x16x32_bf16", 16384.0, 2);
   mfma_row<2>(b, "v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3)", 131072.0, 1);
   mfma_row<2>(b, "v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3)", 131072.0, 2);
+  mfma_row<3>(b, "v_mfma_f32_32x32x16_bf16, one dependent chain", 32768.0, 1);
+  mfma_row<4>(b, "v_mfma_f32_32x32x16_bf16, two chains", 32768.0, 1);
 
   printf("\n## VALU issue (8 independent chains per wavefront)\n\n");
   printf("| operation | waves/SIMD | cycles per wavefront instruction (element for the polynomial) per SIMD |\n|---|---|---|\n");
