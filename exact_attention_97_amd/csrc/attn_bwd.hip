@@ -3,9 +3,9 @@
 // The forward pass stored only O and the row log-sum-exp, so the backward
 // pass recomputes the probabilities from them:
 //
-//   Delta_i = sum_d dO_id O_id                       (bwd_pre_kernel)
-//   P  = exp2(S * scale*log2e - LSE*log2e),  S = Q K^T   (-LSE log2e from
-//                                                       bwd_pre_kernel)
+//   Delta_i = sum_d dO_id O_id                       (bwd_pre_kernel; in the
+//                                                       split mode the dQ kernel)
+//   P  = exp2(S * scale*log2e - LSE*log2e),  S = Q K^T   (-LSE log2e likewise)
 //   dV += P^T dO,   dP = dO V^T,   dS = P * (dP - Delta)
 //   dK += dS^T Q,   dQ += dS K                       (bwd_main_kernel)
 //   dQ (bf16) = fp32 accumulator                     (dq_convert_kernel)
@@ -1234,14 +1234,15 @@ hipError_t launch_bwd_atomic(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Split mode: the dQ kernel forms Delta and -LSE log2e of its rows (it
+// holds their dO anyway) and writes them for the dK/dV kernel that follows,
+// so no separate preprocessing pass runs.
 hipError_t launch_bwd_split(const BwdArgs& a, hipStream_t st) {
   BwdArgs b = a;
-  b.dq32 = nullptr;  // Delta only
-  hipError_t e = launch_pre(b, st);
+  b.dq32 = nullptr;
+  hipError_t e = launch_bwd_dq(b, st);
   if (e != hipSuccess) return e;
-  e = launch_main<false>(b, st);
-  if (e != hipSuccess) return e;
-  return launch_bwd_dq(b, st);
+  return launch_main<false>(b, st);
 }
 
 }  // namespace attn97

@@ -9,6 +9,8 @@
 // and dV in one kernel (per key tile) and dQ here, per query tile, walking
 // the key sequence like the forward pass and recomputing what dQ needs:
 //
+//   Delta = rowsum(dO O), -LSE log2e   (per query row, also written out for
+//                                       the dK/dV kernel, launched after this one)
 //   S^T  = K Q^T           dP^T = V dO^T           (bf16 MFMA)
 //   P    = exp2(S c - LSE log2e)                   (per lane: one query)
 //   dS   = P (dP - Delta)
@@ -210,8 +212,9 @@ struct DqWavePipe {
 template <class Cfg, int OCC, bool PIPE, int TW = 1>
 __global__ __launch_bounds__(64 * Cfg::NW, OCC) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ nlse2v, const float* __restrict__ delta,
-    uint16_t* __restrict__ dQ, int BH, int S, float scale, float C, int nqt, int causal) {
+    const uint16_t* __restrict__ dO, const uint16_t* __restrict__ O, const float* __restrict__ LSE,
+    float* __restrict__ nlse2v, float* __restrict__ delta, uint16_t* __restrict__ dQ, int BH, int S, float scale,
+    float C, int nqt, int causal) {
   using W = typename std::conditional<PIPE, DqWavePipe<Cfg>, DqWave<Cfg>>::type;
   constexpr int D = Cfg::D, BC = Cfg::BC, BR = Cfg::BR, NKS = Cfg::NKS, NDB = Cfg::NDB;
   // LDS tiles of TW steps of BC keys (one load issue and one barrier per TW steps)
@@ -252,13 +255,23 @@ __global__ __launch_bounds__(64 * Cfg::NW, OCC) void bwd_dq_kernel(
 
   // Q^T and dO^T operands in registers: lane holds row qrow, d = 16 ks + 8 h ..
   bf16x8 qreg[NKS], doreg[NKS];
+  // Delta of this lane's row, sum_d dO_d O_d: each lane of the pair (l, l+32)
+  // takes the half of the row it holds as the dO operand
+  float dlt = 0.0f;
   {
     const u32x4* qs = reinterpret_cast<const u32x4*>(Q + base + (size_t)qc * D);
     const u32x4* ds = reinterpret_cast<const u32x4*>(dO + base + (size_t)qc * D);
+    const u32x4* os = reinterpret_cast<const u32x4*>(O + base + (size_t)qc * D);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
+      const u32x4 g = ds[2 * ks + hh], o = os[2 * ks + hh];
       qreg[ks] = as_bf16x8(qs[2 * ks + hh]);
-      doreg[ks] = as_bf16x8(ds[2 * ks + hh]);
+      doreg[ks] = as_bf16x8(g);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        dlt = __builtin_fmaf(__uint_as_float(o[m] << 16), __uint_as_float(g[m] << 16), dlt);
+        dlt = __builtin_fmaf(__uint_as_float(o[m] & 0xffff0000u), __uint_as_float(g[m] & 0xffff0000u), dlt);
+      }
     }
     // At D = 256 the kernel needs more than the 256 arch VGPRs.  Q and dO are
     // read only as MFMA operands, which gfx950 takes from AGPRs, so their 128
@@ -274,8 +287,13 @@ __global__ __launch_bounds__(64 * Cfg::NW, OCC) void bwd_dq_kernel(
       }
     }
   }
-  const float nlse2 = nlse2v[(size_t)bh * S + qc];  // -LSE log2(e)
-  const float dlt = delta[(size_t)bh * S + qc];
+  dlt += wave_swap_halves(dlt);
+  const float nlse2 = -LSE[(size_t)bh * S + qc] * kLog2e;  // -LSE log2(e)
+  // the dK/dV kernel, launched after this one, reads both per row
+  if (qrow < S && hh == 0) {
+    delta[(size_t)bh * S + qrow] = dlt;
+    nlse2v[(size_t)bh * S + qrow] = nlse2;
+  }
 
   const int kend = causal ? min(S, q0 + BR) : S;
   const int nkt = (kend + BC - 1) / BC;
@@ -378,8 +396,8 @@ static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   prof_begin(KID_BWD_DQ, st);
   hipLaunchKernelGGL((bwd_dq_kernel<Cfg, OCC, PIPE, TW>), dim3(nqt * BH), dim3(64 * Cfg::NW), 0, st, (const uint16_t*)a.Q,
-                     (const uint16_t*)a.K, (const uint16_t*)a.V, (const uint16_t*)a.dO, a.nlse2, a.delta,
-                     (uint16_t*)a.dQ, BH, a.S, a.scale, a.scale * kLog2e, nqt, a.causal);
+                     (const uint16_t*)a.K, (const uint16_t*)a.V, (const uint16_t*)a.dO, (const uint16_t*)a.O,
+                     a.LSE, a.nlse2, a.delta, (uint16_t*)a.dQ, BH, a.S, a.scale, a.scale * kLog2e, nqt, a.causal);
   prof_end(KID_BWD_DQ, st);
   return hipGetLastError();
 }
