@@ -32,81 +32,6 @@ namespace attn97 {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
-template <class Cfg>
-struct DqWave {
-  static constexpr int D = Cfg::D, NKB = Cfg::NKB, NKS = Cfg::NKS, NDB = Cfg::NDB, CPR = Cfg::CPR;
-
-  // One key tile.  MASK: entries with key > lim get P = 0.
-  template <bool MASK>
-  __device__ __forceinline__ static void step(const uint16_t* kt, const uint16_t* vt, const FwdOffsets<Cfg>& of,
-                                              const bf16x8 (&qreg)[NKS], const bf16x8 (&doreg)[NKS],
-                                              f32x16 (&dqacc)[NDB], float C, float nlse2, float dlt, int k0,
-                                              int lim, int hh) {
-    f32x16 sacc[NKB], dpacc[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      sacc[kb] = f32x16{};
-      dpacc[kb] = f32x16{};
-    }
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const int o = of.kfrag[ks] + 32 * kb * CPR * 8;
-        sacc[kb] = mfma32(lds_frag(kt + o), qreg[ks], sacc[kb]);
-        dpacc[kb] = mfma32(lds_frag(vt + o), doreg[ks], dpacc[kb]);
-      }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i = 0; i < 2 * NKS * NKB - 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-
-    bf16x8 dsb[2 * NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        float ds[8];
-#pragma unroll
-        for (int e8 = 0; e8 < 8; ++e8) {
-          const int r = 8 * half + e8;
-          float p = exp2_native(__builtin_fmaf(sacc[kb][r], C, nlse2));
-          if (MASK) {
-            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key > lim) p = 0.0f;
-          }
-          ds[e8] = p * (dpacc[kb][r] - dlt);
-        }
-        dsb[2 * kb + half] = pack_probs(ds);
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < 2 * NKB; ++t) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int o = 16 * t * CPR * 8;
-        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(kt + of.vfrag[db][0] + o));
-        const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(kt + of.vfrag[db][1] + o));
-        const s16x8 v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
-        dqacc[db] = mfma32(__builtin_bit_cast(bf16x8, v), dsb[t], dqacc[db]);
-      }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-#pragma unroll
-    for (int i = 0; i < 2 * NKB * NDB - 2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
-  }
-};
-
 // Two 32-key blocks per tile, software-pipelined like the dK/dV tile:
 //   A: S^T, dP^T of block 0
 //   B: S^T, dP^T of block 1   | softmax of block 0
@@ -118,6 +43,10 @@ template <class Cfg>
 struct DqWavePipe {
   static constexpr int D = Cfg::D, NKS = Cfg::NKS, NDB = Cfg::NDB, CPR = Cfg::CPR;
   static_assert(Cfg::NKB == 2, "two 32-key blocks per tile");
+  // softmax elements (16 per block) per chunk of phase B (one reduction step
+  // of the S and dP products) and of phase C (one dQ MFMA)
+  static constexpr int EB = 16 / NKS, EC = 16 / (2 * NDB);
+  static_assert(EB * NKS == 16 && EC * 2 * NDB == 16, "elements spread evenly over the chunks");
 
   template <bool MASK>
   __device__ __forceinline__ static void elem(const f32x16& sacc, const f32x16& dpacc, int r, float C, float nlse2,
@@ -167,12 +96,20 @@ struct DqWavePipe {
       ka[0] = kfrag(1, 0); va[0] = vfrag(1, 0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
+      for (int ks = 0; ks < NKS; ++ks) {  // EB of block 0's 16 elements per reduction step
         if (ks + 1 < NKS) { ka[ks + 1] = kfrag(1, ks + 1); va[ks + 1] = vfrag(1, ks + 1); }
         s1 = mfma32(ka[ks], qreg[ks], s1);
-        elem<MASK>(s0, dp0, 2 * ks, C, nlse2, dlt, keyof(0, 2 * ks), lim, ds[2 * ks]);
+#pragma unroll
+        for (int e = 0; e < (EB + 1) / 2; ++e) {
+          const int r = EB * ks + e;
+          elem<MASK>(s0, dp0, r, C, nlse2, dlt, keyof(0, r), lim, ds[r]);
+        }
         dp1 = mfma32(va[ks], doreg[ks], dp1);
-        elem<MASK>(s0, dp0, 2 * ks + 1, C, nlse2, dlt, keyof(0, 2 * ks + 1), lim, ds[2 * ks + 1]);
+#pragma unroll
+        for (int e = (EB + 1) / 2; e < EB; ++e) {
+          const int r = EB * ks + e;
+          elem<MASK>(s0, dp0, r, C, nlse2, dlt, keyof(0, r), lim, ds[r]);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       dsb0[0] = pack_probs(*reinterpret_cast<float(*)[8]>(&ds[0]));
@@ -187,8 +124,11 @@ struct DqWavePipe {
         const int t = i / NDB, db = i % NDB;
         if (i + 1 < 2 * NDB) ta[i + 1] = ktr((i + 1) / NDB, (i + 1) % NDB);
         dqacc[db] = mfma32(ta[i], t == 0 ? dsb0[0] : dsb0[1], dqacc[db]);
-        elem<MASK>(s1, dp1, 2 * i, C, nlse2, dlt, keyof(1, 2 * i), lim, ds[2 * i]);
-        elem<MASK>(s1, dp1, 2 * i + 1, C, nlse2, dlt, keyof(1, 2 * i + 1), lim, ds[2 * i + 1]);
+#pragma unroll
+        for (int e = 0; e < EC; ++e) {  // EC of block 1's 16 elements per dQ MFMA
+          const int r = EC * i + e;
+          elem<MASK>(s1, dp1, r, C, nlse2, dlt, keyof(1, r), lim, ds[r]);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       dsb1[0] = pack_probs(*reinterpret_cast<float(*)[8]>(&ds[0]));
@@ -209,13 +149,13 @@ struct DqWavePipe {
   }
 };
 
-template <class Cfg, int OCC, bool PIPE, int TW = 1>
+template <class Cfg, int OCC, int TW = 1>
 __global__ __launch_bounds__(64 * Cfg::NW, OCC) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const uint16_t* __restrict__ O, const float* __restrict__ LSE,
     float* __restrict__ nlse2v, float* __restrict__ delta, uint16_t* __restrict__ dQ, int BH, int S, float scale,
     float C, int nqt, int causal) {
-  using W = typename std::conditional<PIPE, DqWavePipe<Cfg>, DqWave<Cfg>>::type;
+  using W = DqWavePipe<Cfg>;
   constexpr int D = Cfg::D, BC = Cfg::BC, BR = Cfg::BR, NKS = Cfg::NKS, NDB = Cfg::NDB;
   // LDS tiles of TW steps of BC keys (one load issue and one barrier per TW steps)
   using CfgT = FwdCfg<D, BC * TW, Cfg::NW, 2>;
@@ -390,18 +330,24 @@ __global__ __launch_bounds__(64 * Cfg::NW, OCC) void bwd_dq_kernel(
   }
 }
 
-template <class Cfg, int OCC, bool PIPE = false, int TW = 1>
+template <class Cfg, int OCC, int TW = 1>
 static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
   const int nqt = (a.S + Cfg::BR - 1) / Cfg::BR;
   const int BH = a.B * a.H;
   prof_begin(KID_BWD_DQ, st);
-  hipLaunchKernelGGL((bwd_dq_kernel<Cfg, OCC, PIPE, TW>), dim3(nqt * BH), dim3(64 * Cfg::NW), 0, st, (const uint16_t*)a.Q,
+  hipLaunchKernelGGL((bwd_dq_kernel<Cfg, OCC, TW>), dim3(nqt * BH), dim3(64 * Cfg::NW), 0, st, (const uint16_t*)a.Q,
                      (const uint16_t*)a.K, (const uint16_t*)a.V, (const uint16_t*)a.dO, (const uint16_t*)a.O,
                      a.LSE, a.nlse2, a.delta, (uint16_t*)a.dQ, BH, a.S, a.scale, a.scale * kLog2e, nqt, a.causal);
   prof_end(KID_BWD_DQ, st);
   return hipGetLastError();
 }
 
+// Every head dim takes the pipelined step over 64-key tiles.  Against a
+// plain step (a tile's S and dP products, then its softmax, then its dQ
+// product), measured in interleaved same-process runs at S = 8192, B=2,
+// H=16: D = 64 0.764 against 0.781 ms non-causal (two workgroups of four
+// wavefronts per CU), 0.388 against 0.395 causal; D = 256 3.208 against
+// 3.346 ms non-causal (32-key tiles before), 1.644 against 1.756 causal.
 // D = 128: the cooperative big tile, one workgroup of eight wavefronts (256
 // queries) per CU sharing each K / V tile in LDS, 64-key steps in the
 // pipelined step (measured 3-4 % faster than four wavefronts at S = 4096 and
@@ -415,9 +361,9 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
   switch (a.D) {
     case 64: return launch_dq_t<FwdCfg<64, 64, 4, 2>, 2>(a, st);  // two workgroups (eight wavefronts) per CU
     case 128:
-      if (dq_variant() == 1) return launch_dq_t<FwdCfg<128, 64, 4, 2>, 2, true>(a, st);
-      return launch_dq_t<FwdCfg<128, 64, 8, 2>, 1, true, 2>(a, st);
-    case 256: return launch_dq_t<FwdCfg<256, 32, 4, 2>, 1>(a, st);  // 32-key tiles, one workgroup per CU
+      if (dq_variant() == 1) return launch_dq_t<FwdCfg<128, 64, 4, 2>, 2>(a, st);
+      return launch_dq_t<FwdCfg<128, 64, 8, 2>, 1, 2>(a, st);
+    case 256: return launch_dq_t<FwdCfg<256, 64, 4, 2>, 1>(a, st);  // one workgroup per CU
     default: return hipErrorInvalidValue;
   }
 }
