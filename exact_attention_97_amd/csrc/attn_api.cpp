@@ -73,8 +73,8 @@ size_t g_prof_used = 0;
 size_t g_prof_open = (size_t)-1;
 
 // kernel variant overrides (-1: not set, use the environment)
-int g_variant[attn97::VAR_COUNT] = {-1, -1};
-int g_variant_env[attn97::VAR_COUNT] = {-1, -1};
+int g_variant[attn97::VAR_COUNT] = {-1, -1, -1};
+int g_variant_env[attn97::VAR_COUNT] = {-1, -1, -1};
 
 }  // namespace
 
@@ -84,7 +84,7 @@ int kernel_variant(int slot) {
   if (slot < 0 || slot >= VAR_COUNT) return 0;
   if (g_variant[slot] >= 0) return g_variant[slot];
   if (g_variant_env[slot] < 0) {
-    static const char* names[VAR_COUNT] = {"ATTN97_FWD_VARIANT", "ATTN97_DQ_VARIANT"};
+    static const char* names[VAR_COUNT] = {"ATTN97_FWD_VARIANT", "ATTN97_DQ_VARIANT", "ATTN97_DKDV_VARIANT"};
     const char* e = getenv(names[slot]);
     const int v = e ? atoi(e) : 0;
     g_variant_env[slot] = v < 0 ? 0 : v;
@@ -470,8 +470,8 @@ attn_status attn_exp2_eval(const float* x, float* y, long n, int mode, void* str
 
 attn_status attn_set_variant(const char* kernel, int variant) {
   if (!kernel) return ATTN_ERR_NULL;
-  static const char* names[attn97::VAR_COUNT] = {"fwd", "bwd_dq"};
-  static const int count[attn97::VAR_COUNT] = {2, 2};  // variants 0 .. count-1
+  static const char* names[attn97::VAR_COUNT] = {"fwd", "bwd_dq", "bwd_dkdv"};
+  static const int count[attn97::VAR_COUNT] = {2, 2, 2};  // variants 0 .. count-1
   for (int i = 0; i < attn97::VAR_COUNT; ++i) {
     if (strcmp(kernel, names[i]) != 0) continue;
     if (variant < -1 || variant >= count[i]) return ATTN_ERR_VALUE;

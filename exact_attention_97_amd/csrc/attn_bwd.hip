@@ -332,14 +332,18 @@ struct NoDq {
   __device__ __forceinline__ void step(int) {}
 };
 
-template <int D, class Cfg, bool CAUSAL, bool MASK, class IssuePart, class Dq = NoDq>
+// D = 128, or D = 256 with the dK / dV columns split between two workgroups
+// (NDO: the 32-column output blocks this workgroup forms, four either way).
+// At D = 256 the S and dP products take sixteen reduction steps, and phase B
+// carries one softmax element per step instead of two.
+template <int D, class Cfg, bool CAUSAL, bool MASK, int NDO, class IssuePart, class Dq = NoDq>
 __device__ __forceinline__ void dkdv_tile(const uint16_t* Qb, const uint16_t* dOb, const float* nl, const float* dl,
                                           const BwdOffsets<D, Cfg>& of, const bf16x8 (&kreg)[D / 16],
-                                          const bf16x8 (&vreg)[D / 16], f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32],
+                                          const bf16x8 (&vreg)[D / 16], f32x16 (&dk)[NDO], f32x16 (&dv)[NDO],
                                           int q0, int key, int S, float C, int hh, IssuePart&& issue_part,
                                           Dq&& dq = Dq{}) {
-  static_assert(Cfg::NQB == 2 && D / 16 == 8 && D / 32 == 4, "two 32-query blocks, D = 128");
-  constexpr int NKS = Cfg::NKS, NDB = Cfg::NDB, CPR = Cfg::CPR;
+  static_assert(Cfg::NQB == 2 && (D == 128 || D == 256) && NDO == 4, "two 32-query blocks, four output blocks");
+  constexpr int NKS = Cfg::NKS, NDB = NDO, CPR = Cfg::CPR;
   tile_marker<MASK>();
   int mlo = 0, mhi = 0;
   if constexpr (MASK) {  // register (qb, g, e) holds query q0 + 4 hh + 32 qb + 8 g + e
@@ -421,7 +425,32 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* Qb, const uint16_t* dO
   auto sm_ds = [&](const f32x16& ndacc, int r) { put(r, pp[r], -pp[r] * ndacc[r]); };
 
   // B: S, dP of block 1, each step with two elements of block 0's softmax
-  {
+  // (D = 256: one element per step, the same three stages)
+  if constexpr (NKS == 16) {
+    bf16x8 qa[NKS], da[NKS];
+    f32x4 l4[4];
+    qa[0] = qfrag(1, 0); da[0] = dofrag(1, 0);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) l4[g] = *reinterpret_cast<const f32x4*>(&nl[8 * g + 4 * hh]);
+    qa[1] = qfrag(1, 1); da[1] = dofrag(1, 1);
+    sm_arg(s0, l4, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (ks + 2 < NKS) { qa[ks + 2] = qfrag(1, ks + 2); da[ks + 2] = dofrag(1, ks + 2); }
+      if ((ks & 1) == 0) issue_part(NKS / 2 + ks / 2);
+      if (ks == NKS - 1) issue_part(NKS);
+      s1 = mfma32(qa[ks], kreg[ks], s1);
+      if (ks + 1 < NKS) sm_arg(s0, l4, ks + 1);
+      sm_exp(ks, 8 * (ks >> 2) + (ks & 3));
+      dp1 = mfma32(da[ks], vreg[ks], dp1);
+      if (ks >= 1) sm_ds(dp0, ks - 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    sm_ds(dp0, 15);
+    packed(pb0, dsb0);
+    dq.store(0, dsb0);
+  } else {
     bf16x8 qa[NKS], da[NKS];
     f32x4 l4[4];
     qa[0] = qfrag(1, 0); da[0] = dofrag(1, 0);
@@ -735,15 +764,21 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
 // finds them long complete.  Non-causal workgroups start their walk over
 // the query tiles at different tiles (rotated by key tile), so that the
 // workgroups of one head running together add into different rows.
-template <bool CAUSAL, bool RAGGED, bool DQ>
+//
+// D = 256 (DSPLIT = 2): the dK / dV columns are split between two workgroups
+// per key tile (128 each, as in bwd_main_kernel at that head dim); each holds
+// its keys' full K and V rows (the S and dP products contract over all 256
+// columns) and recomputes P and dS.
+template <int D, int DSPLIT, bool CAUSAL, bool RAGGED, bool DQ>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ nlse2, const float* __restrict__ delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ dq32, int BH, int S, float scale,
     float C) {
-  constexpr int D = 128;
+  static_assert((D == 128 && DSPLIT == 1) || (D == 256 && DSPLIT == 2 && !DQ), "D = 128, or D = 256 split in two");
   using Cfg = BwdCfg<D, 64>;
   constexpr int BK = Cfg::BK, BQ = Cfg::BQ, NKS = Cfg::NKS, NDB = Cfg::NDB, DMA_Q = Cfg::DMA_Q;
+  constexpr int NDO = NDB / DSPLIT;  // output column blocks of this workgroup
   constexpr int NPIECE = 2 * DMA_Q + 1;  // Q pieces, dO pieces, then -LSE log2e / Delta
   static_assert(NPIECE == NKS + 1, "pieces are issued over phases A and B");
   // dS^T row stride (elements): 64 queries + 8, so that the rows of a
@@ -763,7 +798,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 
   const int id = blockIdx.x;
   const int bh = id % BH;
-  const int ktile = id / BH;  // causal: lowest keys (most work) first
+  const int ktile = id / BH / DSPLIT;  // causal: lowest keys (most work) first
+  const int d0 = DSPLIT > 1 ? (id / BH) % DSPLIT * (D / DSPLIT) : 0;  // first dK / dV column
   const int k0 = ktile * BK;
   const size_t base = (size_t)bh * (size_t)S * D;
   const uint16_t* Qh = Q + base;
@@ -789,7 +825,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const int key = kw0 + c32;
 
   BwdOffsets<D, Cfg> of;
-  of.init(wave, lane);
+  of.init(wave, lane, d0);
 
   // query tiles in walking order: causal from the diagonal on, non-causal
   // (fused mode) rotated by key tile
@@ -892,9 +928,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     dqlane = (uint32_t)((4 * hh) * D + dcol) * 4u;
   }
 
-  f32x16 dk[NDB], dv[NDB];
+  f32x16 dk[NDO], dv[NDO];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
+  for (int db = 0; db < NDO; ++db) {
     dk[db] = f32x16{};
     dv[db] = f32x16{};
   }
@@ -1003,7 +1039,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(ot.arow[ks]));
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(ot.trq[db][0]), "+v"(ot.trq[db][1]));
+      for (int db = 0; db < NDO; ++db) asm volatile("" : "+v"(ot.trq[db][0]), "+v"(ot.trq[db][1]));
       if constexpr (DQ) {
         int dso_t[2] = {dso[0], dso[1]};
         int dsw_t = dsw;
@@ -1057,8 +1093,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 
   // ---- epilogue: dK = scale * acc, dV = acc (bf16) -------------------------
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const int d = 32 * db + c32;
+  for (int db = 0; db < NDO; ++db) {
+    const int d = d0 + 32 * db + c32;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kk = kw0 + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -1070,13 +1106,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   }
 }
 
-template <bool CAUSAL, bool RAGGED, bool DQ>
+template <bool CAUSAL, bool RAGGED, bool DQ, int D = 128, int DSPLIT = 1>
 static hipError_t launch_dkdv_pipe_rt(const BwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   const int nkt = (a.S + 127) / 128;
   const int kid = DQ ? KID_BWD_MAIN : KID_BWD_DKDV;
   prof_begin(kid, st);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<CAUSAL, RAGGED, DQ>), dim3(nkt * BH), dim3(256), 0, st, (const uint16_t*)a.Q,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, DSPLIT, CAUSAL, RAGGED, DQ>), dim3(nkt * BH * DSPLIT), dim3(256), 0, st,
+                     (const uint16_t*)a.Q,
                      (const uint16_t*)a.K, (const uint16_t*)a.V, (const uint16_t*)a.dO, a.nlse2, a.delta,
                      (uint16_t*)a.dK, (uint16_t*)a.dV, a.dq32, BH, a.S, a.scale, a.scale * kLog2e);
   prof_end(kid, st);
@@ -1173,7 +1210,12 @@ static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
   if constexpr (D == 128) {
     return launch_dkdv_pipe_t<CAUSAL>(a, st);
   } else if constexpr (D == 256) {
-    // 32-query tiles, V tile in LDS, each workgroup forms 128 of the 256 columns
+    // each workgroup forms 128 of the 256 columns: the pipelined 64-query
+    // tile when S is a multiple of 128 (variant 1: the one-pass tile at every
+    // length), else the one-pass tile over 32-query tiles with the V tile in
+    // LDS (the pipelined tile's masked-on-every-tile form crashes the
+    // compiler's AGPR-copy rewrite pass at this head dim)
+    if (a.S % 128 == 0 && kernel_variant(VAR_DKDV) != 1) return launch_dkdv_pipe_rt<CAUSAL, false, false, D, 2>(a, st);
     return (a.S % 32 == 0) ? launch_main_t<D, 32, CAUSAL, false, true, 1, 2, false>(a, st)
                            : launch_main_t<D, 32, CAUSAL, false, true, 1, 2, true>(a, st);
   } else {

@@ -104,8 +104,8 @@ enum KernelId {
 
 // Kernel variants kept for measurement (0 = the default kernel).  The
 // choice comes from attn_set_variant, else from the environment variables
-// ATTN97_FWD_VARIANT, ATTN97_DQ_VARIANT (read once).
-enum VariantSlot { VAR_FWD = 0, VAR_DQ, VAR_COUNT };
+// ATTN97_FWD_VARIANT, ATTN97_DQ_VARIANT, ATTN97_DKDV_VARIANT (read once).
+enum VariantSlot { VAR_FWD = 0, VAR_DQ, VAR_DKDV, VAR_COUNT };
 int kernel_variant(int slot);
 
 // Called by the launchers around each kernel launch (no-ops unless timing is on).

@@ -294,10 +294,12 @@ def test_set_variant():
     assert lib.attn_set_variant(b"bwd_dq", 1) == OK
     assert lib.attn_set_variant(b"bwd_dq", 2) == VALUE
     assert lib.attn_set_variant(b"bwd_dq", -2) == VALUE
+    assert lib.attn_set_variant(b"bwd_dkdv", 1) == OK
+    assert lib.attn_set_variant(b"bwd_dkdv", 2) == VALUE
     # the measured losers are no longer built
-    assert lib.attn_set_variant(b"bwd_dkdv", 0) == UNSUP
     assert lib.attn_set_variant(b"fwd_fp8", 0) == UNSUP
+    assert lib.attn_set_variant(b"bwd_main", 0) == UNSUP
     assert lib.attn_set_variant(b"nope", 0) == UNSUP
     assert lib.attn_set_variant(None, 0) == NULL
-    for k in (b"fwd", b"bwd_dq"):
+    for k in (b"fwd", b"bwd_dq", b"bwd_dkdv"):
         assert lib.attn_set_variant(k, -1) == OK

@@ -602,3 +602,30 @@ def test_two_step_tiles_ragged(S):
         _assert_close("dQ", _np(dq), rdq)
         _assert_close("dK", _np(dk), rdk)
         _assert_close("dV", _np(dv), rdv)
+
+
+# ----------------------------------------------------------------------------
+# D = 256 split backward, S a multiple of 128: the pipelined dK / dV tile with
+# the columns split between two workgroups (bwd_dkdv variant 1: the one-pass
+# tile it replaced), every element against the float64 oracle
+# ----------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("S", (128, 256, 640))
+@pytest.mark.parametrize("variant", (0, 1))
+def test_bwd_d256_dkdv_tiles(S, variant):
+    print(f"[d256 dkdv] S={S} variant={variant}", flush=True)
+    q, k, v, do = make_qkvdo(1, 2, S, 256, seed=400 + S)
+    scale = 1.0 / math.sqrt(256)
+    qg, kg, vg, dog = _gpu(q, k, v, do)
+    L.set_variant("bwd_dkdv", variant)
+    try:
+        for causal in (False, True):
+            o, lse = L.attn_fwd(qg, kg, vg, scale=scale, causal=causal)
+            dq, dk, dv = L.attn_bwd(qg, kg, vg, o, dog, lse, scale=scale, causal=causal, bwd_mode="split")
+            rdq, rdk, rdv = oracle.attention_bwd(q, k, v, do, scale, causal)
+            _assert_close("dQ", _np(dq), rdq)
+            _assert_close("dK", _np(dk), rdk)
+            _assert_close("dV", _np(dv), rdv)
+    finally:
+        L.set_variant("bwd_dkdv", -1)
