@@ -342,7 +342,8 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* Qb, const uint16_t* dO
                                           const bf16x8 (&vreg)[D / 16], f32x16 (&dk)[NDO], f32x16 (&dv)[NDO],
                                           int q0, int key, int S, float C, int hh, IssuePart&& issue_part,
                                           Dq&& dq = Dq{}) {
-  static_assert(Cfg::NQB == 2 && (D == 128 || D == 256) && NDO == 4, "two 32-query blocks, four output blocks");
+  static_assert(Cfg::NQB == 2 && ((D == 64 && NDO == 2) || ((D == 128 || D == 256) && NDO == 4)),
+                "two 32-query blocks; four output blocks (two at D = 64)");
   constexpr int NKS = Cfg::NKS, NDB = NDO, CPR = Cfg::CPR;
   tile_marker<MASK>();
   int mlo = 0, mhi = 0;
@@ -425,8 +426,40 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* Qb, const uint16_t* dO
   auto sm_ds = [&](const f32x16& ndacc, int r) { put(r, pp[r], -pp[r] * ndacc[r]); };
 
   // B: S, dP of block 1, each step with two elements of block 0's softmax
-  // (D = 256: one element per step, the same three stages)
-  if constexpr (NKS == 16) {
+  // (D = 256: one element per step, D = 64: four, the same three stages)
+  if constexpr (NKS == 4) {
+    bf16x8 qa[NKS], da[NKS];
+    f32x4 l4[4];
+    qa[0] = qfrag(1, 0); da[0] = dofrag(1, 0);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) l4[g] = *reinterpret_cast<const f32x4*>(&nl[8 * g + 4 * hh]);
+    qa[1] = qfrag(1, 1); da[1] = dofrag(1, 1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm_arg(s0, l4, e);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {  // elements 4 ks .. 4 ks + 3 (query rows 8 ks + e)
+      if (ks + 2 < NKS) { qa[ks + 2] = qfrag(1, ks + 2); da[ks + 2] = dofrag(1, ks + 2); }
+      if ((ks & 1) == 0) issue_part(NKS / 2 + ks / 2);
+      if (ks == NKS - 1) issue_part(NKS);
+      s1 = mfma32(qa[ks], kreg[ks], s1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (ks + 1 < NKS) sm_arg(s0, l4, 4 * ks + 4 + e);
+        sm_exp(4 * ks + e, 8 * ks + e);
+      }
+      dp1 = mfma32(da[ks], vreg[ks], dp1);
+      if (ks >= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm_ds(dp0, 4 * ks - 4 + e);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm_ds(dp0, 12 + e);
+    packed(pb0, dsb0);
+    dq.store(0, dsb0);
+  } else if constexpr (NKS == 16) {
     bf16x8 qa[NKS], da[NKS];
     f32x4 l4[4];
     qa[0] = qfrag(1, 0); da[0] = dofrag(1, 0);
@@ -489,7 +522,38 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* Qb, const uint16_t* dO
     dq.store(0, dsb0);
   }
   // C: dV, dK with block 0, each MFMA with one element of block 1's softmax
-  {
+  // (D = 64: two elements per MFMA)
+  if constexpr (NDB == 2) {
+    bf16x8 ta[2 * NDB], tb[2 * NDB];
+    f32x4 l4[4];
+    ta[0] = trdo(0, 0); tb[0] = trq(0, 0);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) l4[g] = *reinterpret_cast<const f32x4*>(&nl[32 + 8 * g + 4 * hh]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm_arg(s1, l4, e);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 2 * NDB; ++i) {  // i = 2 t + db; elements 4 i .. 4 i + 3
+      const int t = i / NDB, db = i % NDB;
+      if (i + 1 < 2 * NDB) { ta[i + 1] = trdo((i + 1) / NDB, (i + 1) % NDB); tb[i + 1] = trq((i + 1) / NDB, (i + 1) % NDB); }
+      dv[db] = mfma32(pb0[t], ta[i], dv[db]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (i + 1 < 2 * NDB) sm_arg(s1, l4, 4 * i + 4 + e);
+        sm_exp(4 * i + e, 32 + 8 * i + e);
+      }
+      dk[db] = mfma32(dsb0[t], tb[i], dk[db]);
+      if (i >= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm_ds(dp1, 4 * i - 4 + e);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm_ds(dp1, 12 + e);
+    packed(pb1, dsb1);
+    dq.store(1, dsb1);
+  } else {
     bf16x8 ta[2 * NDB], tb[2 * NDB];  // [t][db] transposed dO / Q operands
     f32x4 l4[4];
     ta[0] = trdo(0, 0); tb[0] = trq(0, 0);
@@ -775,7 +839,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ dO, const float* __restrict__ nlse2, const float* __restrict__ delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ dq32, int BH, int S, float scale,
     float C) {
-  static_assert((D == 128 && DSPLIT == 1) || (D == 256 && DSPLIT == 2 && !DQ), "D = 128, or D = 256 split in two");
+  static_assert((D == 128 && DSPLIT == 1) || (D == 64 && DSPLIT == 1 && !DQ) || (D == 256 && DSPLIT == 2 && !DQ),
+                "D = 64 or 128, or D = 256 split in two");
   using Cfg = BwdCfg<D, 64>;
   constexpr int BK = Cfg::BK, BQ = Cfg::BQ, NKS = Cfg::NKS, NDB = Cfg::NDB, DMA_Q = Cfg::DMA_Q;
   constexpr int NDO = NDB / DSPLIT;  // output column blocks of this workgroup
@@ -1219,6 +1284,7 @@ static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
     return (a.S % 32 == 0) ? launch_main_t<D, 32, CAUSAL, false, true, 1, 2, false>(a, st)
                            : launch_main_t<D, 32, CAUSAL, false, true, 1, 2, true>(a, st);
   } else {
+    if (a.S % 128 == 0 && kernel_variant(VAR_DKDV) != 1) return launch_dkdv_pipe_rt<CAUSAL, false, false, D, 1>(a, st);
     // (the clamp-free variant measured no faster here: non-causal -0.5 %, causal +2 %)
     return launch_main_t<D, 32, CAUSAL, false, false, 2>(a, st);
   }

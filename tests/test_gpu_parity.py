@@ -605,18 +605,20 @@ def test_two_step_tiles_ragged(S):
 
 
 # ----------------------------------------------------------------------------
-# D = 256 split backward, S a multiple of 128: the pipelined dK / dV tile with
-# the columns split between two workgroups (bwd_dkdv variant 1: the one-pass
-# tile it replaced), every element against the float64 oracle
+# D = 64 and 256 split backward, S a multiple of 128: the pipelined dK / dV
+# tile (at D = 256 with the columns split between two workgroups; bwd_dkdv
+# variant 1: the one-pass tile it replaced), every element against the
+# float64 oracle
 # ----------------------------------------------------------------------------
 
 
+@pytest.mark.parametrize("D", (64, 256))
 @pytest.mark.parametrize("S", (128, 256, 640))
 @pytest.mark.parametrize("variant", (0, 1))
-def test_bwd_d256_dkdv_tiles(S, variant):
-    print(f"[d256 dkdv] S={S} variant={variant}", flush=True)
-    q, k, v, do = make_qkvdo(1, 2, S, 256, seed=400 + S)
-    scale = 1.0 / math.sqrt(256)
+def test_bwd_dkdv_tiles_d64_d256(D, S, variant):
+    print(f"[dkdv tiles] D={D} S={S} variant={variant}", flush=True)
+    q, k, v, do = make_qkvdo(1, 2, S, D, seed=400 + S + D)
+    scale = 1.0 / math.sqrt(D)
     qg, kg, vg, dog = _gpu(q, k, v, do)
     L.set_variant("bwd_dkdv", variant)
     try:
