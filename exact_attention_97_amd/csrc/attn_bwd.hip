@@ -101,6 +101,50 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
+// Epilogue of the dK / dV kernels.  The accumulators hold one column per
+// lane (16 keys per lane and 32-column block); stored straight out that is
+// one 2-byte store per lane and element.  Instead the wavefront stages its 32
+// keys x DW columns as bf16 in its own LDS slice (row-major, stride DW) and
+// stores whole 16-byte chunks of rows: DW / 16 stores per matrix instead of
+// 16 NDO.  dK is multiplied by `scale`.  The slice is reused for dV once
+// dK's rows have been read back (the LDS operations of one wavefront
+// complete in issue order).  dKw / dVw: row 0 of the wavefront's keys at its
+// first column; ld: row stride (elements); rows at or past nrows are not
+// stored.
+template <int NDO>
+__device__ __forceinline__ void store_dkdv_rows(const f32x16 (&dk)[NDO], const f32x16 (&dv)[NDO], float scale,
+                                                uint16_t* slice, uint16_t* dKw, uint16_t* dVw, int ld, int nrows,
+                                                int lane) {
+  constexpr int DW = 32 * NDO, CPR = DW / 8, RPI = 64 / CPR;
+  static_assert(64 % CPR == 0 && 32 % RPI == 0, "whole rows per store");
+  const int hh = lane >> 5, c32 = lane & 31;
+  const int rr = lane / CPR, c8 = (lane % CPR) * 8;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+#pragma unroll
+    for (int db = 0; db < NDO; ++db) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = m == 0 ? dk[db][r] * scale : dv[db][r];
+        slice[(8 * (r >> 2) + 4 * hh + (r & 3)) * DW + 32 * db + c32] = __builtin_bit_cast(uint16_t, (__bf16)x);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint16_t* dst = m == 0 ? dKw : dVw;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int row = i * RPI + rr;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(slice + row * DW + c8);
+      if (row < nrows) *reinterpret_cast<u32x4*>(dst + (size_t)row * ld + c8) = v;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
 // Two LDS transpose loads (four rows each, at this lane's column) as one
 // MFMA operand.
 __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* p0, const uint16_t* p1) {
@@ -782,18 +826,15 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
     barrier_keep_loads();
   }
 
-  // ---- epilogue: dK = scale * acc, dV = acc (bf16) -------------------------
-#pragma unroll
-  for (int db = 0; db < NDO; ++db) {
-    const int d = d0 + 32 * db + c32;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kk = kw0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (kk < S) {
-        dK[base + (size_t)kk * D + d] = __builtin_bit_cast(uint16_t, (__bf16)(dk[db][r] * scale));
-        dV[base + (size_t)kk * D + d] = __builtin_bit_cast(uint16_t, (__bf16)dv[db][r]);
-      }
-    }
+  // ---- epilogue: dK = scale * acc, dV = acc (bf16), staged in the query-tile
+  // buffers (free once every wavefront is past the last tile) -----------------
+  static_assert(2 * 32 * 32 * NDO <= 2 * Cfg::QTILE, "two staging slices per buffer pair");
+  __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (0 << 14));  // vmcnt(0) lgkmcnt(0)
+  __syncthreads();
+  if (kw0 < S) {
+    uint16_t* slice = (wave < 2 ? &sm.Qs[0][0] : &sm.dOs[0][0]) + (wave & 1) * 32 * 32 * NDO;
+    store_dkdv_rows<NDO>(dk, dv, scale, slice, dK + base + (size_t)kw0 * D + d0, dV + base + (size_t)kw0 * D + d0, D,
+                         S - kw0, lane);
   }
 }
 
@@ -1156,16 +1197,28 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     dq_atomics(acc, qt_at(last) * BQ);
   }
 
-  // ---- epilogue: dK = scale * acc, dV = acc (bf16) -------------------------
+  // ---- epilogue: dK = scale * acc, dV = acc (bf16), staged in the query-tile
+  // buffers (free once every wavefront is past the last tile).  The ragged
+  // instantiation stores straight from the accumulators: it has no
+  // registers to spare (with the staging its allocation spills to scratch).
+  if constexpr (!RAGGED) {
+    static_assert(2 * 32 * 32 * NDO <= Cfg::QTILE, "two staging slices per buffer");
+    __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (0 << 14));  // vmcnt(0) lgkmcnt(0)
+    __syncthreads();
+    uint16_t* slice = (wave < 2 ? Qs0 : Qs1) + (wave & 1) * 32 * 32 * NDO;
+    store_dkdv_rows<NDO>(dk, dv, scale, slice, dK + base + (size_t)kw0 * D + d0, dV + base + (size_t)kw0 * D + d0, D,
+                         S - kw0, lane);
+  } else {
 #pragma unroll
-  for (int db = 0; db < NDO; ++db) {
-    const int d = d0 + 32 * db + c32;
+    for (int db = 0; db < NDO; ++db) {
+      const int d = d0 + 32 * db + c32;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kk = kw0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (kk < S) {
-        dK[base + (size_t)kk * D + d] = __builtin_bit_cast(uint16_t, (__bf16)(dk[db][r] * scale));
-        dV[base + (size_t)kk * D + d] = __builtin_bit_cast(uint16_t, (__bf16)dv[db][r]);
+      for (int r = 0; r < 16; ++r) {
+        const int kk = kw0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (kk < S) {
+          dK[base + (size_t)kk * D + d] = __builtin_bit_cast(uint16_t, (__bf16)(dk[db][r] * scale));
+          dV[base + (size_t)kk * D + d] = __builtin_bit_cast(uint16_t, (__bf16)dv[db][r]);
+        }
       }
     }
   }
