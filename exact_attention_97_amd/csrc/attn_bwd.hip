@@ -902,10 +902,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(256))) uint16_t dsT0[DQ ? BK * DRS : 8];
   __shared__ __attribute__((aligned(256))) uint16_t dsT1[DQ ? BK * DRS : 8];
 
-  const int id = blockIdx.x;
-  const int bh = id % BH;
-  const int ktile = id / BH / DSPLIT;  // causal: lowest keys (most work) first
-  const int d0 = DSPLIT > 1 ? (id / BH) % DSPLIT * (D / DSPLIT) : 0;  // first dK / dV column
+  // one head's key tiles together on an XCD, except for causal passes with
+  // fewer than 128 tiles per head, where the grid-wide heaviest-first order
+  // balances the tail better (same-process A/B: non-causal 0.2-4 % faster,
+  // ctx32k causal 3.7 % faster, S = 4096 / 8192 causal 2-3.5 % slower)
+  int bh, kt2;
+  const int ntl = gridDim.x / BH;
+  xcd_head_order(blockIdx.x, BH, ntl, !CAUSAL || ntl >= 128, bh, kt2);
+  const int ktile = kt2 / DSPLIT;  // causal: lowest keys (most work) first
+  const int d0 = DSPLIT > 1 ? kt2 % DSPLIT * (D / DSPLIT) : 0;  // first dK / dV column
   const int k0 = ktile * BK;
   const size_t base = (size_t)bh * (size_t)S * D;
   const uint16_t* Qh = Q + base;

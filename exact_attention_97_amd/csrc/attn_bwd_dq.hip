@@ -170,10 +170,11 @@ __global__ __launch_bounds__(64 * Cfg::NW, OCC) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) uint16_t Vb0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t Vb1[TILE];
 
-  // heaviest causal query tiles first; one head's tiles on one XCD when B*H % 8 == 0
-  const int id = blockIdx.x;
-  const int bh = id % BH;
-  const int rank = id / BH;
+  // block order (xcd_head_order): one head's query tiles together on an XCD,
+  // except for causal passes with fewer than 128 tiles per head, which run
+  // the heaviest query tiles of all heads first
+  int bh, rank;
+  xcd_head_order(blockIdx.x, BH, nqt, !causal || nqt >= 128, bh, rank);
   const int qt = causal ? (nqt - 1 - rank) : rank;
   const int q0 = qt * BR;
   const size_t base = (size_t)bh * (size_t)S * D;

@@ -305,11 +305,19 @@ __global__ __launch_bounds__(64 * Cfg::NW, (Cfg::D == 256 || Cfg::NW == 8) ? 1 :
   auto kbuf = [&](int i) -> uint16_t* { return i == 0 ? Kb0 : (i == 1 ? Kb1 : Kb2); };
   auto vbuf = [&](int i) -> uint16_t* { return i == 0 ? Vb0 : (i == 1 ? Vb1 : Vb2); };
 
-  // Heaviest causal query tiles first, all heads of one rank together; with
-  // B*H a multiple of 8 every workgroup of one head lands on the same XCD.
+  // Block order (xcd_head_order): one head's query tiles together on an XCD,
+  // except for causal passes with fewer than 128 tiles per head and the
+  // split-KV kernel, which take the grid-wide order (heaviest causal query
+  // tiles first, all heads of one rank together; with B*H a multiple of 8
+  // every workgroup of one head still lands on the same XCD).
   const int id = blockIdx.x;
-  const int bh = id % BH;
-  const int rank = SPLITKV ? (id / BH) % nqt : id / BH;
+  int bh, rank;
+  if (SPLITKV) {
+    bh = id % BH;
+    rank = (id / BH) % nqt;
+  } else {
+    xcd_head_order(id, BH, nqt, !causal || nqt >= 128, bh, rank);
+  }
   const int split = SPLITKV ? id / BH / nqt : 0;
   const int qt = causal ? (nqt - 1 - rank) : rank;
   const int q0 = qt * BR;

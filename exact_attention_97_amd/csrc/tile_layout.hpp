@@ -8,6 +8,27 @@
 
 namespace attn97 {
 
+// Block order.  Workgroups are dispatched to the eight XCDs in turn (block
+// id mod 8) and, within an XCD, in id order.  grouped (and BH a multiple of
+// 8): block id takes head x + 8 (s / n) and tile s mod n (x = id mod 8,
+// s = id / 8): each XCD owns whole heads and runs one head's n tiles one
+// after another, so the workgroups an XCD runs together stream the same
+// head's operand tiles through its L2.  Otherwise head id mod BH, tile
+// id / BH: tile t of every head before tile t + 1 of any (with B*H a
+// multiple of 8 each head still on one XCD), the order that puts a causal
+// pass's heaviest tiles first across the whole grid.  n: tiles per head
+// (gridDim.x / BH).
+__device__ __forceinline__ void xcd_head_order(int id, int BH, int n, bool grouped, int& bh, int& t) {
+  if (grouped && BH % 8 == 0) {
+    const int x = id & 7, s = id >> 3;
+    bh = x + 8 * (s / n);
+    t = s - (s / n) * n;
+  } else {
+    bh = id % BH;
+    t = id / BH;
+  }
+}
+
 // Physical 16-byte chunk index, inside a K or V tile, of logical chunk c of
 // row `row`.  Rows of 256 bytes (D = 128) or 512 bytes (D = 256) XOR the low
 // four bits of the chunk with f(row) = ((row & 3) << 2) | ((row >> 2) & 3),
