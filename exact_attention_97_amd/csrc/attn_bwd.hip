@@ -1,4 +1,6 @@
-// attn_bwd.hip - backward pass of exact attention on gfx950 (dQ by atomics).
+// attn_bwd.hip - backward pass of exact attention on gfx950: the dK/dV
+// kernels (split mode; with dQ by fp32 atomics in the atomic mode) and the
+// launch logic of both modes.
 //
 // The forward pass stored only O and the row log-sum-exp, so the backward
 // pass recomputes the probabilities from them:
@@ -838,8 +840,10 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
   }
 }
 
-// dK/dV kernel for D = 128: the software-pipelined tile of dkdv_tile over
-// 64-query tiles.  One workgroup of four wavefronts owns 128 keys; each
+// dK/dV kernel (D = 64 and 128; D = 256 with the columns split, below) with
+// S a multiple of 128, and the fused atomic mode at D = 128: the
+// software-pipelined tile of dkdv_tile over 64-query tiles.  One workgroup
+// of four wavefronts owns 128 keys; each
 // wavefront keeps its 32 keys' K and V rows and dK, dV accumulators in
 // registers.  The two query-tile buffers are separate __shared__ arrays and
 // the loop is unrolled by two, so that every buffer a tile reads or loads

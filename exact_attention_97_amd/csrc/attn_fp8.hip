@@ -391,10 +391,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_fp8_kernel(Fp8Buf f, uint
   __shared__ __attribute__((aligned(1024))) uint8_t Vb1[FD * FBC];
 
   const int Sp = f.Sp;
-  const int id = blockIdx.x;
-  const int bh = id % BH;
-  const int rank = id / BH;
-  const int qt = causal ? (nqt - 1 - rank) : rank;  // heaviest causal tiles first
+  // block order (xcd_head_order): one head's query tiles together on an XCD
+  // in non-causal passes (same-process A/B: 1.1 % faster at S = 8192, 2.9 %
+  // at S = 32768); causal passes run the heaviest query tiles of all heads
+  // first (the grouped order measured 1.1 % slower at S = 32768)
+  int bh, rank;
+  xcd_head_order(blockIdx.x, BH, nqt, !causal, bh, rank);
+  const int qt = causal ? (nqt - 1 - rank) : rank;
   const int q0 = qt * BR;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
