@@ -44,9 +44,9 @@ struct DqWavePipe {
   static constexpr int D = Cfg::D, NKS = Cfg::NKS, NDB = Cfg::NDB, CPR = Cfg::CPR;
   static_assert(Cfg::NKB == 2, "two 32-key blocks per tile");
   // softmax elements (16 per block) per chunk of phase B (one reduction step
-  // of the S and dP products) and of phase C (one dQ MFMA)
-  static constexpr int EB = 16 / NKS, EC = 16 / (2 * NDB);
-  static_assert(EB * NKS == 16 && EC * 2 * NDB == 16, "elements spread evenly over the chunks");
+  // of the S and dP products)
+  static constexpr int EB = 16 / NKS;
+  static_assert(EB * NKS == 16 && 8 % NDB == 0, "elements spread evenly over the chunks");
 
   template <bool MASK>
   __device__ __forceinline__ static void elem(const f32x16& sacc, const f32x16& dpacc, int r, float C, float nlse2,
@@ -115,6 +115,12 @@ struct DqWavePipe {
       dsb0[0] = pack_probs(*reinterpret_cast<float(*)[8]>(&ds[0]));
       dsb0[1] = pack_probs(*reinterpret_cast<float(*)[8]>(&ds[8]));
     }
+    // Block 1's elements: at D = 64 and 256, 0 .. 7 (the first k-step of its
+    // dQ product) over phase C's 2 NDB MFMAs and 8 .. 15 over the first NDB
+    // MFMAs of phase D, which need only elements 0 .. 7 (same-process A/B:
+    // dQ 3 % faster at D = 256, 0.7 % at D = 64); at D = 128 all sixteen
+    // over phase C (the split measured 0.4-0.7 % slower there)
+    constexpr int NC = D == 128 ? 16 : 8;  // block 1 elements in phase C
     {  // C
       bf16x8 ta[2 * NDB];
       ta[0] = ktr(0, 0);
@@ -125,14 +131,12 @@ struct DqWavePipe {
         if (i + 1 < 2 * NDB) ta[i + 1] = ktr((i + 1) / NDB, (i + 1) % NDB);
         dqacc[db] = mfma32(ta[i], t == 0 ? dsb0[0] : dsb0[1], dqacc[db]);
 #pragma unroll
-        for (int e = 0; e < EC; ++e) {  // EC of block 1's 16 elements per dQ MFMA
-          const int r = EC * i + e;
+        for (int r = NC * i / (2 * NDB); r < NC * (i + 1) / (2 * NDB); ++r)
           elem<MASK>(s1, dp1, r, C, nlse2, dlt, keyof(1, r), lim, ds[r]);
-        }
         __builtin_amdgcn_sched_barrier(0);
       }
       dsb1[0] = pack_probs(*reinterpret_cast<float(*)[8]>(&ds[0]));
-      dsb1[1] = pack_probs(*reinterpret_cast<float(*)[8]>(&ds[8]));
+      if constexpr (NC == 16) dsb1[1] = pack_probs(*reinterpret_cast<float(*)[8]>(&ds[8]));
     }
     {  // D
       bf16x8 ta[2 * NDB];
@@ -143,6 +147,12 @@ struct DqWavePipe {
         const int t = i / NDB, db = i % NDB;
         if (i + 1 < 2 * NDB) ta[i + 1] = ktr(2 + (i + 1) / NDB, (i + 1) % NDB);
         dqacc[db] = mfma32(ta[i], t == 0 ? dsb1[0] : dsb1[1], dqacc[db]);
+        if (NC == 8 && i < NDB) {
+#pragma unroll
+          for (int r = 8 + 8 * i / NDB; r < 8 + 8 * (i + 1) / NDB; ++r)
+            elem<MASK>(s1, dp1, r, C, nlse2, dlt, keyof(1, r), lim, ds[r]);
+          if (i == NDB - 1) dsb1[1] = pack_probs(*reinterpret_cast<float(*)[8]>(&ds[8]));
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
