@@ -631,3 +631,29 @@ def test_bwd_dkdv_tiles_d64_d256(D, S, variant):
             _assert_close("dV", _np(dv), rdv)
     finally:
         L.set_variant("bwd_dkdv", -1)
+
+
+# ----------------------------------------------------------------------------
+# Block order with B*H a multiple of 8 (each XCD takes whole heads, one head's
+# tiles together in non-causal passes) at small, ragged and tile-multiple
+# lengths: every element of the forward and backward outputs against the
+# float64 oracle (the other small tests have B*H of 2 to 6, the other order)
+# ----------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("B,H,S,D", ((2, 4, 300, 128), (1, 8, 640, 128), (2, 8, 256, 64), (1, 8, 384, 256)))
+def test_grouped_block_order(B, H, S, D):
+    print(f"[grouped block order] B={B} H={H} S={S} D={D}", flush=True)
+    q, k, v, do = make_qkvdo(B, H, S, D, seed=600 + S + D)
+    scale = 1.0 / math.sqrt(D)
+    qg, kg, vg, dog = _gpu(q, k, v, do)
+    for causal in (False, True):
+        o, lse = L.attn_fwd(qg, kg, vg, scale=scale, causal=causal)
+        ro, rl = oracle.attention_fwd(q, k, v, scale, causal)
+        _assert_close("O", _np(o), ro)
+        _assert_lse(_np(lse), rl)
+        dq, dk, dv = L.attn_bwd(qg, kg, vg, o, dog, lse, scale=scale, causal=causal, bwd_mode="split")
+        rdq, rdk, rdv = oracle.attention_bwd(q, k, v, do, scale, causal)
+        _assert_close("dQ", _np(dq), rdq)
+        _assert_close("dK", _np(dk), rdk)
+        _assert_close("dV", _np(dv), rdv)
