@@ -471,7 +471,7 @@ attn_status attn_exp2_eval(const float* x, float* y, long n, int mode, void* str
 attn_status attn_set_variant(const char* kernel, int variant) {
   if (!kernel) return ATTN_ERR_NULL;
   static const char* names[attn97::VAR_COUNT] = {"fwd", "bwd_dq", "bwd_dkdv"};
-  static const int count[attn97::VAR_COUNT] = {2, 2, 2};  // variants 0 .. count-1
+  static const int count[attn97::VAR_COUNT] = {3, 3, 2};  // variants 0 .. count-1
   for (int i = 0; i < attn97::VAR_COUNT; ++i) {
     if (strcmp(kernel, names[i]) != 0) continue;
     if (variant < -1 || variant >= count[i]) return ATTN_ERR_VALUE;

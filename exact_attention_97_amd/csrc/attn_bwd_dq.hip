@@ -359,21 +359,27 @@ static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
 // H=16: D = 64 0.764 against 0.781 ms non-causal (two workgroups of four
 // wavefronts per CU), 0.388 against 0.395 causal; D = 256 3.208 against
 // 3.346 ms non-causal (32-key tiles before), 1.644 against 1.756 causal.
-// D = 128: the cooperative big tile, one workgroup of eight wavefronts (256
-// queries) per CU sharing each K / V tile in LDS, 64-key steps in the
-// pipelined step (measured 3-4 % faster than four wavefronts at S = 4096 and
-// 8192, 2.5 % at 32768), two steps per LDS tile (128 KiB of LDS: one load
-// issue and one barrier per 128 keys; 10 % faster non-causal at S = 8192,
-// 12 % at 4096, 1-3 % causal).  Variant 1 (attn_set_variant("bwd_dq", 1) or
-// ATTN97_DQ_VARIANT=1): two workgroups of four wavefronts per CU.
+// D = 128, non-causal with S >= 8192: the cooperative big tile, one
+// workgroup of eight wavefronts (256 queries) per CU sharing each K / V tile
+// in LDS, 64-key steps in the pipelined step, two steps per LDS tile (128
+// KiB of LDS: one load issue and one barrier per 128 keys).  Otherwise two
+// workgroups of four wavefronts per CU, which balance shorter and causal
+// passes better.  Interleaved same-process A/B of the two (B*H*S fixed at
+// 2^19, D = 128; ms, eight against four wavefronts): S = 2048 0.396 / 0.366
+// non-causal, 0.231 / 0.206 causal; S = 4096 0.690 / 0.676, 0.375 / 0.360;
+// S = 8192 1.300 / 1.315, 0.683 / 0.677; S = 32768 (B*H = 32) 20.21 / 20.42,
+// 10.30 / 10.27.  Variants (attn_set_variant("bwd_dq", v) or
+// ATTN97_DQ_VARIANT=v): 1 four wavefronts, 2 eight wavefronts, at every
+// length.
 static int dq_variant() { return kernel_variant(VAR_DQ); }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
   switch (a.D) {
     case 64: return launch_dq_t<FwdCfg<64, 64, 4, 2>, 2>(a, st);  // two workgroups (eight wavefronts) per CU
     case 128:
-      if (dq_variant() == 1) return launch_dq_t<FwdCfg<128, 64, 4, 2>, 2>(a, st);
-      return launch_dq_t<FwdCfg<128, 64, 8, 2>, 1, 2>(a, st);
+      if (dq_variant() == 2 || (dq_variant() == 0 && !a.causal && a.S >= 8192))
+        return launch_dq_t<FwdCfg<128, 64, 8, 2>, 1, 2>(a, st);
+      return launch_dq_t<FwdCfg<128, 64, 4, 2>, 2>(a, st);
     case 256: return launch_dq_t<FwdCfg<256, 64, 4, 2>, 1>(a, st);  // one workgroup per CU
     default: return hipErrorInvalidValue;
   }

@@ -790,6 +790,7 @@ static int device_cus() {
 
 static bool fwd_big_tile(const FwdArgs& a) {
   if (fwd_variant() == 1) return true;
+  if (fwd_variant() == 2) return false;
   const long wgs = (long)((a.S + 255) / 256) * a.B * a.H;
   return a.S >= 4096 && wgs % device_cus() == 0;
 }

@@ -285,8 +285,9 @@ attn_status attn_exp2_eval(const float* x, float* y, long n, int mode, void* str
 /*
  * Diagnostic: select a kernel variant kept for measurement, for subsequent
  * calls in this process.  kernel: "fwd" (D = 128 forward: 0 default, 1 the
- * eight-wavefront tile at every length), "bwd_dq" (D = 128 dQ of the split
- * backward: 0 default, 1 four wavefronts per workgroup), "bwd_dkdv" (D = 64
+ * eight-wavefront tile at every length, 2 the four-wavefront tile at every
+ * length), "bwd_dq" (D = 128 dQ of the split backward: 0 default, 1 four
+ * wavefronts per workgroup, 2 eight, at every length), "bwd_dkdv" (D = 64
  * and 256 dK / dV of the split backward: 0 default, 1 the one-pass tile also
  * where S is a multiple of 128); variant -1 returns to the choice of the
  * environment variables ATTN97_FWD_VARIANT / ATTN97_DQ_VARIANT /

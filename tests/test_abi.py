@@ -289,10 +289,12 @@ def test_fwd_fp8_rejects(kw, code):
 def test_set_variant():
     lib = L.load()
     assert lib.attn_set_variant(b"fwd", 1) == OK
-    assert lib.attn_set_variant(b"fwd", 2) == VALUE
+    assert lib.attn_set_variant(b"fwd", 2) == OK
+    assert lib.attn_set_variant(b"fwd", 3) == VALUE
     assert lib.attn_set_variant(b"fwd", -1) == OK
     assert lib.attn_set_variant(b"bwd_dq", 1) == OK
-    assert lib.attn_set_variant(b"bwd_dq", 2) == VALUE
+    assert lib.attn_set_variant(b"bwd_dq", 2) == OK
+    assert lib.attn_set_variant(b"bwd_dq", 3) == VALUE
     assert lib.attn_set_variant(b"bwd_dq", -2) == VALUE
     assert lib.attn_set_variant(b"bwd_dkdv", 1) == OK
     assert lib.attn_set_variant(b"bwd_dkdv", 2) == VALUE

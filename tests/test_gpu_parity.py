@@ -540,12 +540,12 @@ def test_splitkv_workload_full_size(name):
 
 
 # ----------------------------------------------------------------------------
-# kernel variants kept for measurement (fwd 1: the eight-wavefront cooperative
-# tile at every length; dQ 1: the four-wavefront dQ tile):
+# kernel variants kept for measurement (fwd 1 / 2: the eight- / four-wavefront
+# tile at every length; dQ 1 / 2: the four- / eight-wavefront dQ tile):
 # each against the float64 oracle, ragged length, both causal settings
 # ----------------------------------------------------------------------------
 
-VARIANTS = [("fwd", 1), ("bwd_dq", 1)]
+VARIANTS = [("fwd", 1), ("fwd", 2), ("bwd_dq", 1), ("bwd_dq", 2)]
 
 
 @pytest.mark.parametrize("kernel,variant", VARIANTS)
