@@ -223,7 +223,7 @@ __device__ __forceinline__ void dma_row_part(const uint16_t* __restrict__ src, i
     const uint32_t last = (uint32_t)(S - 1 - r0);
     off = (row > last ? last : row) * (2 * D) + off % (2 * D);
   }
-  lds_dma<16>(tile, (uint32_t)(S - r0) * (uint32_t)(D * 2), off, dst + 512 * (wave * NPW + n));
+  lds_dma<16>(tile, (uint32_t)(S > r0 ? S - r0 : 0) * (uint32_t)(D * 2), off, dst + 512 * (wave * NPW + n));
 }
 
 template <int D, int NPW, bool CLAMP = true>
@@ -840,9 +840,9 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
   }
 }
 
-// dK/dV kernel (D = 64 and 128; D = 256 with the columns split, below) with
-// S a multiple of 128, and the fused atomic mode at D = 128: the
-// software-pipelined tile of dkdv_tile over 64-query tiles.  One workgroup
+// dK/dV kernel of the split mode (D = 64 and 128; D = 256 with the columns
+// split, below), and of the fused atomic mode at D = 128 with S a multiple
+// of 128: the software-pipelined tile of dkdv_tile over 64-query tiles.  One workgroup
 // of four wavefronts owns 128 keys; each
 // wavefront keeps its 32 keys' K and V rows and dK, dV accumulators in
 // registers.  The two query-tile buffers are separate __shared__ arrays and
@@ -853,11 +853,13 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
 // MFMA work.
 //
 // Only unmasked tiles sit in the loop (two copies of the tile code, one per
-// buffer set; four would not fit the register budget): with S a multiple of
-// 128 a non-causal tile never needs the mask, and a causal one only in the
-// workgroup's first two query tiles (queries k0 .. k0 + 127, the diagonal
-// block), which are peeled off before the loop.  RAGGED (S not a multiple of
-// 128) masks every tile instead.
+// buffer set; four would not fit the register budget): a non-causal tile
+// never needs the mask, also at lengths that are not a multiple of 128
+// (query rows past S load as zeros and add nothing, keys past S reach only
+// their own unstored dK / dV columns; see ntiles below), and a causal one
+// only in the workgroup's first two query tiles (queries k0 .. k0 + 127,
+// the diagonal block), which are peeled off before the loop.  (The atomic
+// mode takes bwd_main_kernel at lengths that are not a multiple of 128.)
 //
 // DQ (the fused atomic mode): the kernel also forms dQ, so no second kernel
 // recomputes S and dP.  Each tile's dS goes to LDS transposed (dS^T[key][q],
@@ -878,7 +880,7 @@ __global__ __launch_bounds__(256, OCC) void bwd_main_kernel(
 // per key tile (128 each, as in bwd_main_kernel at that head dim); each holds
 // its keys' full K and V rows (the S and dP products contract over all 256
 // columns) and recomputes P and dS.
-template <int D, int DSPLIT, bool CAUSAL, bool RAGGED, bool DQ>
+template <int D, int DSPLIT, bool CAUSAL, bool DQ>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ nlse2, const float* __restrict__ delta,
@@ -946,9 +948,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   // (fused mode) rotated by key tile
   const int nqt = (S + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? (k0 / BQ) : 0;
-  const int ntiles = nqt - qt0;
+  // Any S: the tile count is rounded up to even (the loop takes tiles in
+  // pairs; the atomic mode's lengths, multiples of 128, give an even count).  A tile past the last one, like the rows
+  // past S of a partial one, loads as zeros (out-of-range lanes of the
+  // range-checked LDS-direct loads write zeros), and a zero query row adds
+  // nothing: its Q, dO, -LSE log2e and Delta are 0, so P = 1, dP = 0 and
+  // dS = 0, while dO = 0 zeroes its dV term.  Keys past S are clamped to
+  // S - 1 and only their own (unstored) dK / dV columns see them.
+  const int ntiles = (nqt - qt0 + 1) & ~1;
   const int rot = (!CAUSAL && DQ) ? (ktile * (nqt >= 8 ? nqt / 8 : 1)) % nqt : 0;
-  auto qt_at = [&](int i) { return CAUSAL ? qt0 + i : (i + rot < nqt ? i + rot : i + rot - nqt); };
+  auto qt_at = [&](int i) { return CAUSAL ? qt0 + i : !DQ ? i : (i + rot < nqt ? i + rot : i + rot - nqt); };
 
   // piece p of query tile qt's loads into buffer set P (0: Qs0 ..., 1: Qs1 ...)
   auto piece = [&](int qt, auto P, int p) {
@@ -957,9 +966,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     uint16_t* dd = set ? dOs1 : dOs0;
     const int q0 = qt * BQ;
     if (p < DMA_Q) {
-      dma_row_part<D, DMA_Q, RAGGED>(Qh, q0, BQ, S, qd, wave_u, of.dmaq, p);
+      dma_row_part<D, DMA_Q, false>(Qh, q0, BQ, S, qd, wave_u, of.dmaq, p);
     } else if (p < 2 * DMA_Q) {
-      dma_row_part<D, DMA_Q, RAGGED>(dOh, q0, BQ, S, dd, wave_u, of.dmaq, p - DMA_Q);
+      dma_row_part<D, DMA_Q, false>(dOh, q0, BQ, S, dd, wave_u, of.dmaq, p - DMA_Q);
     } else if (p == 2 * DMA_Q) {
       // -LSE log2e rows from waves 0 and 2, Delta from 1 and 3 (the pairs
       // write the same values): no branch on the wavefront index, which
@@ -968,8 +977,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       const bool odd = (wave_u & 1) != 0;
       const float* src = odd ? DLh : NLh;
       float* dst = odd ? (set ? dl1 : dl0) : (set ? nl1 : nl0);
-      // without RAGGED, S is a multiple of 128 and q0 + 63 < S
-      lds_dma<4>(src, (uint32_t)S * 4u, (uint32_t)(RAGGED ? min(q0 + lane, S - 1) : q0 + lane) * 4u, dst);
+      // rows past S load as zeros (range-checked)
+      lds_dma<4>(src, (uint32_t)S * 4u, (uint32_t)(q0 + lane) * 4u, dst);
     }
   };
 
@@ -1179,16 +1188,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
-  using M = std::integral_constant<bool, RAGGED>;
+  using M = std::false_type;
   int i = 0;
-  if constexpr (CAUSAL && !RAGGED) {  // diagonal block: qt0 even, nqt >= qt0 + 2
+  if constexpr (CAUSAL) {  // diagonal block: qt0 even, ntiles >= 2
     tile(0, P0{}, std::true_type{});
     tile(1, P1{}, std::true_type{});
     i = 2;
   }
   for (; i < ntiles; i += 2) {
     tile(i, P0{}, M{});
-    if (RAGGED && i + 1 >= ntiles) break;  // without RAGGED the tile count is even
     tile(i + 1, P1{}, M{});
   }
 
@@ -1207,39 +1215,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   }
 
   // ---- epilogue: dK = scale * acc, dV = acc (bf16), staged in the query-tile
-  // buffers (free once every wavefront is past the last tile).  The ragged
-  // instantiation stores straight from the accumulators: it has no
-  // registers to spare (with the staging its allocation spills to scratch).
-  if constexpr (!RAGGED) {
-    static_assert(2 * 32 * 32 * NDO <= Cfg::QTILE, "two staging slices per buffer");
-    __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (0 << 14));  // vmcnt(0) lgkmcnt(0)
-    __syncthreads();
-    uint16_t* slice = (wave < 2 ? Qs0 : Qs1) + (wave & 1) * 32 * 32 * NDO;
-    store_dkdv_rows<NDO>(dk, dv, scale, slice, dK + base + (size_t)kw0 * D + d0, dV + base + (size_t)kw0 * D + d0, D,
-                         S - kw0, lane);
-  } else {
-#pragma unroll
-    for (int db = 0; db < NDO; ++db) {
-      const int d = d0 + 32 * db + c32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = kw0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (kk < S) {
-          dK[base + (size_t)kk * D + d] = __builtin_bit_cast(uint16_t, (__bf16)(dk[db][r] * scale));
-          dV[base + (size_t)kk * D + d] = __builtin_bit_cast(uint16_t, (__bf16)dv[db][r]);
-        }
-      }
-    }
-  }
+  // buffers (free once every wavefront is past the last tile) --------------
+  static_assert(2 * 32 * 32 * NDO <= Cfg::QTILE, "two staging slices per buffer");
+  __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (0 << 14));  // vmcnt(0) lgkmcnt(0)
+  __syncthreads();
+  uint16_t* slice = (wave < 2 ? Qs0 : Qs1) + (wave & 1) * 32 * 32 * NDO;
+  store_dkdv_rows<NDO>(dk, dv, scale, slice, dK + base + (size_t)kw0 * D + d0, dV + base + (size_t)kw0 * D + d0, D,
+                       S - kw0, lane);
 }
 
-template <bool CAUSAL, bool RAGGED, bool DQ, int D = 128, int DSPLIT = 1>
+template <bool CAUSAL, bool DQ, int D = 128, int DSPLIT = 1>
 static hipError_t launch_dkdv_pipe_rt(const BwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   const int nkt = (a.S + 127) / 128;
   const int kid = DQ ? KID_BWD_MAIN : KID_BWD_DKDV;
   prof_begin(kid, st);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, DSPLIT, CAUSAL, RAGGED, DQ>), dim3(nkt * BH * DSPLIT), dim3(256), 0, st,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, DSPLIT, CAUSAL, DQ>), dim3(nkt * BH * DSPLIT), dim3(256), 0, st,
                      (const uint16_t*)a.Q,
                      (const uint16_t*)a.K, (const uint16_t*)a.V, (const uint16_t*)a.dO, a.nlse2, a.delta,
                      (uint16_t*)a.dK, (uint16_t*)a.dV, a.dq32, BH, a.S, a.scale, a.scale * kLog2e);
@@ -1249,8 +1240,7 @@ static hipError_t launch_dkdv_pipe_rt(const BwdArgs& a, hipStream_t st) {
 
 template <bool CAUSAL>
 static hipError_t launch_dkdv_pipe_t(const BwdArgs& a, hipStream_t st) {
-  return (a.S % 128 == 0) ? launch_dkdv_pipe_rt<CAUSAL, false, false>(a, st)
-                          : launch_dkdv_pipe_rt<CAUSAL, true, false>(a, st);
+  return launch_dkdv_pipe_rt<CAUSAL, false>(a, st);
 }
 
 // Delta_i = sum_d dO_id O_id (fp32), nlse2_i = -LSE_i log2(e), and zero the
@@ -1338,16 +1328,14 @@ static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
     return launch_dkdv_pipe_t<CAUSAL>(a, st);
   } else if constexpr (D == 256) {
     // each workgroup forms 128 of the 256 columns: the pipelined 64-query
-    // tile when S is a multiple of 128 (variant 1: the one-pass tile at every
-    // length), else the one-pass tile over 32-query tiles with the V tile in
-    // LDS (the pipelined tile's masked-on-every-tile form crashes the
-    // compiler's AGPR-copy rewrite pass at this head dim)
-    if (a.S % 128 == 0 && kernel_variant(VAR_DKDV) != 1) return launch_dkdv_pipe_rt<CAUSAL, false, false, D, 2>(a, st);
+    // tile (variant 1: the one-pass tile over 32-query tiles with the V tile
+    // in LDS)
+    if (kernel_variant(VAR_DKDV) != 1) return launch_dkdv_pipe_rt<CAUSAL, false, D, 2>(a, st);
     return (a.S % 32 == 0) ? launch_main_t<D, 32, CAUSAL, false, true, 1, 2, false>(a, st)
                            : launch_main_t<D, 32, CAUSAL, false, true, 1, 2, true>(a, st);
   } else {
-    if (a.S % 128 == 0 && kernel_variant(VAR_DKDV) != 1) return launch_dkdv_pipe_rt<CAUSAL, false, false, D, 1>(a, st);
-    // (the clamp-free variant measured no faster here: non-causal -0.5 %, causal +2 %)
+    // the pipelined tile (variant 1: the one-pass tile)
+    if (kernel_variant(VAR_DKDV) != 1) return launch_dkdv_pipe_rt<CAUSAL, false, D, 1>(a, st);
     return launch_main_t<D, 32, CAUSAL, false, false, 2>(a, st);
   }
 }
@@ -1362,10 +1350,10 @@ static hipError_t launch_main(const BwdArgs& a, hipStream_t st) {
       // one-pass tile (the fused tile's masked-on-every-tile form needs more
       // registers than the compiler can allocate)
       case 256:
-        return a.S % 128 == 0 ? launch_dkdv_pipe_rt<false, false, true>(a, st)
+        return a.S % 128 == 0 ? launch_dkdv_pipe_rt<false, true>(a, st)
                               : launch_main_t<128, 64, false, true, false, 1>(a, st);
       case 257:
-        return a.S % 128 == 0 ? launch_dkdv_pipe_rt<true, false, true>(a, st)
+        return a.S % 128 == 0 ? launch_dkdv_pipe_rt<true, true>(a, st)
                               : launch_main_t<128, 64, true, true, false, 1>(a, st);
       default: return hipErrorInvalidValue;
     }
