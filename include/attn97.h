@@ -288,8 +288,8 @@ attn_status attn_exp2_eval(const float* x, float* y, long n, int mode, void* str
  * eight-wavefront tile at every length, 2 the four-wavefront tile at every
  * length), "bwd_dq" (D = 128 dQ of the split backward: 0 default, 1 four
  * wavefronts per workgroup, 2 eight, at every length), "bwd_dkdv" (D = 64
- * and 256 dK / dV of the split backward: 0 default, 1 the one-pass tile also
- * where S is a multiple of 128); variant -1 returns to the choice of the
+ * and 256 dK / dV of the split backward: 0 default, the pipelined tile;
+ * 1 the one-pass tile); variant -1 returns to the choice of the
  * environment variables ATTN97_FWD_VARIANT / ATTN97_DQ_VARIANT /
  * ATTN97_DKDV_VARIANT (default 0).  Every variant computes the same result.
  * The choice is process-global state shared by every thread and stream of

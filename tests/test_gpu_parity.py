@@ -605,15 +605,16 @@ def test_two_step_tiles_ragged(S):
 
 
 # ----------------------------------------------------------------------------
-# D = 64 and 256 split backward, S a multiple of 128: the pipelined dK / dV
-# tile (at D = 256 with the columns split between two workgroups; bwd_dkdv
-# variant 1: the one-pass tile it replaced), every element against the
-# float64 oracle
+# D = 64 and 256 split backward: the pipelined dK / dV tile (at D = 256 with
+# the columns split between two workgroups; bwd_dkdv variant 1: the one-pass
+# tile it replaced), every element against the float64 oracle.  Ragged
+# lengths with an odd number of 64-query tiles (150, 700) walk one extra
+# all-zero tile; 333 has an even count and a partial last tile.
 # ----------------------------------------------------------------------------
 
 
 @pytest.mark.parametrize("D", (64, 256))
-@pytest.mark.parametrize("S", (128, 256, 640))
+@pytest.mark.parametrize("S", (128, 256, 640, 150, 333, 700))
 @pytest.mark.parametrize("variant", (0, 1))
 def test_bwd_dkdv_tiles_d64_d256(D, S, variant):
     print(f"[dkdv tiles] D={D} S={S} variant={variant}", flush=True)
