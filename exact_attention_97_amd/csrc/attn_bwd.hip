@@ -226,6 +226,27 @@ __device__ __forceinline__ void dma_row_part(const uint16_t* __restrict__ src, i
   lds_dma<16>(tile, (uint32_t)(S > r0 ? S - r0 : 0) * (uint32_t)(D * 2), off, dst + 512 * (wave * NPW + n));
 }
 
+// The same piece at a given byte offset `off` (rows past S load as zeros).
+template <int D, int NPW>
+__device__ __forceinline__ void dma_row_at(const uint16_t* __restrict__ src, int r0, int S, uint16_t* dst, int wave,
+                                           int n, uint32_t off) {
+  lds_dma<16>(src + (size_t)r0 * D, (uint32_t)(S > r0 ? S - r0 : 0) * (uint32_t)(D * 2), off,
+              dst + 512 * (wave * NPW + n));
+}
+
+// Closed form of BwdOffsets::dmaq[n] at D = 128 and 256 (16 rows per wave's
+// pieces, 64 / (D / 8) rows per piece): with lr = lane / (D / 8) and
+// cc = lane % (D / 8), piece n's offset is y + 1024 n + 16 (x ^ g(n)) for the
+// per-lane values x = cc ^ 4 lr and y = 32 D wave + 2 D lr, where g(n) is the
+// swizzle term of the piece's rows; the two fields of the swizzle's XOR land
+// in disjoint bits, so the lane's part folds into x.
+template <int D>
+__device__ __forceinline__ uint32_t dmaq_closed(uint32_t x, uint32_t y, int n) {
+  static_assert(D == 128 || D == 256, "rows of 256 or 512 bytes");
+  const uint32_t g = D == 128 ? (uint32_t)n : (uint32_t)(8 * (n & 1) + (n >> 1));
+  return y + 1024u * (uint32_t)n + 16u * (x ^ g);
+}
+
 template <int D, int NPW, bool CLAMP = true>
 __device__ __forceinline__ void dma_rows(const uint16_t* __restrict__ src, int r0, int rows, int S, uint16_t* dst,
                                          int wave, const uint32_t (&loff)[NPW]) {
@@ -943,6 +964,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 
   BwdOffsets<D, Cfg> of;
   of.init(wave, lane, d0);
+  // D = 256, non-causal: the Q / dO load offsets are formed per piece from
+  // two per-lane values (dmaq_closed) instead of being held in eight
+  // registers; held, they pushed this kernel into scratch, and every reload
+  // of a spilled offset waited for all loads in flight (5 % of its time).
+  // Made opaque once per tile below, so that the compiler does not hoist the
+  // eight offsets back out of the loop.  (The causal kernel does not spill,
+  // and measured 1 % slower this way.)
+  constexpr bool DMA_CLOSED = D == 256 && !CAUSAL;
+  uint32_t dmx = 0, dmy = 0;
+  if constexpr (DMA_CLOSED) {
+    const int lr = lane / (D / 8), cc = lane % (D / 8);
+    dmx = (uint32_t)(cc ^ (4 * lr));
+    dmy = (uint32_t)(32 * D * wave_u + 2 * D * lr);
+  }
 
   // query tiles in walking order: causal from the diagonal on, non-causal
   // (fused mode) rotated by key tile
@@ -966,9 +1001,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     uint16_t* dd = set ? dOs1 : dOs0;
     const int q0 = qt * BQ;
     if (p < DMA_Q) {
-      dma_row_part<D, DMA_Q, false>(Qh, q0, BQ, S, qd, wave_u, of.dmaq, p);
+      if constexpr (DMA_CLOSED)
+        dma_row_at<D, DMA_Q>(Qh, q0, S, qd, wave_u, p, dmaq_closed<D>(dmx, dmy, p));
+      else
+        dma_row_part<D, DMA_Q, false>(Qh, q0, BQ, S, qd, wave_u, of.dmaq, p);
     } else if (p < 2 * DMA_Q) {
-      dma_row_part<D, DMA_Q, false>(dOh, q0, BQ, S, dd, wave_u, of.dmaq, p - DMA_Q);
+      if constexpr (DMA_CLOSED)
+        dma_row_at<D, DMA_Q>(dOh, q0, S, dd, wave_u, p - DMA_Q, dmaq_closed<D>(dmx, dmy, p - DMA_Q));
+      else
+        dma_row_part<D, DMA_Q, false>(dOh, q0, BQ, S, dd, wave_u, of.dmaq, p - DMA_Q);
     } else if (p == 2 * DMA_Q) {
       // -LSE log2e rows from waves 0 and 2, Delta from 1 and 3 (the pairs
       // write the same values): no branch on the wavefront index, which
@@ -1160,6 +1201,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       // (twice the offsets); this way every read is offset register + the
       // array's constant LDS address, which folds into the instruction.
       BwdOffsets<D, Cfg> ot = of;
+      if constexpr (DMA_CLOSED) asm volatile("" : "+v"(dmx), "+v"(dmy));
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(ot.arow[ks]));
 #pragma unroll
