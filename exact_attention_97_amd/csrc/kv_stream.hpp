@@ -101,6 +101,19 @@ struct FwdOffsets {
       for (int r2 = 0; r2 < 2; ++r2)
         vfrag[db][r2] = swz_chunk<D>(8 * r2 + 4 * (g16 >> 1) + (i >> 2), d >> 3) * 8 + (d & 7);
     }
+    if constexpr (D == 256) {
+      // The swizzle XORs only the low four bits of the chunk index, so chunks
+      // 16 apart sit 128 elements apart in every row: the upper half's
+      // offsets are written as the lower half's plus a constant, which folds
+      // into the LDS instructions' immediate offset and halves the registers
+      // that hold offsets (the D = 256 tiles are short of arch VGPRs).
+#pragma unroll
+      for (int ks = NKS / 2; ks < NKS; ++ks) kfrag[ks] = kfrag[ks - NKS / 2] + 128;
+#pragma unroll
+      for (int db = NDB / 2; db < NDB; ++db)
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2) vfrag[db][r2] = vfrag[db - NDB / 2][r2] + 128;
+    }
 #pragma unroll
     for (int n = 0; n < Cfg::DMA_PER_WAVE; ++n) {
       int row, c;
