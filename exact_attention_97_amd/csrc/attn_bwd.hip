@@ -1202,8 +1202,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       // array's constant LDS address, which folds into the instruction.
       BwdOffsets<D, Cfg> ot = of;
       if constexpr (DMA_CLOSED) asm volatile("" : "+v"(dmx), "+v"(dmy));
+      // D = 256: the swizzle XORs only the low four bits of a chunk index, so
+      // the offsets of reduction steps 8 .. 15 are those of steps 0 .. 7 plus
+      // 256 bytes; written after the opaque copies, the constant folds into
+      // the LDS instructions' immediate offset (eight registers fewer)
+      constexpr int NOPQ = D == 256 ? NKS / 2 : NKS;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(ot.arow[ks]));
+      for (int ks = 0; ks < NOPQ; ++ks) asm volatile("" : "+v"(ot.arow[ks]));
+#pragma unroll
+      for (int ks = NOPQ; ks < NKS; ++ks) ot.arow[ks] = ot.arow[ks - NOPQ] + 256;
 #pragma unroll
       for (int db = 0; db < NDO; ++db) asm volatile("" : "+v"(ot.trq[db][0]), "+v"(ot.trq[db][1]));
       if constexpr (DQ) {
