@@ -1170,7 +1170,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   f32x16 pend[2] = {f32x16{}, f32x16{}};
 
   // one tile: reads buffer set P, loads the next tile into set 1 - P.  M:
-  // masked tile (diagonal or ragged), where a causal wave may also have no
+  // masked tile (the causal diagonal block), where a causal wave may also have no
   // query at or after its keys (inactive: it only issues its loads; in the
   // fused mode every wave stays active, its masked dS being the zeros the
   // dQ product needs).
